@@ -1,0 +1,583 @@
+// Host side of libbsp: the per-step planner, argument validation and the C
+// entry points declared in include/bsp.h.
+//
+// The plan is built once per step on the host and read by every layer of that
+// step (TensorRT-LLM PR #21738, "Add opt-in cascade attention for wide beam
+// search on KVCM V2", first commit message). It validates lengths and page ids
+// and raises rather than clamping a bad prompt page index (eligibility commit),
+// rejects a tail longer than a fixed maximum (review thread on MAX_TAIL), takes
+// the shared prompt's page table from beam 0 (KV-cache-manager-V2 commit), and
+// hands its tables to the device through pinned staging and an asynchronous
+// copy, without waiting for the stream (commit making re-planning non-blocking).
+// In cached-prefix mode it bounds each request's keys to the valid prefix
+// rounded up to the key bucket, capped at the allocation, one row for an empty
+// cache (Phi-4 cached-prefix PR, TensorRT-Model-Connect #2202: Exit Criteria,
+// Implementation).
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "bsp_internal.h"
+
+using bsp::DevHeader;
+using bsp::ReqInfo;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+bsp_status_t fail(bsp_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+bsp_status_t ok() {
+  g_last_error.clear();
+  return BSP_OK;
+}
+
+bsp_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(BSP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int log2i(int32_t x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int elem_bytes(int dtype) { return dtype == BSP_F32 ? 4 : 2; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+struct bsp_plan_s {
+  bsp_layer_desc_t desc;
+  int32_t max_requests = 0, max_beam = 0, max_blocks = 0, max_seq_len = 0, max_q_len = 0;
+  uint32_t flags = 0;
+  bool host_only = false;
+  bool check_mode = false;
+  int page_shift = 0;
+  size_t ws_bytes = 0;
+
+  // staging ring (pinned host memory, or malloc for host-only plans)
+  void* staging[2] = {nullptr, nullptr};
+  hipEvent_t staged[2] = {nullptr, nullptr};
+  bool staged_pending[2] = {false, false};
+  int ring = 0;
+
+  // current plan
+  bool planned = false;
+  int32_t B = 0, W = 0, q_len = 0, tail_pad = 0, n_split = 1, rows_per_req = 0;
+  void* ws_d = nullptr;
+  void* zeroed_ws = nullptr;  // workspace whose header this plan has cleared
+  std::vector<ReqInfo> h_req;
+  std::vector<int32_t> h_pages;
+};
+
+namespace {
+
+size_t req_offset() { return bsp::kHeaderBytes; }
+size_t pages_offset(int32_t B) { return align_up(bsp::kHeaderBytes + sizeof(ReqInfo) * B, 16); }
+
+DevHeader* dev_header(const bsp_plan_s* pl) { return static_cast<DevHeader*>(pl->ws_d); }
+const ReqInfo* dev_req(const bsp_plan_s* pl) {
+  return reinterpret_cast<const ReqInfo*>(static_cast<char*>(pl->ws_d) + req_offset());
+}
+const int32_t* dev_pages(const bsp_plan_s* pl) {
+  return reinterpret_cast<const int32_t*>(static_cast<char*>(pl->ws_d) + pages_offset(pl->B));
+}
+
+int32_t bucket_rows(int32_t valid, int32_t bucket, int32_t cap) {
+  if (valid <= 0) return 1;
+  const int64_t r = ceil_div(valid, bucket) * bucket;
+  return (int32_t)(r < cap ? r : cap);
+}
+
+bsp_status_t check_device_ready(const bsp_plan_s* pl) {
+  if (pl == nullptr) return fail(BSP_ERR_ARG, "null plan");
+  if (!pl->planned)
+    return fail(BSP_ERR_STALE_PLAN, "plan has no valid step: call bsp_plan first");
+  if (pl->host_only) return fail(BSP_ERR_ARG, "host-only plan cannot launch kernels");
+  return BSP_OK;
+}
+
+// Check mode: wait for the launch and surface any recorded index fault.
+bsp_status_t after_launch(bsp_plan_s* pl, hipError_t launch, const char* what,
+                          hipStream_t stream) {
+  if (launch != hipSuccess) return hip_fail(launch, what);
+  if (pl != nullptr && pl->check_mode) return bsp_check(pl, stream);
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bsp_last_error(void) { return g_last_error.c_str(); }
+
+int32_t bsp_version(void) { return 100; }
+
+bsp_status_t bsp_plan_create(const bsp_layer_desc_t* desc, int32_t max_requests,
+                             int32_t max_beam, int32_t max_blocks_per_seq, int32_t max_seq_len,
+                             int32_t max_q_len, uint32_t flags, bsp_plan_t* out) {
+  if (out == nullptr || desc == nullptr) return fail(BSP_ERR_ARG, "null argument");
+  *out = nullptr;
+  const bsp_layer_desc_t& d = *desc;
+  if (d.dtype != BSP_F32 && d.dtype != BSP_F16 && d.dtype != BSP_BF16)
+    return fail(BSP_ERR_DTYPE, "dtype %d is not one of f32, f16, bf16", d.dtype);
+  if (d.num_q_heads <= 0 || d.num_kv_heads <= 0 || d.num_q_heads % d.num_kv_heads != 0)
+    return fail(BSP_ERR_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                d.num_q_heads, d.num_kv_heads);
+  if (d.head_dim != 64 && d.head_dim != 128 && d.head_dim != 256)
+    return fail(BSP_ERR_UNSUPPORTED, "head_dim %d is not 64, 128 or 256", d.head_dim);
+  if (!is_pow2(d.page_size) || d.page_size > 1024)
+    return fail(BSP_ERR_UNSUPPORTED, "page_size %d is not a power of two <= 1024", d.page_size);
+  if (d.num_pages <= 0) return fail(BSP_ERR_ARG, "num_pages must be positive");
+  if ((int64_t)d.num_pages * d.page_size > INT32_MAX)
+    return fail(BSP_ERR_UNSUPPORTED, "num_pages * page_size exceeds the int32 slot range");
+  if (!(d.sm_scale >= 0.f) || std::isinf(d.sm_scale))
+    return fail(BSP_ERR_ARG, "sm_scale must be finite and >= 0");
+  if (d.max_tail < 0) return fail(BSP_ERR_ARG, "max_tail must be >= 0");
+  if (d.key_bucket < 0) return fail(BSP_ERR_ARG, "key_bucket must be >= 0");
+  if (d.key_bucket > 0 && d.max_cache_rows <= 0)
+    return fail(BSP_ERR_ARG, "cached-prefix mode needs max_cache_rows > 0");
+  if (d.mask != BSP_MASK_NONE && d.mask != BSP_MASK_CAUSAL)
+    return fail(BSP_ERR_ARG, "mask %d is not NONE or CAUSAL", d.mask);
+  if (d.kv_split < 0 || d.kv_split % 64 != 0)
+    return fail(BSP_ERR_ARG, "kv_split (%d) must be 0 or a positive multiple of 64", d.kv_split);
+  if (max_requests <= 0 || max_beam <= 0 || max_blocks_per_seq <= 0 || max_seq_len <= 0 ||
+      max_q_len <= 0)
+    return fail(BSP_ERR_ARG, "capacities must be positive");
+  if ((int64_t)max_blocks_per_seq * d.page_size < max_seq_len)
+    return fail(BSP_ERR_ARG, "max_blocks_per_seq * page_size (%lld) < max_seq_len (%d)",
+                (long long)max_blocks_per_seq * d.page_size, max_seq_len);
+  if (d.key_bucket > 0 && (int64_t)max_blocks_per_seq * d.page_size < d.max_cache_rows)
+    return fail(BSP_ERR_ARG, "block tables cannot cover max_cache_rows");
+
+  bsp_plan_s* pl = new bsp_plan_s();
+  pl->desc = d;
+  if (pl->desc.sm_scale == 0.f) pl->desc.sm_scale = 1.0f / std::sqrt((float)d.head_dim);
+  pl->max_requests = max_requests;
+  pl->max_beam = max_beam;
+  pl->max_blocks = max_blocks_per_seq;
+  pl->max_seq_len = max_seq_len;
+  pl->max_q_len = max_q_len;
+  pl->flags = flags;
+  pl->host_only = (flags & BSP_PLAN_HOST_ONLY) != 0;
+  const char* env = std::getenv("BSP_CHECK");
+  pl->check_mode = env != nullptr && env[0] == '1';
+  pl->page_shift = log2i(d.page_size);
+  pl->ws_bytes = align_up(pages_offset(max_requests) +
+                              sizeof(int32_t) * (size_t)max_requests * max_blocks_per_seq,
+                          256);
+  for (int i = 0; i < 2; ++i) {
+    if (pl->host_only) {
+      pl->staging[i] = std::calloc(1, pl->ws_bytes);
+      if (pl->staging[i] == nullptr) {
+        bsp_plan_destroy(pl);
+        return fail(BSP_ERR_ARG, "out of host memory");
+      }
+      continue;
+    }
+    hipError_t e = hipHostMalloc(&pl->staging[i], pl->ws_bytes, hipHostMallocDefault);
+    if (e != hipSuccess) {
+      pl->staging[i] = nullptr;
+      bsp_plan_destroy(pl);
+      return hip_fail(e, "hipHostMalloc (plan staging)");
+    }
+    std::memset(pl->staging[i], 0, pl->ws_bytes);
+    e = hipEventCreateWithFlags(&pl->staged[i], hipEventDisableTiming);
+    if (e != hipSuccess) {
+      pl->staged[i] = nullptr;
+      bsp_plan_destroy(pl);
+      return hip_fail(e, "hipEventCreate (plan staging)");
+    }
+  }
+  *out = pl;
+  return ok();
+}
+
+size_t bsp_plan_workspace_bytes(bsp_plan_t plan) { return plan ? plan->ws_bytes : 0; }
+
+void bsp_plan_destroy(bsp_plan_t plan) {
+  if (plan == nullptr) return;
+  for (int i = 0; i < 2; ++i) {
+    if (plan->staged[i] != nullptr) {
+      if (plan->staged_pending[i]) (void)hipEventSynchronize(plan->staged[i]);
+      (void)hipEventDestroy(plan->staged[i]);
+    }
+    if (plan->staging[i] != nullptr) {
+      if (plan->host_only) std::free(plan->staging[i]);
+      else (void)hipHostFree(plan->staging[i]);
+    }
+  }
+  delete plan;
+}
+
+bsp_status_t bsp_plan(bsp_plan_t pl, int32_t B, int32_t W, int32_t q_len,
+                      const int32_t* prefix_len_h, const int32_t* seq_len_h,
+                      const int32_t* block_tables_h, void* workspace_d, size_t workspace_bytes,
+                      hipStream_t stream) {
+  if (pl == nullptr) return fail(BSP_ERR_ARG, "null plan");
+  pl->planned = false;
+  if (B < 1 || B > pl->max_requests)
+    return fail(BSP_ERR_ARG, "B = %d outside [1, %d]", B, pl->max_requests);
+  if (W < 1 || W > pl->max_beam) return fail(BSP_ERR_ARG, "W = %d outside [1, %d]", W, pl->max_beam);
+  if (q_len < 1 || q_len > pl->max_q_len)
+    return fail(BSP_ERR_ARG, "q_len = %d outside [1, %d]", q_len, pl->max_q_len);
+  if (prefix_len_h == nullptr || seq_len_h == nullptr || block_tables_h == nullptr)
+    return fail(BSP_ERR_ARG, "null host table");
+  if (pl->host_only) {
+    if (workspace_d != nullptr) return fail(BSP_ERR_ARG, "host-only plan takes no workspace");
+  } else {
+    if (workspace_d == nullptr) return fail(BSP_ERR_WORKSPACE, "null workspace");
+    if (workspace_bytes < pl->ws_bytes)
+      return fail(BSP_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
+                  pl->ws_bytes);
+    if ((reinterpret_cast<uintptr_t>(workspace_d) & 255u) != 0)
+      return fail(BSP_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
+
+  const bsp_layer_desc_t& d = pl->desc;
+  const int ps = d.page_size;
+  const int MB = pl->max_blocks;
+  const bool cached = d.key_bucket > 0;
+  auto bt = [&](int b, int k, int i) -> int32_t {
+    return block_tables_h[((int64_t)b * W + k) * MB + i];
+  };
+
+  std::vector<ReqInfo> req(B);
+  int64_t total_pages = 0;
+  int32_t max_tail_seen = 0, n_split = 1;
+  for (int b = 0; b < B; ++b) {
+    const int32_t P = prefix_len_h[b], S = seq_len_h[b];
+    ReqInfo& r = req[b];
+    std::memset(&r, 0, sizeof(r));
+    if (cached) {
+      if (P < 0 || P > d.max_cache_rows)
+        return fail(BSP_ERR_ARG, "request %d: valid rows %d outside [0, %d]", b, P,
+                    d.max_cache_rows);
+      if (S != P)
+        return fail(BSP_ERR_ARG, "request %d: cached-prefix mode needs seq_len == prefix_len", b);
+      r.n_keys = bucket_rows(P, d.key_bucket, d.max_cache_rows);
+      r.valid = P;
+    } else {
+      if (P < 0 || S < P || S > pl->max_seq_len)
+        return fail(BSP_ERR_ARG, "request %d: need 0 <= prefix_len (%d) <= seq_len (%d) <= %d", b,
+                    P, S, pl->max_seq_len);
+      const int32_t T = S - P;
+      if (d.max_tail > 0 && T > d.max_tail)
+        return fail(BSP_ERR_TAIL_OVERFLOW,
+                    "request %d: a beam carries %d tail positions but the plan's fixed tail "
+                    "length is %d",
+                    b, T, d.max_tail);
+      r.n_keys = P;
+      r.valid = P;
+      r.tail = T;
+      if (T > max_tail_seen) max_tail_seen = T;
+    }
+    r.prefix = P;
+    r.seq = S;
+    const int64_t nblk = ceil_div(r.n_keys, ps);
+    if (nblk > MB) return fail(BSP_ERR_ARG, "request %d: %lld blocks > max_blocks %d", b,
+                               (long long)nblk, MB);
+    for (int64_t i = 0; i < nblk; ++i) {
+      const int32_t pg = bt(b, 0, (int)i);
+      if (pg < 0 || pg >= d.num_pages)
+        return fail(BSP_ERR_PAGE_INDEX, "request %d beam 0 block %lld: page id %d outside [0, %d)",
+                    b, (long long)i, pg, d.num_pages);
+    }
+    if (!cached && S > P) {  // every beam's tail blocks may be read through the indirection
+      for (int k = 0; k < W; ++k)
+        for (int i = P / ps; i <= (S - 1) / ps; ++i) {
+          const int32_t pg = bt(b, k, i);
+          if (pg < 0 || pg >= d.num_pages)
+            return fail(BSP_ERR_PAGE_INDEX, "request %d beam %d block %d: page id %d outside [0, %d)",
+                        b, k, i, pg, d.num_pages);
+        }
+    }
+    if (pl->check_mode && !cached) {
+      for (int k = 1; k < W; ++k)
+        for (int i = 0; i < P / ps; ++i)
+          if (bt(b, k, i) != bt(b, 0, i))
+            return fail(BSP_ERR_ARG,
+                        "check mode: request %d beam %d does not share prompt block %d with beam 0",
+                        b, k, i);
+    }
+    r.page_off = (int32_t)total_pages;
+    total_pages += nblk;
+    r.n_split = d.kv_split > 0 ? (int32_t)(r.valid > 0 ? ceil_div(r.valid, d.kv_split) : 1) : 1;
+    if (r.n_split > n_split) n_split = r.n_split;
+  }
+
+  // Fill the staging buffer: header (zero), request info, page table.
+  const int slot = pl->ring;
+  if (pl->staged_pending[slot]) {
+    const hipError_t e = hipEventSynchronize(pl->staged[slot]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize (plan staging)");
+    pl->staged_pending[slot] = false;
+  }
+  char* st = static_cast<char*>(pl->staging[slot]);
+  std::memset(st, 0, bsp::kHeaderBytes);
+  std::memcpy(st + req_offset(), req.data(), sizeof(ReqInfo) * B);
+  int32_t* pg_out = reinterpret_cast<int32_t*>(st + pages_offset(B));
+  std::vector<int32_t> pages((size_t)total_pages);
+  for (int b = 0; b < B; ++b)
+    for (int64_t i = 0; i < ceil_div(req[b].n_keys, ps); ++i)
+      pages[(size_t)req[b].page_off + i] = bt(b, 0, (int)i);
+  if (!pages.empty()) std::memcpy(pg_out, pages.data(), sizeof(int32_t) * pages.size());
+
+  if (!pl->host_only) {
+    const size_t end = pages_offset(B) + sizeof(int32_t) * pages.size();
+    const size_t begin = workspace_d == pl->zeroed_ws ? req_offset() : 0;
+    hipError_t e = hipMemcpyAsync(static_cast<char*>(workspace_d) + begin, st + begin,
+                                  end - begin, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (plan tables)");
+    e = hipEventRecord(pl->staged[slot], stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord (plan staging)");
+    pl->staged_pending[slot] = true;
+    pl->ring = 1 - slot;
+    pl->zeroed_ws = workspace_d;
+  }
+
+  pl->B = B;
+  pl->W = W;
+  pl->q_len = q_len;
+  pl->tail_pad = d.max_tail > 0 ? d.max_tail : max_tail_seen;
+  pl->n_split = n_split;
+  pl->rows_per_req = W * q_len * (d.num_q_heads / d.num_kv_heads);
+  pl->ws_d = workspace_d;
+  pl->h_req = std::move(req);
+  pl->h_pages = std::move(pages);
+  pl->planned = true;
+  return ok();
+}
+
+int32_t bsp_plan_num_splits(bsp_plan_t pl) { return pl && pl->planned ? pl->n_split : -1; }
+int32_t bsp_plan_tail_len(bsp_plan_t pl) { return pl && pl->planned ? pl->tail_pad : -1; }
+
+bsp_status_t bsp_write_kv(bsp_plan_t pl, const void* k_new, const void* v_new,
+                          int64_t src_row_stride, const int32_t* slots_d, int32_t n, void* k_pool,
+                          void* v_pool, hipStream_t stream) {
+  bsp_status_t st = check_device_ready(pl);
+  if (st != BSP_OK) return st;
+  if (n < 0) return fail(BSP_ERR_ARG, "n < 0");
+  if (n == 0) return ok();
+  const bsp_layer_desc_t& d = pl->desc;
+  if (!k_new || !v_new || !slots_d || !k_pool || !v_pool) return fail(BSP_ERR_ARG, "null pointer");
+  const int vec = 16 / elem_bytes(d.dtype);
+  if (src_row_stride < (int64_t)d.num_kv_heads * d.head_dim || src_row_stride % vec != 0)
+    return fail(BSP_ERR_ARG, "src_row_stride %lld must be >= %d and a multiple of %d",
+                (long long)src_row_stride, d.num_kv_heads * d.head_dim, vec);
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(BSP_ERR_ARG, "k_new, v_new and the pools must be 16-byte aligned");
+  bsp::WriteKvParams p;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.src_stride = src_row_stride;
+  p.slots = slots_d;
+  p.n = n;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.hkv = d.num_kv_heads;
+  p.d = d.head_dim;
+  p.page_size = d.page_size;
+  p.num_slots = (int64_t)d.num_pages * d.page_size;
+  p.hdr = dev_header(pl);
+  return after_launch(pl, bsp::launch_write_kv(p, d.dtype, stream), "write_kv launch", stream);
+}
+
+bsp_status_t bsp_prefix_attn(bsp_plan_t pl, const void* q, const void* k_pool, const void* v_pool,
+                             float* o_part, float* lse_part, hipStream_t stream) {
+  bsp_status_t st = check_device_ready(pl);
+  if (st != BSP_OK) return st;
+  if (!q || !k_pool || !v_pool || !o_part || !lse_part) return fail(BSP_ERR_ARG, "null pointer");
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o_part))
+    return fail(BSP_ERR_ARG, "q, the pools and o_part must be 16-byte aligned");
+  const bsp_layer_desc_t& d = pl->desc;
+  bsp::PrefixParams p;
+  p.q = q;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.o_part = o_part;
+  p.lse_part = lse_part;
+  p.req = dev_req(pl);
+  p.pages = dev_pages(pl);
+  p.hdr = dev_header(pl);
+  p.B = pl->B;
+  p.W = pl->W;
+  p.q_len = pl->q_len;
+  p.hq = d.num_q_heads;
+  p.hkv = d.num_kv_heads;
+  p.group = d.num_q_heads / d.num_kv_heads;
+  p.page_shift = pl->page_shift;
+  p.num_pages = d.num_pages;
+  p.n_split = pl->n_split;
+  p.split_keys = d.kv_split;
+  const int rows_per_tile = bsp::prefix_rows_per_tile(d.dtype, d.head_dim, pl->rows_per_req);
+  p.n_qtiles = (int32_t)ceil_div(pl->rows_per_req, rows_per_tile);
+  p.causal = d.mask == BSP_MASK_CAUSAL ? 1 : 0;
+  p.rows_total = pl->B * pl->W * pl->q_len;
+  p.scale = d.sm_scale;
+  p.scale_log2e = d.sm_scale * 1.4426950408889634f;
+  return after_launch(pl, bsp::launch_prefix(p, d.dtype, d.head_dim, pl->rows_per_req, stream),
+                      "prefix launch", stream);
+}
+
+static bsp::TailParams tail_params(const bsp_plan_s* pl, const void* q, const void* k_pool,
+                                   const void* v_pool, const int32_t* bt, const int32_t* ci) {
+  const bsp_layer_desc_t& d = pl->desc;
+  bsp::TailParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = q;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.block_tables = bt;
+  p.ci = ci;
+  p.req = dev_req(pl);
+  p.hdr = dev_header(pl);
+  p.B = pl->B;
+  p.W = pl->W;
+  p.hq = d.num_q_heads;
+  p.hkv = d.num_kv_heads;
+  p.group = d.num_q_heads / d.num_kv_heads;
+  p.page_shift = pl->page_shift;
+  p.num_pages = d.num_pages;
+  p.max_blocks = pl->max_blocks;
+  p.max_seq_len = pl->max_seq_len;
+  p.tail_pad = pl->tail_pad;
+  p.scale = d.sm_scale;
+  p.scale_log2e = d.sm_scale * 1.4426950408889634f;
+  return p;
+}
+
+bsp_status_t bsp_tail_attn(bsp_plan_t pl, const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* block_tables_d, const int32_t* cache_indirection_d,
+                           float* o_tail, float* lse_tail, hipStream_t stream) {
+  bsp_status_t st = check_device_ready(pl);
+  if (st != BSP_OK) return st;
+  if (pl->q_len != 1) return fail(BSP_ERR_UNSUPPORTED, "tail attention needs q_len == 1");
+  if (!q || !k_pool || !v_pool || !block_tables_d || !cache_indirection_d || !o_tail || !lse_tail)
+    return fail(BSP_ERR_ARG, "null pointer");
+  bsp::TailParams p = tail_params(pl, q, k_pool, v_pool, block_tables_d, cache_indirection_d);
+  p.o_tail = o_tail;
+  p.lse_tail = lse_tail;
+  return after_launch(pl, bsp::launch_tail(p, pl->desc.dtype, pl->desc.head_dim, stream),
+                      "tail launch", stream);
+}
+
+bsp_status_t bsp_naive_beam_attn(bsp_plan_t pl, const void* q, const void* k_pool,
+                                 const void* v_pool, const int32_t* block_tables_d,
+                                 const int32_t* cache_indirection_d, void* o_out, float* lse_out,
+                                 hipStream_t stream) {
+  bsp_status_t st = check_device_ready(pl);
+  if (st != BSP_OK) return st;
+  if (pl->q_len != 1) return fail(BSP_ERR_UNSUPPORTED, "naive attention needs q_len == 1");
+  if (pl->desc.key_bucket > 0) return fail(BSP_ERR_UNSUPPORTED, "naive attention is beam mode only");
+  if (!q || !k_pool || !v_pool || !block_tables_d || !cache_indirection_d || !o_out)
+    return fail(BSP_ERR_ARG, "null pointer");
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(BSP_ERR_ARG, "q and the pools must be 16-byte aligned");
+  bsp::TailParams p = tail_params(pl, q, k_pool, v_pool, block_tables_d, cache_indirection_d);
+  return after_launch(pl,
+                      bsp::launch_naive(p, o_out, lse_out, pl->desc.dtype, pl->desc.head_dim, stream),
+                      "naive launch", stream);
+}
+
+bsp_status_t bsp_merge(int32_t rows, int32_t heads, int32_t head_dim, int32_t n_parts,
+                       const float* o_parts, const float* lse_parts, int64_t o_part_stride,
+                       int64_t lse_part_stride, void* o_out, int32_t out_dtype, float* lse_out,
+                       hipStream_t stream) {
+  if (rows < 0 || heads <= 0 || head_dim <= 0 || head_dim % 4 != 0 || n_parts <= 0)
+    return fail(BSP_ERR_ARG, "bad merge sizes (rows %d heads %d head_dim %d parts %d)", rows, heads,
+                head_dim, n_parts);
+  if (out_dtype != BSP_F32 && out_dtype != BSP_F16 && out_dtype != BSP_BF16)
+    return fail(BSP_ERR_DTYPE, "out_dtype %d is not one of f32, f16, bf16", out_dtype);
+  if (rows == 0) return ok();
+  if (!o_parts || !lse_parts || !o_out) return fail(BSP_ERR_ARG, "null pointer");
+  const int64_t o_need = (int64_t)rows * heads * head_dim, l_need = (int64_t)rows * heads;
+  if (n_parts > 1 && (o_part_stride < o_need || lse_part_stride < l_need))
+    return fail(BSP_ERR_ARG, "part strides smaller than one part");
+  if (!aligned16(o_parts) || o_part_stride % 4 != 0)
+    return fail(BSP_ERR_ARG, "o_parts must be 16-byte aligned with a stride multiple of 4");
+  bsp::MergeParams p;
+  p.rows = rows;
+  p.heads = heads;
+  p.d = head_dim;
+  p.n_parts = n_parts;
+  p.o_parts = o_parts;
+  p.lse_parts = lse_parts;
+  p.o_stride = o_part_stride;
+  p.lse_stride = lse_part_stride;
+  p.o_out = o_out;
+  p.lse_out = lse_out;
+  const hipError_t e = bsp::launch_merge(p, out_dtype, stream);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return ok();
+}
+
+bsp_status_t bsp_check(bsp_plan_t pl, hipStream_t stream) {
+  if (pl == nullptr) return fail(BSP_ERR_ARG, "null plan");
+  if (pl->host_only || pl->ws_d == nullptr) return ok();
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  DevHeader h;
+  e = hipMemcpy(&h, pl->ws_d, sizeof(h), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy (error word)");
+  if (h.error_bits == 0) return ok();
+  DevHeader zero;
+  std::memset(&zero, 0, sizeof(zero));
+  e = hipMemcpy(pl->ws_d, &zero, sizeof(zero), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy (clear error word)");
+  return fail(BSP_ERR_DEVICE_INDEX,
+              "kernels skipped %d out-of-range index reads/writes (bits 0x%x: 1 prompt page, 2 "
+              "cache_indirection parent, 4 tail page, 8 write slot); first value %d",
+              h.fault_count, h.error_bits, h.first_value);
+}
+
+bsp_status_t bsp_debug_plan_tables(bsp_plan_t pl, int32_t* indptr_h, int32_t* pages_h,
+                                   int32_t* n_keys_h, int32_t* valid_h, int32_t* tail_h) {
+  if (pl == nullptr) return fail(BSP_ERR_ARG, "null plan");
+  if (!pl->planned) return fail(BSP_ERR_STALE_PLAN, "plan has no valid step");
+  for (int b = 0; b < pl->B; ++b) {
+    const ReqInfo& r = pl->h_req[b];
+    if (indptr_h) indptr_h[b] = r.page_off;
+    if (n_keys_h) n_keys_h[b] = r.n_keys;
+    if (valid_h) valid_h[b] = r.valid;
+    if (tail_h) tail_h[b] = r.tail;
+  }
+  if (indptr_h) indptr_h[pl->B] = (int32_t)pl->h_pages.size();
+  if (pages_h && !pl->h_pages.empty())
+    std::memcpy(pages_h, pl->h_pages.data(), sizeof(int32_t) * pl->h_pages.size());
+  return ok();
+}
+
+bsp_status_t bsp_debug_tail_slots(bsp_plan_t pl, const int32_t* block_tables_d,
+                                  const int32_t* cache_indirection_d, int32_t* slots_d,
+                                  hipStream_t stream) {
+  bsp_status_t st = check_device_ready(pl);
+  if (st != BSP_OK) return st;
+  if (!block_tables_d || !cache_indirection_d || !slots_d) return fail(BSP_ERR_ARG, "null pointer");
+  bsp::TailParams p = tail_params(pl, nullptr, nullptr, nullptr, block_tables_d, cache_indirection_d);
+  p.slots_out = slots_d;
+  return after_launch(pl, bsp::launch_tail_slots(p, stream), "tail slots launch", stream);
+}
+
+}  // extern "C"

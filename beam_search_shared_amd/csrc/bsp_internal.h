@@ -1,0 +1,126 @@
+// Internal declarations shared by the host planner (bsp_host.cpp) and the HIP
+// kernels. Not part of the public ABI.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/bsp.h"
+
+namespace bsp {
+
+// ---------------------------------------------------------------------------
+// Device workspace written by bsp_plan (caller-owned device memory).
+//
+//   [0, 256)                 header: error word, fault count, first bad value
+//   [256, 256 + 32*maxB)     per-request info, ReqInfo
+//   then                     shared-key page table, int32 [sum of pages]
+// ---------------------------------------------------------------------------
+constexpr size_t kHeaderBytes = 256;
+
+enum ErrorBits : int32_t {
+  kErrPrefixPage = 1,   // a shared-key page id outside [0, num_pages)
+  kErrTailParent = 2,   // a cache_indirection entry outside [0, W)
+  kErrTailPage = 4,     // a tail block-table entry outside [0, num_pages)
+  kErrWriteSlot = 8,    // a KV-write slot outside [0, num_pages * page_size)
+};
+
+struct DevHeader {
+  int32_t error_bits;   // OR of ErrorBits
+  int32_t fault_count;
+  int32_t first_value;  // the first offending value a kernel saw (racy, informative)
+  int32_t pad[61];
+};
+static_assert(sizeof(DevHeader) == kHeaderBytes, "header size");
+
+struct ReqInfo {
+  int32_t page_off;  // first entry of this request in the page table
+  int32_t n_keys;    // rows the page table covers (P_b, or the bound rows)
+  int32_t valid;     // rows attended (P_b, or the valid cached rows L_b)
+  int32_t prefix;    // P_b
+  int32_t seq;       // S_b
+  int32_t tail;      // S_b - P_b
+  int32_t n_split;   // splits holding keys
+  int32_t pad;
+};
+static_assert(sizeof(ReqInfo) == 32, "ReqInfo size");
+
+// ---------------------------------------------------------------------------
+// Kernel parameter blocks (passed by value).
+// ---------------------------------------------------------------------------
+struct WriteKvParams {
+  const void* k_new;
+  const void* v_new;
+  int64_t src_stride;   // elements between consecutive tokens
+  const int32_t* slots;
+  int32_t n;
+  void* k_pool;
+  void* v_pool;
+  int32_t hkv, d, page_size;
+  int64_t num_slots;
+  DevHeader* hdr;
+};
+
+struct PrefixParams {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  float* o_part;
+  float* lse_part;
+  const ReqInfo* req;
+  const int32_t* pages;
+  DevHeader* hdr;
+  int32_t B, W, q_len, hq, hkv, group;
+  int32_t page_shift;   // log2(page_size)
+  int32_t num_pages;
+  int32_t n_split, split_keys, n_qtiles;
+  int32_t causal;
+  int32_t rows_total;   // B * W * q_len
+  float scale;          // softmax scale
+  float scale_log2e;    // scale * log2(e)
+};
+
+struct TailParams {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* ci;
+  float* o_tail;
+  float* lse_tail;
+  int32_t* slots_out;   // debug: resolved slots [B*W*tail_pad] or null
+  const ReqInfo* req;
+  DevHeader* hdr;
+  int32_t B, W, hq, hkv, group;
+  int32_t page_shift, num_pages;
+  int32_t max_blocks, max_seq_len, tail_pad;
+  float scale, scale_log2e;
+};
+
+struct MergeParams {
+  int32_t rows, heads, d, n_parts;
+  const float* o_parts;
+  const float* lse_parts;
+  int64_t o_stride, lse_stride;
+  void* o_out;
+  float* lse_out;
+};
+
+// ---------------------------------------------------------------------------
+// Launchers (defined next to their kernels). They return hipSuccess or the
+// launch error; shape checks are done by the host entry points beforehand.
+// ---------------------------------------------------------------------------
+hipError_t launch_write_kv(const WriteKvParams& p, int dtype, hipStream_t s);
+hipError_t launch_prefix(const PrefixParams& p, int dtype, int head_dim, int rows_per_req,
+                         hipStream_t s);
+// Rows per workgroup the prefix kernel picks for this shape (so the host can
+// size the grid before launching).
+int prefix_rows_per_tile(int dtype, int head_dim, int rows_per_req);
+hipError_t launch_tail(const TailParams& p, int dtype, int head_dim, hipStream_t s);
+hipError_t launch_tail_slots(const TailParams& p, hipStream_t s);
+hipError_t launch_merge(const MergeParams& p, int out_dtype, hipStream_t s);
+hipError_t launch_naive(const TailParams& p, void* o_out, float* lse_out, int dtype,
+                        int head_dim, hipStream_t s);
+
+}  // namespace bsp

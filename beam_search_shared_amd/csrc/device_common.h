@@ -1,0 +1,95 @@
+// Device helpers for the gfx950 kernels: storage-type traits, 16-byte vector
+// loads, and wave-level reductions built on DPP row permutations.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace bsp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Storage-type traits: conversion to and from fp32.
+template <typename T> struct Traits;
+template <> struct Traits<float> {
+  static __device__ __forceinline__ float to_f(float x) { return x; }
+  static __device__ __forceinline__ float from_f(float x) { return x; }
+};
+template <> struct Traits<_Float16> {
+  static __device__ __forceinline__ float to_f(_Float16 x) { return (float)x; }
+  static __device__ __forceinline__ _Float16 from_f(float x) { return (_Float16)x; }
+};
+template <> struct Traits<__bf16> {
+  static __device__ __forceinline__ float to_f(__bf16 x) { return (float)x; }
+  static __device__ __forceinline__ __bf16 from_f(float x) { return (__bf16)x; }
+};
+
+// 2^x on the transcendental unit (v_exp_f32); exp2(-inf) = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// DPP move with a compile-time control word; every source lane is valid for
+// the quad permutations and mirrors used here.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i inside each group of 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i inside each row of 16
+
+// Sum / max over each row of 16 lanes; every lane of the row gets the result.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_mov<kDppXor1>(x);
+  x += dpp_mov<kDppXor2>(x);
+  x += dpp_mov<kDppHalfMirror>(x);
+  x += dpp_mov<kDppMirror>(x);
+  return x;
+}
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_mov<kDppXor1>(x));
+  x = fmaxf(x, dpp_mov<kDppXor2>(x));
+  x = fmaxf(x, dpp_mov<kDppHalfMirror>(x));
+  x = fmaxf(x, dpp_mov<kDppMirror>(x));
+  return x;
+}
+
+// Wave-uniform sum / max over all 64 lanes.
+__device__ __forceinline__ float wave_sum(float x) {
+  x = row16_sum(x);
+  float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+  float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
+  float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+  float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
+  return (a + b) + (c + d);
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = row16_max(x);
+  float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+  float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
+  float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+  float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+// Exchange with lane (lane ^ 16) / (lane ^ 32) of the same wave.
+__device__ __forceinline__ float xor16(float x) { return __shfl_xor(x, 16, 64); }
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+__device__ __forceinline__ void record_fault(int32_t* bits, int32_t* count, int32_t* first,
+                                             int32_t bit, int32_t value) {
+  // Vector-memory atomics on the caller's workspace.
+  if (atomicAdd(count, 1) == 0) atomicExch(first, value);
+  atomicOr(bits, bit);
+}
+
+}  // namespace bsp

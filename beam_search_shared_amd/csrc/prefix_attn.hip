@@ -1,0 +1,436 @@
+// Shared-key ("prefix") attention: every query row of a request against the
+// request's shared keys, read once per request and KV head.
+//
+// The prompt is attended once per request with all beams' query rows together
+// (TensorRT-LLM PR #21738, "Add opt-in cascade attention for wide beam search
+// on KVCM V2", Description: Solution; the FA4 commit feeds one group of
+// beam_width queries per request). With W beams and G query heads per KV head
+// that is M = W * G rows against the same keys, a real dense contraction, so
+// bf16/f16 run on the gfx950 matrix cores (v_mfma_f32_16x16x32_{bf16,f16}).
+//
+// Work item: (request b, KV head g, key split, query-row tile). A workgroup is
+// 4 waves; each wave owns 16*MB query rows. Keys stream through LDS in tiles
+// of KT rows (K and V, row stride padded by 16 bytes); the next tile's global
+// loads are issued into registers before the current tile is computed.
+//
+// Products are taken transposed so that queries sit on the MFMA "n" index
+// (lane % 16) in both of them:
+//   S^T[key][query] = sum_d K[key][d] * Q[query][d]     A = K (LDS), B = Q^T (registers)
+//   O^T[d][query]  += sum_key V[key][d] * P[query][key] A = V^T (LDS), B = P^T
+// The 16x16 accumulator layout puts S^T[4*(lane/16)+e][lane%16] in lane
+// `lane`, element e; those are exactly the (query, key) pairs the lane must
+// supply as the B operand of the second product, so P^T never crosses lanes,
+// and O^T's rows per query live in the same lane as that query's softmax
+// statistics. Both operands of each product enumerate the contraction index
+// in the same per-lane order, so the result does not depend on how the
+// hardware orders the 32-wide contraction inside an instruction.
+//
+// Online softmax (running max m and sum l per query row, rescaling O when m
+// grows) is taken in base 2 on the raw dot products: p = 2^((s - m) * scale *
+// log2 e). f32 runs a vector-ALU kernel (one wave per query row).
+#include <climits>
+
+#include "bsp_internal.h"
+#include "device_common.h"
+
+namespace bsp {
+
+template <typename T> struct Mfma;
+template <> struct Mfma<__bf16> {
+  using V8 = bf16x8;
+  static __device__ __forceinline__ f32x4 mma(V8 a, V8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Mfma<_Float16> {
+  using V8 = f16x8;
+  static __device__ __forceinline__ f32x4 mma(V8 a, V8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+struct WorkItem {
+  int b, g, split, qt;
+  int k_lo, k_hi;  // key range of this item (keys >= k_hi are never read)
+};
+
+// Large row blocks need more than half of a SIMD's registers: those variants
+// run one workgroup per CU so accumulators can also live in AGPRs.
+template <int D, int MB>
+constexpr int prefix_min_blocks() { return MB * D >= 384 ? 1 : 2; }
+
+template <typename T, int D, int MB, int KT>
+__global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma_kernel(PrefixParams p) {
+  using V8 = typename Mfma<T>::V8;
+  constexpr int RS = D + 8;             // LDS row stride in elements (16-byte pad)
+  constexpr int NDS = D / 32;           // contraction steps of S^T
+  constexpr int NDB = D / 16;           // 16-row blocks of O^T
+  constexpr int NKB = KT / 16;          // 16-key blocks of S^T per tile
+  constexpr int NS2 = KT / 32;          // contraction steps of O^T per tile
+  constexpr int CPR = D / 8;            // 16-byte chunks per key row
+  constexpr int CPT = KT * CPR / 256;   // chunks per thread per tile (each of K, V)
+  static_assert(CPT >= 1 && KT * CPR % 256 == 0, "tile must split over 256 threads");
+  __shared__ __attribute__((aligned(16))) T lds_k[KT * RS];
+  __shared__ __attribute__((aligned(16))) T lds_v[KT * RS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l16 = lane & 15;
+  const int l4 = lane >> 4;
+
+  WorkItem w;
+  {
+    int bid = blockIdx.x;
+    w.qt = bid % p.n_qtiles;
+    bid /= p.n_qtiles;
+    w.split = bid % p.n_split;
+    bid /= p.n_split;
+    w.g = bid % p.hkv;
+    w.b = bid / p.hkv;
+  }
+  const ReqInfo ri = p.req[w.b];
+  w.k_lo = p.split_keys > 0 ? w.split * p.split_keys : 0;
+  w.k_hi = p.split_keys > 0 ? min(ri.valid, w.k_lo + p.split_keys) : ri.valid;
+  if (w.k_hi < w.k_lo) w.k_hi = w.k_lo;
+
+  const int M = p.W * p.q_len * p.group;
+  const int row0 = w.qt * (64 * MB) + wave * (16 * MB);
+  const bool wave_active = row0 < M;
+  const int ps_mask = (1 << p.page_shift) - 1;
+
+  // ---- query rows of this lane (B operand of S^T), causal limits
+  V8 qv[MB][NDS];
+  int climit[MB];
+#pragma unroll
+  for (int qb = 0; qb < MB; ++qb) {
+    const int r = row0 + qb * 16 + l16;
+    climit[qb] = INT_MAX;
+    if (r < M) {
+      const int hh = r % p.group;
+      const int t = r / p.group;
+      const int i = t % p.q_len;
+      const int kbeam = t / p.q_len;
+      const int64_t qrow =
+          (((int64_t)w.b * p.W + kbeam) * p.q_len + i) * p.hq + w.g * p.group + hh;
+      const T* qp = static_cast<const T*>(p.q) + qrow * D + l4 * 8;
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) qv[qb][ds] = *reinterpret_cast<const V8*>(qp + ds * 32);
+      if (p.causal) climit[qb] = ri.n_keys - p.q_len + i;
+    } else {
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[qb][ds][e] = Traits<T>::from_f(0.f);
+      }
+    }
+  }
+
+  f32x4 oacc[NDB][MB];
+  float mrow[MB], lrow[MB];
+#pragma unroll
+  for (int qb = 0; qb < MB; ++qb) {
+    mrow[qb] = -INFINITY;
+    lrow[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const T* kpool = static_cast<const T*>(p.k_pool);
+  const T* vpool = static_cast<const T*>(p.v_pool);
+  u32x4 pk[CPT], pv[CPT];
+
+  auto load_tile = [&](int t0) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int c = tid + u * 256;
+      const int key = c / CPR;
+      const int dc = c % CPR;
+      const int j = t0 + key;
+      pk[u] = u32x4{0u, 0u, 0u, 0u};
+      pv[u] = u32x4{0u, 0u, 0u, 0u};
+      if (j < w.k_hi) {
+        const int32_t page = p.pages[ri.page_off + (j >> p.page_shift)];
+        if (page >= 0 && page < p.num_pages) {
+          const int64_t off =
+              ((((int64_t)page * p.hkv + w.g) << p.page_shift) + (j & ps_mask)) * D + dc * 8;
+          pk[u] = *reinterpret_cast<const u32x4*>(kpool + off);
+          pv[u] = *reinterpret_cast<const u32x4*>(vpool + off);
+        } else if (dc == 0) {
+          record_fault(&p.hdr->error_bits, &p.hdr->fault_count, &p.hdr->first_value,
+                       kErrPrefixPage, page);
+        }
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int c = tid + u * 256;
+      const int key = c / CPR;
+      const int dc = c % CPR;
+      *reinterpret_cast<u32x4*>(&lds_k[key * RS + dc * 8]) = pk[u];
+      *reinterpret_cast<u32x4*>(&lds_v[key * RS + dc * 8]) = pv[u];
+    }
+  };
+
+  const float c2 = p.scale_log2e;
+  if (w.k_lo < w.k_hi) load_tile(w.k_lo);
+  for (int t0 = w.k_lo; t0 < w.k_hi; t0 += KT) {
+    __syncthreads();
+    store_tile();
+    __syncthreads();
+    if (t0 + KT < w.k_hi) load_tile(t0 + KT);
+    if (!wave_active) continue;
+
+    // ---- S^T = K Q^T for this tile
+    f32x4 sacc[NKB][MB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < MB; ++qb) sacc[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const V8 a = *reinterpret_cast<const V8*>(&lds_k[(kb * 16 + l16) * RS + ds * 32 + l4 * 8]);
+#pragma unroll
+        for (int qb = 0; qb < MB; ++qb) sacc[kb][qb] = Mfma<T>::mma(a, qv[qb][ds], sacc[kb][qb]);
+      }
+    }
+
+    // ---- masking and online softmax, per query block
+    const bool full = (t0 + KT <= w.k_hi) && !p.causal;
+#pragma unroll
+    for (int qb = 0; qb < MB; ++qb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float s = sacc[kb][qb][e];
+          if (!full) {
+            const int j = t0 + kb * 16 + l4 * 4 + e;
+            if (j >= w.k_hi || j > climit[qb]) s = -INFINITY;
+          }
+          sacc[kb][qb][e] = s;
+          mx = fmaxf(mx, s);
+        }
+      }
+      mx = fmaxf(mx, xor16(mx));
+      mx = fmaxf(mx, xor32(mx));
+      const float m_new = fmaxf(mrow[qb], mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2((mrow[qb] - m_use) * c2);
+      const float moff = -m_use * c2;
+      mrow[qb] = m_new;
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float pr = fast_exp2(fmaf(sacc[kb][qb][e], c2, moff));
+          sacc[kb][qb][e] = pr;
+          rs += pr;
+        }
+      }
+      lrow[qb] = fmaf(lrow[qb], alpha, rs);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db][qb] *= alpha;
+    }
+
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int s2 = 0; s2 < NS2; ++s2) {
+      V8 pb[MB];
+#pragma unroll
+      for (int qb = 0; qb < MB; ++qb) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pb[qb][e] = Traits<T>::from_f(sacc[2 * s2][qb][e]);
+          pb[qb][4 + e] = Traits<T>::from_f(sacc[2 * s2 + 1][qb][e]);
+        }
+      }
+      const T* v0 = &lds_v[(32 * s2 + 4 * l4) * RS + l16];
+      const T* v1 = &lds_v[(32 * s2 + 16 + 4 * l4) * RS + l16];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        V8 a;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = v0[e * RS + db * 16];
+          a[4 + e] = v1[e * RS + db * 16];
+        }
+#pragma unroll
+        for (int qb = 0; qb < MB; ++qb) oacc[db][qb] = Mfma<T>::mma(a, pb[qb], oacc[db][qb]);
+      }
+    }
+  }
+
+  // ---- epilogue: normalise and write the partial state
+#pragma unroll
+  for (int qb = 0; qb < MB; ++qb) {
+    float lt = lrow[qb];
+    lt += xor16(lt);
+    lt += xor32(lt);
+    const int r = row0 + qb * 16 + l16;
+    if (!wave_active || r >= M) continue;
+    const int hh = r % p.group;
+    const int t = r / p.group;
+    const int i = t % p.q_len;
+    const int kbeam = t / p.q_len;
+    const int64_t grow = ((int64_t)w.b * p.W + kbeam) * p.q_len + i;
+    const int64_t ohead = ((int64_t)w.split * p.rows_total + grow) * p.hq + w.g * p.group + hh;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    float* op = p.o_part + ohead * D + l4 * 4;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      *reinterpret_cast<f32x4*>(op + db * 16) = oacc[db][qb] * inv;
+    if (l4 == 0) p.lse_part[ohead] = lt > 0.f ? mrow[qb] * p.scale + __logf(lt) : -INFINITY;
+  }
+}
+
+// f32: one wave per query row, lanes split head_dim, keys in chunks of 8.
+template <int D>
+__global__ __launch_bounds__(256) void prefix_simt_kernel(PrefixParams p) {
+  constexpr int EPL = D / 64;
+  constexpr int CHUNK = 8;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int bid = blockIdx.x;
+  const int qt = bid % p.n_qtiles;
+  bid /= p.n_qtiles;
+  const int split = bid % p.n_split;
+  bid /= p.n_split;
+  const int g = bid % p.hkv;
+  const int b = bid / p.hkv;
+  const ReqInfo ri = p.req[b];
+  const int M = p.W * p.q_len * p.group;
+  const int r = qt * 4 + wave;
+  if (r >= M) return;
+  int k_lo = p.split_keys > 0 ? split * p.split_keys : 0;
+  int k_hi = p.split_keys > 0 ? min(ri.valid, k_lo + p.split_keys) : ri.valid;
+  const int hh = r % p.group;
+  const int t = r / p.group;
+  const int i = t % p.q_len;
+  const int kbeam = t / p.q_len;
+  if (p.causal) k_hi = min(k_hi, ri.n_keys - p.q_len + i + 1);
+  const int ps = 1 << p.page_shift;
+  const int64_t grow = ((int64_t)b * p.W + kbeam) * p.q_len + i;
+  const int h = g * p.group + hh;
+  const float* qp = static_cast<const float*>(p.q) + (grow * p.hq + h) * D + lane * EPL;
+  const float* kpool = static_cast<const float*>(p.k_pool);
+  const float* vpool = static_cast<const float*>(p.v_pool);
+  float q[EPL], acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    q[e] = qp[e];
+    acc[e] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  for (int j0 = k_lo; j0 < k_hi; j0 += CHUNK) {
+    float kr[CHUNK][EPL], vr[CHUNK][EPL];
+    bool ok[CHUNK];
+#pragma unroll
+    for (int c = 0; c < CHUNK; ++c) {
+      const int j = j0 + c;
+      ok[c] = false;
+      if (j < k_hi) {
+        const int32_t page = p.pages[ri.page_off + (j >> p.page_shift)];
+        if (page >= 0 && page < p.num_pages) {
+          ok[c] = true;
+          const int64_t off = (((int64_t)page * p.hkv + g) * ps + (j & (ps - 1))) * D + lane * EPL;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) {
+            kr[c][e] = kpool[off + e];
+            vr[c][e] = vpool[off + e];
+          }
+        } else if (lane == 0) {
+          record_fault(&p.hdr->error_bits, &p.hdr->fault_count, &p.hdr->first_value,
+                       kErrPrefixPage, page);
+        }
+      }
+      if (!ok[c]) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) kr[c][e] = vr[c][e] = 0.f;
+      }
+    }
+    float s[CHUNK], cmax = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < CHUNK; ++c) {
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) part = fmaf(q[e], kr[c][e], part);
+      s[c] = ok[c] ? wave_sum(part) * p.scale_log2e : -INFINITY;
+      cmax = fmaxf(cmax, s[c]);
+    }
+    const float m_new = fmaxf(m, cmax);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_use);
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int c = 0; c < CHUNK; ++c) {
+      const float pc = fast_exp2(s[c] - m_use);
+      l += pc;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(pc, vr[c][e], acc[e]);
+    }
+    m = m_new;
+  }
+  const int64_t ohead = ((int64_t)split * p.rows_total + grow) * p.hq + h;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) p.o_part[ohead * D + lane * EPL + e] = acc[e] * inv;
+  if (lane == 0) p.lse_part[ohead] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+}
+
+// Query-row blocks of 16 per wave for an M-row item (4 waves per workgroup).
+static int pick_mb(int head_dim, int rows_per_req) {
+  const int mb = (rows_per_req + 63) / 64;
+  const int cap = head_dim == 256 ? 2 : 3;
+  return mb < 1 ? 1 : (mb > cap ? cap : mb);
+}
+
+int prefix_rows_per_tile(int dtype, int head_dim, int rows_per_req) {
+  if (dtype == BSP_F32) return 4;
+  return 64 * pick_mb(head_dim, rows_per_req);
+}
+
+template <typename T>
+static void launch_mfma(const PrefixParams& p, int head_dim, int mb, unsigned blocks,
+                        hipStream_t s) {
+#define BSP_PFX(DD, MBB, KTT) prefix_mfma_kernel<T, DD, MBB, KTT><<<blocks, 256, 0, s>>>(p)
+  if (head_dim == 64) {
+    if (mb == 1) BSP_PFX(64, 1, 64);
+    else if (mb == 2) BSP_PFX(64, 2, 64);
+    else BSP_PFX(64, 3, 64);
+  } else if (head_dim == 128) {
+    if (mb == 1) BSP_PFX(128, 1, 64);
+    else if (mb == 2) BSP_PFX(128, 2, 64);
+    else BSP_PFX(128, 3, 64);
+  } else {
+    if (mb == 1) BSP_PFX(256, 1, 32);
+    else BSP_PFX(256, 2, 32);
+  }
+#undef BSP_PFX
+}
+
+hipError_t launch_prefix(const PrefixParams& p, int dtype, int head_dim, int rows_per_req,
+                         hipStream_t s) {
+  const unsigned blocks = (unsigned)(p.B * p.hkv * p.n_split * p.n_qtiles);
+  if (blocks == 0) return hipSuccess;
+  if (dtype == BSP_F32) {
+    if (head_dim == 64) prefix_simt_kernel<64><<<blocks, 256, 0, s>>>(p);
+    else if (head_dim == 128) prefix_simt_kernel<128><<<blocks, 256, 0, s>>>(p);
+    else prefix_simt_kernel<256><<<blocks, 256, 0, s>>>(p);
+  } else {
+    const int mb = pick_mb(head_dim, rows_per_req);
+    if (dtype == BSP_F16) launch_mfma<_Float16>(p, head_dim, mb, blocks, s);
+    else launch_mfma<__bf16>(p, head_dim, mb, blocks, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bsp

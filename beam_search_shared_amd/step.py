@@ -1,0 +1,226 @@
+"""One decode step of one layer, composed from the C entry points.
+
+torch is used for device memory and streams only: every arithmetic step runs in
+libbsp's kernels. A beam step is
+
+    bsp_write_kv     current token of every beam -> its own page
+    bsp_prefix_attn  all beams' query rows x the shared prompt, once per request
+    bsp_tail_attn    each beam's tail through cache_indirection
+    bsp_merge        exact LSE merge of the two partial states
+
+and a cached-prefix call (beam 1) is
+
+    bsp_write_kv     this call's rows -> scratch pages
+    bsp_prefix_attn  the bound cache rows (valid rows only), split into chunks
+    bsp_prefix_attn  this call's rows, causal
+    bsp_merge        n-way merge of all the partial states
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _binding as B
+
+TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def to_device(a: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """Upload float32 values (already representable in ``dtype``) exactly."""
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device=device).to(TORCH_DTYPE[dtype])
+
+
+def _i32(a: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+
+
+@dataclass
+class BeamStepDevice:
+    dtype: str
+    batch: int
+    beam: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    plan: B.Plan
+    prefix_len: np.ndarray
+    seq_len: np.ndarray
+    block_tables_h: np.ndarray
+    q: torch.Tensor
+    k_pool: torch.Tensor
+    v_pool: torch.Tensor
+    block_tables: torch.Tensor
+    cache_indirection: torch.Tensor
+    k_new: torch.Tensor
+    v_new: torch.Tensor
+    slots: torch.Tensor
+    workspace: torch.Tensor
+    o_part: torch.Tensor     # float [2, rows, Hq, D]: part 0 prefix, part 1 tail
+    lse_part: torch.Tensor   # float [2, rows, Hq]
+    out: torch.Tensor        # dtype [rows, Hq, D]
+    lse_out: torch.Tensor    # float [rows, Hq]
+
+    @property
+    def rows(self) -> int:
+        return self.batch * self.beam
+
+
+def upload_beam_step(inp, device="cuda", max_tail: Optional[int] = None,
+                     sm_scale: float = 0.0) -> BeamStepDevice:
+    """Copy a ``synth.BeamStepInputs`` to the GPU and create its plan."""
+    mt = inp.max_tail if max_tail is None else max_tail
+    desc = B.make_desc(inp.num_q_heads, inp.num_kv_heads, inp.head_dim, inp.page_size,
+                       inp.num_pages, inp.dtype, sm_scale=sm_scale, max_tail=mt)
+    plan = B.Plan(desc, max_requests=inp.batch, max_beam=inp.beam,
+                  max_blocks_per_seq=inp.max_blocks, max_seq_len=inp.max_seq_len, max_q_len=1)
+    rows, Hq, D = inp.batch * inp.beam, inp.num_q_heads, inp.head_dim
+    f32 = dict(device=device, dtype=torch.float32)
+    return BeamStepDevice(
+        dtype=inp.dtype, batch=inp.batch, beam=inp.beam, num_q_heads=Hq,
+        num_kv_heads=inp.num_kv_heads, head_dim=D, plan=plan,
+        prefix_len=inp.prefix_len.copy(), seq_len=inp.seq_len.copy(),
+        block_tables_h=inp.block_tables.copy(),
+        q=to_device(inp.q, inp.dtype, device),
+        k_pool=to_device(inp.k_pool, inp.dtype, device),
+        v_pool=to_device(inp.v_pool, inp.dtype, device),
+        block_tables=_i32(inp.block_tables, device),
+        cache_indirection=_i32(inp.cache_indirection, device),
+        k_new=to_device(inp.k_new, inp.dtype, device),
+        v_new=to_device(inp.v_new, inp.dtype, device),
+        slots=_i32(inp.slots, device),
+        workspace=torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device=device),
+        o_part=torch.zeros((2, rows, Hq, D), **f32),
+        lse_part=torch.zeros((2, rows, Hq), **f32),
+        out=torch.zeros((rows, Hq, D), device=device, dtype=TORCH_DTYPE[inp.dtype]),
+        lse_out=torch.zeros((rows, Hq), **f32),
+    )
+
+
+def plan_beam_step(s: BeamStepDevice, stream=None) -> None:
+    B.bsp_plan(s.plan, s.batch, s.beam, 1, s.prefix_len, s.seq_len, s.block_tables_h,
+               s.workspace, stream)
+
+
+def write_current_tokens(s: BeamStepDevice, stream=None) -> None:
+    n = int(s.slots.numel())
+    B.bsp_write_kv(s.plan, s.k_new, s.v_new, s.num_kv_heads * s.head_dim, s.slots, n,
+                   s.k_pool, s.v_pool, stream)
+
+
+def run_beam_step(s: BeamStepDevice, stream=None, write: bool = True) -> None:
+    """write_kv + prefix + tail + merge for the current plan (plan_beam_step first)."""
+    if write:
+        write_current_tokens(s, stream)
+    B.bsp_prefix_attn(s.plan, s.q, s.k_pool, s.v_pool, s.o_part[0], s.lse_part[0], stream)
+    B.bsp_tail_attn(s.plan, s.q, s.k_pool, s.v_pool, s.block_tables, s.cache_indirection,
+                    s.o_part[1], s.lse_part[1], stream)
+    rows = s.rows
+    B.bsp_merge(rows, s.num_q_heads, s.head_dim, 2, s.o_part, s.lse_part,
+                rows * s.num_q_heads * s.head_dim, rows * s.num_q_heads, s.out, s.dtype,
+                s.lse_out, stream)
+
+
+@dataclass
+class CachedPrefixDevice:
+    dtype: str
+    q_len: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    cache_pages: int
+    plan_cache: B.Plan
+    plan_new: B.Plan
+    valid_rows: int
+    bt_cache: np.ndarray
+    bt_new: np.ndarray
+    q: torch.Tensor
+    k_pool: torch.Tensor
+    v_pool: torch.Tensor
+    new_k: torch.Tensor
+    new_v: torch.Tensor
+    slots: torch.Tensor
+    ws_cache: torch.Tensor
+    ws_new: torch.Tensor
+    o_part: Optional[torch.Tensor] = None
+    lse_part: Optional[torch.Tensor] = None
+    out: Optional[torch.Tensor] = None
+    lse_out: Optional[torch.Tensor] = None
+    n_split: int = 1
+
+
+def upload_cached_prefix(inp, device="cuda", page_size: int = 32, key_bucket: int = 256,
+                         kv_split: Optional[int] = None, causal: bool = True,
+                         pool_fill: float = float("nan")) -> CachedPrefixDevice:
+    """Lay a ``synth.CachedPrefixInputs`` out as identity pages plus scratch pages.
+
+    The cache allocation ``[max_cache_rows, Hkv, D]`` becomes pages
+    ``0 .. cache_pages-1`` (page p holds rows p*ps .. p*ps+ps-1); this call's
+    rows go to scratch pages after them through ``bsp_write_kv``.
+    ``kv_split`` defaults to 256 keys per chunk for one-row decode, else 0.
+    """
+    from synth import paged_from_rows  # layout only
+
+    ps = page_size
+    Sq, Hq, D = inp.q.shape
+    Hkv = inp.cache_k.shape[1]
+    rows = inp.max_cache_rows
+    cache_pages = -(-rows // ps)
+    new_pages = -(-Sq // ps)
+    num_pages = cache_pages + new_pages
+    split = (256 if Sq == 1 else 0) if kv_split is None else kv_split
+    mk = lambda **kw: B.make_desc(Hq, Hkv, D, ps, num_pages, inp.dtype, **kw)  # noqa: E731
+    d_cache = mk(key_bucket=key_bucket, max_cache_rows=rows, kv_split=split)
+    d_new = mk(mask=B.BSP_MASK_CAUSAL if causal else B.BSP_MASK_NONE)
+    plan_cache = B.Plan(d_cache, 1, 1, cache_pages, rows, Sq)
+    plan_new = B.Plan(d_new, 1, 1, new_pages, Sq, Sq)
+    kpool = paged_from_rows(inp.cache_k, ps, num_pages, fill=pool_fill)
+    vpool = paged_from_rows(inp.cache_v, ps, num_pages, fill=pool_fill)
+    bt_cache = np.arange(cache_pages, dtype=np.int32).reshape(1, 1, -1)
+    bt_new = (cache_pages + np.arange(new_pages, dtype=np.int32)).reshape(1, 1, -1)
+    slots = (cache_pages * ps + np.arange(Sq)).astype(np.int32)
+    return CachedPrefixDevice(
+        dtype=inp.dtype, q_len=Sq, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=ps,
+        cache_pages=cache_pages, plan_cache=plan_cache, plan_new=plan_new,
+        valid_rows=int(inp.valid_rows), bt_cache=bt_cache, bt_new=bt_new,
+        q=to_device(inp.q.reshape(1, 1, Sq, Hq, D), inp.dtype, device),
+        k_pool=to_device(kpool, inp.dtype, device), v_pool=to_device(vpool, inp.dtype, device),
+        new_k=to_device(inp.new_k, inp.dtype, device), new_v=to_device(inp.new_v, inp.dtype, device),
+        slots=_i32(slots, device),
+        ws_cache=torch.zeros(plan_cache.workspace_bytes, dtype=torch.uint8, device=device),
+        ws_new=torch.zeros(plan_new.workspace_bytes, dtype=torch.uint8, device=device),
+    )
+
+
+def plan_cached_prefix(c: CachedPrefixDevice, stream=None) -> None:
+    L = np.array([c.valid_rows], np.int32)
+    Sq = np.array([c.q_len], np.int32)
+    B.bsp_plan(c.plan_cache, 1, 1, c.q_len, L, L, c.bt_cache, c.ws_cache, stream)
+    B.bsp_plan(c.plan_new, 1, 1, c.q_len, Sq, Sq, c.bt_new, c.ws_new, stream)
+    n_split = c.plan_cache.num_splits
+    if c.o_part is None or c.n_split != n_split:
+        dev = c.q.device
+        rows, Hq, D = c.q_len, c.num_q_heads, c.head_dim
+        c.n_split = n_split
+        c.o_part = torch.zeros((n_split + 1, rows, Hq, D), device=dev, dtype=torch.float32)
+        c.lse_part = torch.zeros((n_split + 1, rows, Hq), device=dev, dtype=torch.float32)
+        c.out = torch.zeros((rows, Hq, D), device=dev, dtype=TORCH_DTYPE[c.dtype])
+        c.lse_out = torch.zeros((rows, Hq), device=dev, dtype=torch.float32)
+
+
+def run_cached_prefix(c: CachedPrefixDevice, stream=None) -> None:
+    """write new rows + cache segment + new-row segment + n-way merge."""
+    Hkv, D = c.num_kv_heads, c.head_dim
+    B.bsp_write_kv(c.plan_new, c.new_k, c.new_v, Hkv * D, c.slots, c.q_len, c.k_pool, c.v_pool,
+                   stream)
+    ns = c.n_split
+    B.bsp_prefix_attn(c.plan_cache, c.q, c.k_pool, c.v_pool, c.o_part[:ns], c.lse_part[:ns],
+                      stream)
+    B.bsp_prefix_attn(c.plan_new, c.q, c.k_pool, c.v_pool, c.o_part[ns], c.lse_part[ns], stream)
+    rows = c.q_len
+    B.bsp_merge(rows, c.num_q_heads, D, ns + 1, c.o_part, c.lse_part, rows * c.num_q_heads * D,
+                rows * c.num_q_heads, c.out, c.dtype, c.lse_out, stream)

@@ -1,0 +1,238 @@
+"""Benchmark: one cascade beam-decode attention step per layer on one MI355X.
+
+A step is bsp_write_kv (current tokens) + bsp_prefix_attn + bsp_tail_attn +
+bsp_merge over all B*W beams of one layer. Consecutive timed steps rotate over
+several layers, each with its own KV pool, query and new-token buffers, so
+every step reads its prompt pages from HBM rather than from the 256 MB
+last-level cache (as consecutive layers of a model would). Inputs are seeded
+synthetic draws already resident in HBM when the timed region starts.
+
+Prints one JSON line. The dominant kernel's roofline entry uses HIP events
+recorded on the launch stream around every timed launch of it.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "beam-decode attention steps/s per layer + achieved HBM GB/s vs roofline"
+HBM_PEAK_GBPS = 8000.0
+EBYTES = {"f32": 4, "f16": 2, "bf16": 2}
+WORKLOADS = {
+    "qwen3_0p6b": "Qwen3-0.6B-like layer: 16 Q / 8 KV heads, head_dim 128, bf16, 32-token pages, "
+                  "64 requests x beam 30, prompts U{400..600}, tails U{0..4}",
+    "wide_beam": "wide-beam recommendation shape: 16 Q / 8 KV heads, head_dim 128, bf16, 32-token "
+                 "pages shuffled, 128 requests x beam 96, prompts U{2800..3200}, tails U{0..8}",
+    "qwen3_4b": "Qwen3-4B-like layer: 32 Q / 8 KV heads, head_dim 128, fp16, 32-token pages, "
+                "64 requests x beam 30, prompts U{1600..2400}, tails U{1..4}",
+}
+
+
+def algorithmic_bytes(inp):
+    """Bytes the method must move in one step, and those of the prefix kernel alone.
+
+    step: shared prompt K+V once per request + distinct tail rows gathered + Q
+    read + O written + current-token K/V written. prefix kernel: shared prompt
+    K+V once per request + Q read + its fp32 partial (o and lse) written.
+    """
+    e = EBYTES[inp.dtype]
+    Hkv, D, Hq = inp.num_kv_heads, inp.head_dim, inp.num_q_heads
+    row = Hkv * D * e * 2                    # one position's K and V over all KV heads
+    prefix = int(inp.prefix_len.astype(np.int64).sum()) * row
+    uniq = 0
+    ps = inp.page_size
+    for b in range(inp.batch):
+        P, S = int(inp.prefix_len[b]), int(inp.seq_len[b])
+        seen = set()
+        for j in range(P, S):
+            for src in np.unique(inp.cache_indirection[b, :, j]):
+                seen.add((int(inp.block_tables[b, src, j // ps]), j % ps))
+        uniq += len(seen)
+    rows = inp.batch * inp.beam
+    q_bytes = rows * Hq * D * e
+    o_bytes = rows * Hq * D * e
+    write = len(inp.slots) * row
+    step = prefix + uniq * row + q_bytes + o_bytes + write
+    prefix_kernel = prefix + q_bytes + rows * Hq * (D + 1) * 4
+    return step, prefix_kernel
+
+
+def cpu_baseline(config: str, seed: int, budget_s: float):
+    """Time the fp64 oracle on the first requests of the same workload."""
+    import oracle
+    import synth
+    from threadpoolctl import threadpool_info
+
+    spec = synth.BEAM_CONFIGS[config]
+    n = 1
+    t_used = 0.0
+    while True:
+        inp = synth.make_beam_step(config, seed, batch=n, garbage="unit")
+        kp, vp = oracle.write_kv(inp.k_pool, inp.v_pool, inp.slots, inp.k_new, inp.v_new,
+                                 inp.page_size)
+        inp.k_pool, inp.v_pool = kp, vp
+        t0 = time.perf_counter()
+        oracle.beam_decode_attention(inp)
+        t_used = time.perf_counter() - t0
+        if t_used * 2 > budget_s or n * 2 > spec.batch:
+            break
+        n *= 2
+    threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    steps_per_s = (n / spec.batch) / t_used
+    return {"value": steps_per_s, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {spec.batch} requests of the same workload (seed {seed}), "
+                      f"{t_used:.2f} s of fp64 numpy, scaled to a whole step"}
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="qwen3_0p6b", choices=sorted(WORKLOADS))
+    ap.add_argument("--layers", type=int, default=0,
+                    help="rotating layer copies (0: enough to exceed 1 GB of KV)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--naive", action="store_true", help="also time the per-beam comparator")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this path runs on a "
+              "single MI355X; see DESIGN.md for how it would shard.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    from beam_search_shared_amd import _binding as B
+    from beam_search_shared_amd import step as S
+
+    B.load_library()
+    dev = "cuda"
+    inp = synth.make_beam_step(args.config, args.seed, garbage="unit")
+    step_bytes, prefix_bytes = algorithmic_bytes(inp)
+    base = S.upload_beam_step(inp, dev)
+    pool_bytes = base.k_pool.numel() * base.k_pool.element_size() * 2
+    layers = args.layers or max(2, int(np.ceil(1.0e9 / pool_bytes)))
+    copies = [base]
+    for _ in range(layers - 1):
+        c = S.BeamStepDevice(**{**base.__dict__})
+        c.q = base.q.clone()
+        c.k_pool = base.k_pool.clone()
+        c.v_pool = base.v_pool.clone()
+        c.k_new = base.k_new.clone()
+        c.v_new = base.v_new.clone()
+        copies.append(c)
+    t_plan = time.perf_counter()
+    S.plan_beam_step(base)
+    t_plan = time.perf_counter() - t_plan
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+
+    def one(i, timed_ev=None):
+        c = copies[i % layers]
+        S.write_current_tokens(c)
+        if timed_ev is not None:
+            timed_ev[0].record(stream)
+        B.bsp_prefix_attn(c.plan, c.q, c.k_pool, c.v_pool, c.o_part[0], c.lse_part[0])
+        if timed_ev is not None:
+            timed_ev[1].record(stream)
+        B.bsp_tail_attn(c.plan, c.q, c.k_pool, c.v_pool, c.block_tables, c.cache_indirection,
+                        c.o_part[1], c.lse_part[1])
+        rows = c.rows
+        B.bsp_merge(rows, c.num_q_heads, c.head_dim, 2, c.o_part, c.lse_part,
+                    rows * c.num_q_heads * c.head_dim, rows * c.num_q_heads, c.out, c.dtype,
+                    c.lse_out)
+
+    for i in range(args.warmup):
+        one(i)
+    B.bsp_check(base.plan)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one(i, ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    B.bsp_check(base.plan)
+    sec = t1 - t0
+    ms_per_step = sec / args.steps * 1e3
+    prefix_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    achieved = prefix_bytes / (prefix_ms * 1e-3) / 1e9
+
+    extra = {}
+    if args.naive:
+        out = torch.empty_like(base.out)
+        for i in range(3):
+            c = copies[i % layers]
+            B.bsp_naive_beam_attn(c.plan, c.q, c.k_pool, c.v_pool, c.block_tables,
+                                  c.cache_indirection, out)
+        torch.cuda.synchronize()
+        n_naive = max(3, min(20, args.steps // 10))
+        ta = time.perf_counter()
+        for i in range(n_naive):
+            c = copies[i % layers]
+            S.write_current_tokens(c)
+            B.bsp_naive_beam_attn(c.plan, c.q, c.k_pool, c.v_pool, c.block_tables,
+                                  c.cache_indirection, out)
+        torch.cuda.synchronize()
+        naive_ms = (time.perf_counter() - ta) / n_naive * 1e3
+        extra["naive_per_beam_ms_per_step"] = naive_ms
+        extra["cascade_speedup_vs_naive"] = naive_ms / ms_per_step
+
+    result = {
+        "metric": METRIC,
+        "value": args.steps / sec,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": inp.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOADS[args.config],
+            "name": args.config,
+            "batch": inp.batch,
+            "beam": inp.beam,
+            "layers_rotated": layers,
+            "step_alg_bytes": step_bytes,
+            "step_alg_gbps": step_bytes / (ms_per_step * 1e-3) / 1e9,
+            "plan_host_ms": t_plan * 1e3,
+            **extra,
+        },
+        "roofline": {
+            "kernel": "prefix_mfma_kernel (bsp_prefix_attn)",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": None,
+            "alg_bytes_per_launch": prefix_bytes,
+            "avg_launch_us": prefix_ms * 1e3,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args.config, args.seed, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

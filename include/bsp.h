@@ -1,0 +1,258 @@
+/*
+ * bsp.h — C ABI of libbsp: one decode step of cascade attention for wide beam
+ * search over a shared prompt, on a paged KV cache, for AMD MI355X (gfx950).
+ *
+ * The method (TensorRT-LLM PR #21738, "Add opt-in cascade attention for wide
+ * beam search on KVCM V2", Description: Problem and Solution): all beams of a
+ * request share one prompt, so the prompt's keys are attended once per request
+ * with every beam's query rows at once, each beam's own generated tail is
+ * attended separately through cache_indirection, and the two partial results
+ * are merged exactly through their log-sum-exp. A beam-1 variant bounds the
+ * key range to the valid cached prefix rounded up to 256 rows (Phi-4 cached-
+ * prefix PR, TensorRT-Model-Connect #2202: Exit Criteria, Implementation).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Device pointers belong to the caller. The library never allocates device
+ *   memory; its only allocation is the pinned host staging owned by a plan.
+ * - Every call is asynchronous and ordered on the caller's stream. Only
+ *   bsp_check and check mode (environment BSP_CHECK=1 when the plan is
+ *   created) wait for the device.
+ * - Errors: each call returns a bsp_status_t; bsp_last_error() gives a
+ *   message for the calling thread. A call that fails validation returns
+ *   before any launch and leaves every buffer unchanged. Indices are never
+ *   clamped (the eligibility commit of PR #21738 raises on a bad prompt page
+ *   index rather than clamping it).
+ * - Index values that only the device sees (slots, cache_indirection entries,
+ *   device block-table entries) are bounds-checked in the kernels: a bad one
+ *   is skipped and recorded in the plan workspace's error word, which
+ *   bsp_check reports.
+ * - Layouts (all row-major, innermost last):
+ *     K/V pool        [num_pages, num_kv_heads, page_size, head_dim]
+ *     q               [B, W, q_len, num_q_heads, head_dim]
+ *     block tables    int32 [B, W, max_blocks_per_seq]
+ *     cache_indirection int32 [B, W, max_seq_len]
+ *     partial o       float [n_parts][B * W * q_len][num_q_heads][head_dim]
+ *     partial lse     float [n_parts][B * W * q_len][num_q_heads]
+ *   Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ * - LSE is the natural log of the softmax denominator, scale included; an
+ *   empty key set gives o = 0 and lse = -inf.
+ */
+#ifndef BSP_H
+#define BSP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { BSP_F32 = 0, BSP_F16 = 1, BSP_BF16 = 2 } bsp_dtype_t;
+
+/* Self mask of the query rows when q_len > 1. */
+typedef enum {
+  BSP_MASK_NONE = 0,   /* every query row sees every valid key                 */
+  BSP_MASK_CAUSAL = 1  /* row i of q_len sees keys j <= n_keys - q_len + i     */
+} bsp_mask_t;
+
+typedef enum {
+  BSP_OK = 0,
+  BSP_ERR_ARG = 1,            /* null pointer, bad size, misaligned buffer        */
+  BSP_ERR_PAGE_INDEX = 2,     /* a host block-table entry outside [0, num_pages)  */
+  BSP_ERR_TAIL_OVERFLOW = 3,  /* a tail longer than the fixed max_tail            */
+  BSP_ERR_DTYPE = 4,          /* unsupported dtype                                 */
+  BSP_ERR_UNSUPPORTED = 5,    /* unsupported geometry (head_dim, page_size, ...)  */
+  BSP_ERR_STALE_PLAN = 6,     /* attention call on a plan with no bsp_plan yet    */
+  BSP_ERR_WORKSPACE = 7,      /* workspace missing or too small                    */
+  BSP_ERR_DEVICE_INDEX = 8,   /* a kernel met an out-of-range index (bsp_check)   */
+  BSP_ERR_HIP = 9             /* a HIP runtime call failed                          */
+} bsp_status_t;
+
+/* Geometry of one attention layer. */
+typedef struct {
+  int32_t num_q_heads;    /* Hq, a multiple of num_kv_heads                          */
+  int32_t num_kv_heads;   /* Hkv                                                      */
+  int32_t head_dim;       /* D: 64, 128 or 256                                        */
+  int32_t page_size;      /* rows per page: a power of two, 1..1024                   */
+  int32_t num_pages;      /* pages in each of the K and V pools                       */
+  int32_t dtype;          /* bsp_dtype_t of q, the pools and the final output         */
+  float sm_scale;         /* softmax scale; 0 selects 1/sqrt(head_dim)                */
+  int32_t max_tail;       /* 0: tail length set per step; > 0: fixed padded tail
+                             length (graph-style), a longer tail is an error
+                             (PR #21738: Correctness and limits; MAX_TAIL thread)     */
+  int32_t key_bucket;     /* 0: beam mode, the shared keys are the prompt rows;
+                             > 0: cached-prefix mode, rows bound per request =
+                             valid rows rounded up to key_bucket, capped at
+                             max_cache_rows, 1 for an empty cache (PR #2202)           */
+  int32_t max_cache_rows; /* cap of the bound rows in cached-prefix mode              */
+  int32_t mask;           /* bsp_mask_t of the query rows (q_len > 1)                 */
+  int32_t kv_split;       /* 0: one pass over the shared keys; > 0: split them into
+                             chunks of this many keys (a multiple of 64), each
+                             giving its own partial (o, lse) to merge afterwards      */
+} bsp_layer_desc_t;
+
+typedef struct bsp_plan_s* bsp_plan_t;
+
+/* bsp_plan_create flags */
+#define BSP_PLAN_HOST_ONLY 1u /* validation and table building only: no HIP calls,
+                                 bsp_plan must get a null workspace, and only the
+                                 bsp_debug_* host getters may follow              */
+
+/* Thread-local message of the last failed call on this thread ("" if none). */
+const char* bsp_last_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t bsp_version(void);
+
+/*
+ * Create a per-step plan object for one layer geometry and its capacity. The
+ * plan is made once per step and read by every layer of that step (PR #21738,
+ * first commit: the host plan runs once per step before graph capture or
+ * replay). It owns two pinned host staging buffers and nothing on the device.
+ * Errors: BSP_ERR_ARG, BSP_ERR_UNSUPPORTED, BSP_ERR_DTYPE, BSP_ERR_HIP.
+ */
+bsp_status_t bsp_plan_create(const bsp_layer_desc_t* desc, int32_t max_requests,
+                             int32_t max_beam, int32_t max_blocks_per_seq,
+                             int32_t max_seq_len, int32_t max_q_len, uint32_t flags,
+                             bsp_plan_t* out);
+
+/* Bytes of device workspace the caller must provide to bsp_plan (256-aligned,
+ * caller-owned; zero-filled once after allocation). 0 on a null plan. */
+size_t bsp_plan_workspace_bytes(bsp_plan_t plan);
+
+/* Destroy a plan (waits for its in-flight staging copies). Null is a no-op. */
+void bsp_plan_destroy(bsp_plan_t plan);
+
+/*
+ * Plan one step: validate lengths and page ids on the host, build the shared-
+ * key page table of each request from beam 0's block table (PR #21738, KV-
+ * cache-manager-V2 commit: the prompt page table is beam 0's), the tail
+ * lengths and the key bounds, and copy them into workspace_d with an
+ * asynchronous copy from pinned staging on `stream`, without waiting for the
+ * stream (PR #21738, commit making re-planning non-blocking).
+ *
+ *   B, W, q_len          requests, beams per request, query rows per beam
+ *   prefix_len_h[B]      beam mode: prompt rows shared by the W beams (P_b);
+ *                        cached-prefix mode: valid cached rows (L_b)
+ *   seq_len_h[B]         beam mode: cached rows of each beam, P_b + tail (S_b);
+ *                        cached-prefix mode: must equal prefix_len_h
+ *   block_tables_h       host copy of the block tables, int32 [B][W][max_blocks]
+ *   workspace_d          caller device buffer of bsp_plan_workspace_bytes bytes
+ *                        (null for a BSP_PLAN_HOST_ONLY plan)
+ * Checks: 0 <= P_b <= S_b <= max_seq_len; tail <= max_tail when max_tail > 0
+ * (BSP_ERR_TAIL_OVERFLOW); every block-table entry the step reads (beam 0's
+ * shared blocks, every beam's tail blocks) in [0, num_pages)
+ * (BSP_ERR_PAGE_INDEX); in check mode, also that all beams share the full
+ * prompt blocks. On failure the previous plan is dropped (BSP_ERR_STALE_PLAN
+ * until the next successful call).
+ */
+bsp_status_t bsp_plan(bsp_plan_t plan, int32_t B, int32_t W, int32_t q_len,
+                      const int32_t* prefix_len_h, const int32_t* seq_len_h,
+                      const int32_t* block_tables_h, void* workspace_d,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/* Number of partial states bsp_prefix_attn writes for the current plan (1 when
+ * kv_split is 0), and the tail length each beam is padded to. -1 if unplanned. */
+int32_t bsp_plan_num_splits(bsp_plan_t plan);
+int32_t bsp_plan_tail_len(bsp_plan_t plan);
+
+/*
+ * Write n new tokens' K and V rows into the pools: token i goes to page
+ * slots[i] / page_size, row slots[i] % page_size, for all KV heads, K and V in
+ * one launch (TensorRT-LLM PR #18614, Description: one launch derives page and
+ * row from the flat slot and writes K and V together).
+ *   k_new, v_new   device, token i's [num_kv_heads, head_dim] block starts at
+ *                  element i * src_row_stride (16-byte aligned)
+ *   slots_d        device int32 [n]; a slot outside [0, num_pages*page_size)
+ *                  is skipped and recorded in the error word
+ * n == 0 succeeds without a launch. Uses the plan's geometry and workspace.
+ */
+bsp_status_t bsp_write_kv(bsp_plan_t plan, const void* k_new, const void* v_new,
+                          int64_t src_row_stride, const int32_t* slots_d, int32_t n,
+                          void* k_pool, void* v_pool, hipStream_t stream);
+
+/*
+ * Shared-key attention: for each request b and KV head g, all W * q_len * G
+ * query rows (G = num_q_heads / num_kv_heads) against the request's shared
+ * keys, once per request (PR #21738, Solution: the prompt is attended once per
+ * request; FA4 commit: one group of beam_width queries per request). Keys are
+ * rows [0, valid_b) of the request's page table; in cached-prefix mode rows in
+ * [valid_b, bound_b) are masked and rows past the bound are never read.
+ * Writes bsp_plan_num_splits() normalised partial states: o_part (float,
+ * [n_split][B*W*q_len][Hq][D]) and lse_part (float, [n_split][B*W*q_len][Hq]).
+ * bf16/f16 run on MFMA; f32 runs a vector-ALU kernel.
+ */
+bsp_status_t bsp_prefix_attn(bsp_plan_t plan, const void* q, const void* k_pool,
+                             const void* v_pool, float* o_part, float* lse_part,
+                             hipStream_t stream);
+
+/*
+ * Tail attention: each beam's G query rows against its own tail positions
+ * P_b <= j < S_b, gathered through cache_indirection: position j of beam k is
+ * read from beam src = cache_indirection[b][k][j], page
+ * block_tables[b][src][j / page_size], row j % page_size (PR #21738, Solution
+ * and fused-tail commit). q_len must be 1. Writes o_tail (float,
+ * [B*W][Hq][D]) and lse_tail (float, [B*W][Hq]); an empty tail gives o = 0,
+ * lse = -inf.
+ *   block_tables_d      device int32 [B][W][max_blocks_per_seq]
+ *   cache_indirection_d device int32 [B][W][max_seq_len]
+ */
+bsp_status_t bsp_tail_attn(bsp_plan_t plan, const void* q, const void* k_pool,
+                           const void* v_pool, const int32_t* block_tables_d,
+                           const int32_t* cache_indirection_d, float* o_tail,
+                           float* lse_tail, hipStream_t stream);
+
+/*
+ * Exact merge of n_parts partial states over disjoint key sets (PR #21738,
+ * Solution: merged exactly with the log-sum-exp):
+ *   lse = ln sum_p exp(lse_p),  o = sum_p exp(lse_p - lse) * o_p.
+ * Parts with lse = -inf drop out; all empty gives o = 0, lse = -inf.
+ *   o_parts   float, part p at o_parts + p * o_part_stride, [rows][heads][head_dim]
+ *   lse_parts float, part p at lse_parts + p * lse_part_stride, [rows][heads]
+ *   o_out     out_dtype [rows][heads][head_dim]; lse_out float [rows][heads] or null
+ */
+bsp_status_t bsp_merge(int32_t rows, int32_t heads, int32_t head_dim, int32_t n_parts,
+                       const float* o_parts, const float* lse_parts, int64_t o_part_stride,
+                       int64_t lse_part_stride, void* o_out, int32_t out_dtype,
+                       float* lse_out, hipStream_t stream);
+
+/*
+ * Comparator, not part of the cascade: per-beam attention over each beam's
+ * whole sequence, reading the shared prompt once per (beam, KV head) through
+ * the beam's own block table, as the decode kernel that the cascade replaces
+ * does (PR #21738, first commit: the legacy kernel re-reads the prompt KV once
+ * per beam and head). Final output o_out (dtype, [B*W][Hq][D]) and lse_out
+ * (float, [B*W][Hq], may be null). q_len must be 1.
+ */
+bsp_status_t bsp_naive_beam_attn(bsp_plan_t plan, const void* q, const void* k_pool,
+                                 const void* v_pool, const int32_t* block_tables_d,
+                                 const int32_t* cache_indirection_d, void* o_out,
+                                 float* lse_out, hipStream_t stream);
+
+/* Wait for `stream`, then report (and clear) any index fault the kernels
+ * recorded in the plan's workspace: BSP_ERR_DEVICE_INDEX with a message. */
+bsp_status_t bsp_check(bsp_plan_t plan, hipStream_t stream);
+
+/* Test hooks -------------------------------------------------------------- */
+
+/* Host copy of the current plan's tables (valid for host-only plans too):
+ * indptr[B+1], pages[indptr[B]], and per request n_keys (rows the page table
+ * covers), valid (attended rows) and tail length. Any pointer may be null. */
+bsp_status_t bsp_debug_plan_tables(bsp_plan_t plan, int32_t* indptr_h, int32_t* pages_h,
+                                   int32_t* n_keys_h, int32_t* valid_h, int32_t* tail_h);
+
+/* Device: resolve every tail key to its flat pool slot (page * page_size +
+ * row), int32 [B][W][tail_len], -1 past each request's tail; the same index
+ * path bsp_tail_attn reads through. */
+bsp_status_t bsp_debug_tail_slots(bsp_plan_t plan, const int32_t* block_tables_d,
+                                  const int32_t* cache_indirection_d, int32_t* slots_d,
+                                  hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSP_H */

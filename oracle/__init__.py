@@ -11,6 +11,7 @@ closed forms, invariants and printed values); none is "parity unpinned".
 
 from .attention import (  # noqa: F401
     attend,
+    beam_attention_one,
     beam_decode_attention,
     beam_partial_attention,
     bucket_rows,

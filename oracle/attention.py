@@ -98,28 +98,46 @@ def sequence_slots(b: int, k: int, prefix_len, seq_len, block_tables, cache_indi
     return np.asarray(pages, dtype=np.int64), np.asarray(rows, dtype=np.int64)
 
 
-def _beam_attention(inp, positions_of, scale):
-    B, W = inp.block_tables.shape[:2]
+def _one_beam(inp, b: int, k: int, positions, scale: float):
+    """Attention of beam ``k`` of request ``b`` over the given sequence positions."""
     q = inp.q
     q_len, Hq, D = q.shape[2], q.shape[3], q.shape[4]
     Hkv = inp.k_pool.shape[1]
     G = Hq // Hkv
+    pages, rows = sequence_slots(b, k, inp.prefix_len, inp.seq_len, inp.block_tables,
+                                 inp.cache_indirection, inp.page_size, list(positions))
+    K = inp.k_pool[pages, :, rows, :].astype(np.float64)   # [n, Hkv, D]
+    V = inp.v_pool[pages, :, rows, :].astype(np.float64)
+    o = np.zeros((q_len, Hq, D))
+    lse = np.full((q_len, Hq), NEG_INF)
+    for i in range(q_len):
+        for g in range(Hkv):             # query heads g*G .. g*G+G-1 read KV head g
+            heads = slice(g * G, (g + 1) * G)
+            oo, ll = attend(q[b, k, i, heads], K[:, g, :], V[:, g, :], scale)
+            o[i, heads] = oo
+            lse[i, heads] = ll
+    return o, lse
+
+
+def _beam_attention(inp, positions_of, scale):
+    B, W = inp.block_tables.shape[:2]
+    q = inp.q
+    q_len, Hq, D = q.shape[2], q.shape[3], q.shape[4]
     o = np.zeros((B, W, q_len, Hq, D))
     lse = np.full((B, W, q_len, Hq), NEG_INF)
     for b in range(B):
         for k in range(W):
-            pos = list(positions_of(b))
-            pages, rows = sequence_slots(b, k, inp.prefix_len, inp.seq_len, inp.block_tables,
-                                         inp.cache_indirection, inp.page_size, pos)
-            K = inp.k_pool[pages, :, rows, :].astype(np.float64)   # [n, Hkv, D]
-            V = inp.v_pool[pages, :, rows, :].astype(np.float64)
-            for i in range(q_len):
-                for g in range(Hkv):     # query heads g*G .. g*G+G-1 read KV head g
-                    heads = slice(g * G, (g + 1) * G)
-                    oo, ll = attend(q[b, k, i, heads], K[:, g, :], V[:, g, :], scale)
-                    o[b, k, i, heads] = oo
-                    lse[b, k, i, heads] = ll
+            o[b, k], lse[b, k] = _one_beam(inp, b, k, positions_of(b), scale)
     return o, lse
+
+
+def beam_attention_one(inp, b: int, k: int, scale: Optional[float] = None):
+    """``beam_decode_attention`` of a single beam: ``o [q_len, Hq, D]``, ``lse [q_len, Hq]``.
+
+    Used to check sampled outputs of full-size runs.
+    """
+    sc = default_scale(inp.q.shape[-1]) if scale is None else scale
+    return _one_beam(inp, b, k, range(int(inp.seq_len[b])), sc)
 
 
 def beam_decode_attention(inp, scale: Optional[float] = None):

@@ -1,0 +1,296 @@
+"""GPU parity: every entry point against the fp64 oracle, element by element.
+
+Sizes are the configs' own shapes with fewer requests (several MFMA tiles and
+a ragged last tile per request), plus the edge cases: fp32 at 1e-5, empty
+tails, group sizes 1..8, head_dim 64/128/256, shuffled and strided page ids,
+fixed padded tails, bad device-side indices, and the cached-prefix variant at
+its edge lengths.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from beam_search_shared_amd import _binding as B
+from beam_search_shared_amd import step as S
+from synth import BeamConfig
+from tests.gpu_util import TOL, assert_close, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def _applied(inp):
+    kp, vp = oracle.write_kv(inp.k_pool, inp.v_pool, inp.slots, inp.k_new, inp.v_new,
+                             inp.page_size)
+    inp.k_pool, inp.v_pool = kp, vp
+    return inp
+
+
+# ------------------------------------------------------------------ merge
+
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("n_parts", [1, 2, 5])
+def test_merge_matches_oracle(out_dtype, n_parts):
+    say(f"merge out={out_dtype} parts={n_parts}")
+    rng = np.random.default_rng(n_parts)
+    rows, heads, D = 37, 6, 128
+    o = rng.standard_normal((n_parts, rows, heads, D)).astype(np.float32)
+    lse = (rng.standard_normal((n_parts, rows, heads)) * 3).astype(np.float32)
+    lse[0, :5] = -np.inf                   # some parts empty
+    lse[:, 5:7] = -np.inf                  # every part empty for two rows
+    o[0, :5] = 0.0
+    o[:, 5:7] = 0.0
+    ref_o, ref_l = oracle.merge_states(list(o), list(lse))
+    og = torch.from_numpy(o).to(DEV)
+    lg = torch.from_numpy(lse).to(DEV)
+    out = torch.empty((rows, heads, D), device=DEV, dtype=S.TORCH_DTYPE[out_dtype])
+    lout = torch.empty((rows, heads), device=DEV)
+    B.bsp_merge(rows, heads, D, n_parts, og, lg, rows * heads * D, rows * heads, out, out_dtype,
+                lout)
+    torch.cuda.synchronize()
+    tol_o = 1e-5 if out_dtype == "f32" else 8e-3
+    o_gpu = out.float().cpu().numpy()
+    assert np.abs(o_gpu - ref_o).max() <= tol_o
+    l_gpu = lout.cpu().numpy()
+    fin = np.isfinite(ref_l)
+    assert np.array_equal(np.isneginf(l_gpu), ~fin)
+    assert np.abs(l_gpu[fin] - ref_l[fin]).max() <= 1e-5
+
+
+# ----------------------------------------------------------------- KV write
+
+@pytest.mark.parametrize("cfg", ["tiny", "qwen3_0p6b", "qwen3_4b"])
+def test_write_kv_is_bit_exact(cfg):
+    inp = synth.make_beam_step(cfg, 3, batch=3 if cfg != "tiny" else None)
+    say(f"write_kv {cfg} n={len(inp.slots)}")
+    ref_k, ref_v = oracle.write_kv(inp.k_pool, inp.v_pool, inp.slots, inp.k_new, inp.v_new,
+                                   inp.page_size)
+    s = S.upload_beam_step(inp, DEV)
+    S.plan_beam_step(s)
+    S.write_current_tokens(s)
+    B.bsp_check(s.plan)
+    assert torch.equal(s.k_pool.cpu(), S.to_device(ref_k, inp.dtype, "cpu"))
+    assert torch.equal(s.v_pool.cpu(), S.to_device(ref_v, inp.dtype, "cpu"))
+
+
+def test_write_kv_skips_and_reports_bad_slots():
+    inp = synth.make_beam_step("qwen3_0p6b", 4, batch=2, tail_range=(2, 4))
+    s = S.upload_beam_step(inp, DEV)
+    S.plan_beam_step(s)
+    before_k = s.k_pool.clone()
+    slots = s.slots.clone()
+    slots[1] = inp.num_pages * inp.page_size          # one past the pool
+    slots[3] = -5
+    good = torch.ones(len(slots), dtype=torch.bool)
+    good[[1, 3]] = False
+    B.bsp_write_kv(s.plan, s.k_new, s.v_new, s.num_kv_heads * s.head_dim, slots,
+                   len(slots), s.k_pool, s.v_pool)
+    with pytest.raises(B.BspError) as ei:
+        B.bsp_check(s.plan)
+    assert ei.value.name == "BSP_ERR_DEVICE_INDEX"
+    B.bsp_check(s.plan)  # the error word was cleared
+    ref_k, _ = oracle.write_kv(inp.k_pool, inp.v_pool, inp.slots[good.numpy()],
+                               inp.k_new[good.numpy()], inp.v_new[good.numpy()], inp.page_size)
+    assert torch.equal(s.k_pool.cpu(), S.to_device(ref_k, inp.dtype, "cpu"))
+    assert not torch.equal(s.k_pool, before_k)
+
+
+# ----------------------------------------------------------- index resolution
+
+def _tail_slots_gpu(s, pad):
+    out = torch.full((s.batch, s.beam, max(pad, 1)), -7, dtype=torch.int32, device=DEV)
+    B.bsp_debug_tail_slots(s.plan, s.block_tables, s.cache_indirection, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()[:, :, :pad]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_tail_slots_bit_exact(seed):
+    cfgs = [BeamConfig("idx", 3, 5, 4, 2, 64, "bf16", ps, (1, 40), (0, 9), bool(seed % 2))
+            for ps in (4, 8, 16)]
+    for cfg in cfgs:
+        inp = synth.make_beam_step(cfg, seed, page_stride=1 + seed % 2)
+        say(f"tail slots seed={seed} ps={cfg.page_size}")
+        s = S.upload_beam_step(inp, DEV)
+        S.plan_beam_step(s)
+        pad = s.plan.tail_len
+        ref = oracle.tail_slots(inp.prefix_len, inp.seq_len, inp.block_tables,
+                                inp.cache_indirection, inp.page_size, pad)
+        assert np.array_equal(_tail_slots_gpu(s, pad), ref)
+
+
+def test_bad_cache_indirection_is_skipped_and_reported():
+    inp = synth.make_beam_step("qwen3_0p6b", 5, batch=2, tail_range=(3, 4))
+    s = S.upload_beam_step(inp, DEV)
+    S.plan_beam_step(s)
+    P = int(inp.prefix_len[1])
+    s.cache_indirection[1, 4, P + 1] = inp.beam      # parent beam out of range
+    S.run_beam_step(s)
+    with pytest.raises(B.BspError) as ei:
+        B.bsp_check(s.plan)
+    assert ei.value.name == "BSP_ERR_DEVICE_INDEX"
+    assert not torch.isnan(s.out.float()).any()
+
+
+# ---------------------------------------------------------- whole beam step
+
+STEP_CASES = {
+    "tiny_f32": dict(cfg="tiny"),
+    "qwen3_0p6b_bf16": dict(cfg="qwen3_0p6b", batch=3),
+    "wide_beam_bf16": dict(cfg="wide_beam", batch=2),
+    "wide_beam_fixed_tail8": dict(cfg="wide_beam", batch=2, tail_range=(8, 8)),
+    "qwen3_4b_f16_d128": dict(cfg="qwen3_4b", batch=2),
+    "qwen3_4b_f16_d64": dict(cfg="qwen3_4b", batch=2, head_dim=64),
+    "qwen3_4b_f16_d256": dict(cfg="qwen3_4b", batch=2, head_dim=256),
+    "no_tails_bf16": dict(cfg="qwen3_0p6b", batch=3, tail_range=(0, 0)),
+    "strided_pages_bf16": dict(cfg="qwen3_0p6b", batch=2, page_stride=2, shuffle_pages=True),
+    "f32_d128": dict(cfg="qwen3_0p6b", batch=2, dtype="f32", prefix_range=(30, 90)),
+    "f32_d256": dict(cfg="qwen3_4b", batch=1, dtype="f32", head_dim=256, prefix_range=(50, 90)),
+}
+GROUP_CASES = {f"group{g}_{dt}": (g, dt) for g, dt in
+               [(1, "bf16"), (2, "f16"), (3, "f16"), (4, "bf16"), (6, "bf16"), (8, "f16")]}
+
+
+def _run_and_check(inp, what, max_tail=None):
+    s = S.upload_beam_step(inp, DEV, max_tail=max_tail)
+    S.plan_beam_step(s)
+    S.run_beam_step(s)
+    B.bsp_check(s.plan)
+    torch.cuda.synchronize()
+    ref = _applied(inp)
+    po, pl = oracle.beam_partial_attention(ref, "prefix")
+    to, tl = oracle.beam_partial_attention(ref, "tail")
+    fo, fl = oracle.beam_decode_attention(ref)
+    assert_close(s.o_part[0], s.lse_part[0], po, pl, "f32" if inp.dtype == "f32" else inp.dtype,
+                 f"{what} prefix partial")
+    assert_close(s.o_part[1], s.lse_part[1], to, tl, "f32" if inp.dtype == "f32" else inp.dtype,
+                 f"{what} tail partial")
+    return assert_close(s.out, s.lse_out, fo, fl, inp.dtype, f"{what} output")
+
+
+@pytest.mark.parametrize("case", list(STEP_CASES))
+@pytest.mark.parametrize("seed", [0, 1])
+def test_beam_step_matches_oracle(case, seed):
+    kw = dict(STEP_CASES[case])
+    cfg = kw.pop("cfg")
+    inp = synth.make_beam_step(cfg, seed, **kw)
+    say(f"beam step {case} seed={seed} B={inp.batch} W={inp.beam} D={inp.head_dim} "
+        f"P={inp.prefix_len.tolist()} T={inp.tail_len.tolist()}")
+    mt = 8 if "fixed_tail" in case else None
+    err = _run_and_check(inp, case, max_tail=mt)
+    say(f"  max |dO| = {err:.3g}")
+
+
+@pytest.mark.parametrize("case", list(GROUP_CASES))
+def test_beam_step_group_sizes(case):
+    g, dt = GROUP_CASES[case]
+    cfg = BeamConfig(case, 2, 7, 2 * g, 2, 128, dt, 16, (70, 150), (0, 5), True)
+    inp = synth.make_beam_step(cfg, 11)
+    say(f"group size {g} {dt} M={7 * g}")
+    _run_and_check(inp, case)
+
+
+def test_naive_comparator_matches_oracle():
+    inp = synth.make_beam_step("qwen3_0p6b", 2, batch=2)
+    say("naive comparator")
+    s = S.upload_beam_step(inp, DEV)
+    S.plan_beam_step(s)
+    S.write_current_tokens(s)
+    out = torch.empty_like(s.out)
+    lout = torch.empty_like(s.lse_out)
+    B.bsp_naive_beam_attn(s.plan, s.q, s.k_pool, s.v_pool, s.block_tables, s.cache_indirection,
+                          out, lout)
+    B.bsp_check(s.plan)
+    fo, fl = oracle.beam_decode_attention(_applied(inp))
+    assert_close(out, lout, fo, fl, inp.dtype, "naive")
+
+
+# ------------------------------------------------- cached prefix (beam 1)
+
+CACHED_L = [0, 1, 255, 256, 257, 1000, 5184, 10240, 10241, 10368]
+
+
+def _cached_small(seed, L, q_len, **kw):
+    # Same geometry as the Phi-4 shape with a 1024-row allocation so the oracle is quick
+    # for prefill; decode runs at the full 10368 rows.
+    return synth.make_cached_prefix(seed, valid_rows=L, q_len=q_len, **kw)
+
+
+@pytest.mark.parametrize("L", CACHED_L)
+def test_cached_prefix_decode_matches_oracle(L):
+    R = oracle.bucket_rows(L, 256, 10368)
+    inp = synth.make_cached_prefix(L % 7, valid_rows=L, q_len=1, nan_from_row=R)
+    say(f"cached decode L={L} R={R}")
+    c = S.upload_cached_prefix(inp, DEV)
+    S.plan_cached_prefix(c)
+    S.run_cached_prefix(c)
+    B.bsp_check(c.plan_cache)
+    B.bsp_check(c.plan_new)
+    o, lse = oracle.cached_prefix_attention(inp, causal=True)
+    assert_close(c.out.reshape(1, 24, 128), c.lse_out.reshape(1, 24), o, lse, "f16",
+                 f"decode L={L}")
+    # every split partial against the oracle's partial over the same key chunk
+    for sp in range(c.n_split):
+        po, pl = oracle.cached_prefix_partial(inp, "cache", key_range=(256 * sp, 256 * (sp + 1)))
+        assert_close(c.o_part[sp], c.lse_part[sp], po, pl, "f16", f"decode L={L} split {sp}")
+
+
+@pytest.mark.parametrize("L,Sq,causal", [(0, 37, True), (300, 64, True), (777, 200, True),
+                                          (1024, 130, False), (513, 1, True)])
+def test_cached_prefix_prefill_matches_oracle(L, Sq, causal):
+    R = oracle.bucket_rows(L, 256, 1024)
+    inp = synth.make_cached_prefix(Sq, valid_rows=L, q_len=Sq, max_cache_rows=1024,
+                                   nan_from_row=R)
+    say(f"cached prefill L={L} Sq={Sq} causal={causal}")
+    c = S.upload_cached_prefix(inp, DEV, kv_split=0 if Sq > 1 else 256, causal=causal)
+    S.plan_cached_prefix(c)
+    S.run_cached_prefix(c)
+    B.bsp_check(c.plan_cache)
+    o, lse = oracle.cached_prefix_attention(inp, causal=causal)
+    assert_close(c.out, c.lse_out, o, lse, "f16", f"prefill L={L} Sq={Sq}")
+
+
+def test_cached_prefix_garbage_rows_do_not_matter():
+    L = 700
+    a = synth.make_cached_prefix(1, valid_rows=L, q_len=1)
+    b = synth.make_cached_prefix(1, valid_rows=L, q_len=1, nan_from_row=L)
+    outs = []
+    for inp in (a, b):
+        c = S.upload_cached_prefix(inp, DEV)
+        S.plan_cached_prefix(c)
+        S.run_cached_prefix(c)
+        torch.cuda.synchronize()
+        outs.append((c.out.clone(), c.lse_out.clone()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+# ------------------------------------------- full size, sampled outputs
+
+def test_full_size_qwen3_0p6b_sampled():
+    """64 requests x 30 beams, bf16, in the launch configuration the bench times."""
+    inp = synth.make_beam_step("qwen3_0p6b", 0)
+    say(f"full-size qwen3_0p6b: pages={inp.num_pages}")
+    s = S.upload_beam_step(inp, DEV)
+    S.plan_beam_step(s)
+    S.run_beam_step(s)
+    B.bsp_check(s.plan)
+    torch.cuda.synchronize()
+    ref = _applied(inp)
+    rng = np.random.default_rng(0)
+    picks = [(int(b), int(k)) for b, k in zip(rng.integers(0, 64, 24), rng.integers(0, 30, 24))]
+    picks += [(0, 0), (63, 29)]
+    out = s.out.float().cpu().numpy().reshape(64, 30, 16, 128)
+    lse = s.lse_out.cpu().numpy().reshape(64, 30, 16)
+    to, tl = TOL["bf16"]
+    for b, k in picks:
+        fo, fl = oracle.beam_attention_one(ref, b, k)
+        assert np.abs(out[b, k] - fo[0]).max() <= to
+        assert np.abs(lse[b, k] - fl[0]).max() <= tl

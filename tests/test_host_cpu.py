@@ -1,0 +1,216 @@
+"""CPU tier for libbsp: the library loads and exports every declared symbol, and
+the host planner (no HIP calls in host-only mode) builds the oracle's page
+tables bit for bit and returns the documented status for every host-forcible
+error. No kernel is launched here."""
+
+import ctypes
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from beam_search_shared_amd import _binding as B
+from synth import BeamConfig
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load_library()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = B.declared_symbols()
+    assert len(names) >= 14
+    for name in ["bsp_plan_create", "bsp_plan", "bsp_write_kv", "bsp_prefix_attn",
+                 "bsp_tail_attn", "bsp_merge", "bsp_check", "bsp_last_error"]:
+        assert name in names
+    for name in names:
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+    assert lib.bsp_version() >= 100
+
+
+def _host_plan(inp, max_tail=0, key_bucket=0, max_cache_rows=0):
+    desc = B.make_desc(inp.num_q_heads, inp.num_kv_heads, inp.head_dim, inp.page_size,
+                       inp.num_pages, inp.dtype, max_tail=max_tail, key_bucket=key_bucket,
+                       max_cache_rows=max_cache_rows)
+    return B.Plan(desc, inp.batch, inp.beam, inp.max_blocks, inp.max_seq_len, 1, host_only=True)
+
+
+def _check_plan_against_oracle(inp, plan):
+    B.bsp_plan(plan, inp.batch, inp.beam, 1, inp.prefix_len, inp.seq_len, inp.block_tables)
+    indptr, pages, n_keys, valid, tail = B.bsp_debug_plan_tables(plan, inp.batch)
+    o_indptr, o_pages = oracle.prefix_page_table(inp.prefix_len, inp.block_tables, inp.page_size)
+    assert np.array_equal(indptr, o_indptr) and np.array_equal(pages, o_pages)
+    assert np.array_equal(n_keys, inp.prefix_len) and np.array_equal(valid, inp.prefix_len)
+    assert np.array_equal(tail, inp.seq_len - inp.prefix_len)
+
+
+def test_planner_matches_oracle_on_1200_random_batches():
+    rng = np.random.default_rng(1234)
+    for trial in range(1200):
+        ps = int(rng.choice([1, 2, 4, 8, 16, 32]))
+        cfg = BeamConfig("rand", batch=int(rng.integers(1, 5)), beam=int(rng.integers(1, 6)),
+                         num_q_heads=2, num_kv_heads=1, head_dim=64, dtype="f32", page_size=ps,
+                         prefix_range=(0, int(rng.integers(1, 70))),
+                         tail_range=(0, int(rng.integers(0, 9))),
+                         shuffle_pages=bool(rng.integers(0, 2)))
+        inp = synth.make_beam_step(cfg, trial, page_stride=int(rng.integers(1, 3)))
+        inp.k_pool = inp.v_pool = None  # not needed on the host
+        _check_plan_against_oracle(inp, _host_plan(inp))
+
+
+def test_planner_golden_page_tables(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "prefix_pages.json")))
+    ps = g["page_size"]
+    cases = g["cases"]
+    Bn, W, nb = len(cases), 3, 5
+    bt = np.array([[[100 * r + 10 * k + i for i in range(nb)] for k in range(W)]
+                   for r in range(Bn)], dtype=np.int32)
+    P = np.array([c["prefix_len"] for c in cases], np.int32)
+    desc = B.make_desc(2, 1, 64, ps, 1000, "bf16")
+    plan = B.Plan(desc, Bn, W, nb, nb * ps, 1, host_only=True)
+    B.bsp_plan(plan, Bn, W, 1, P, P, bt)
+    indptr, pages, n_keys, _, _ = B.bsp_debug_plan_tables(plan, Bn)
+    for r, c in enumerate(cases):
+        assert pages[indptr[r]:indptr[r + 1]].tolist() == c["expected_pages"]
+        assert n_keys[r] == c["expected_keys"]
+
+
+def test_planner_bucket_rows_match_printed_rule(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "bucket_rows.json")))
+    cap, gran, ps = g["cap"], g["granularity"], 32
+    L = np.array([c[0] for c in g["rule_256_cases"]], np.int32)
+    nb = cap // ps
+    bt = np.tile(np.arange(nb, dtype=np.int32), (len(L), 1, 1))
+    desc = B.make_desc(24, 8, 128, ps, nb, "f16", key_bucket=gran, max_cache_rows=cap)
+    plan = B.Plan(desc, len(L), 1, nb, cap, 1, host_only=True)
+    B.bsp_plan(plan, len(L), 1, 1, L, L, bt)
+    _, _, n_keys, valid, _ = B.bsp_debug_plan_tables(plan, len(L))
+    assert n_keys.tolist() == [c[1] for c in g["rule_256_cases"]]
+    assert n_keys.tolist() == [oracle.bucket_rows(int(x), gran, cap) for x in L]
+    assert valid.tolist() == L.tolist()
+
+
+PLAN_CFG = BeamConfig("errs", batch=3, beam=4, num_q_heads=4, num_kv_heads=2, head_dim=64,
+                      dtype="bf16", page_size=8, prefix_range=(9, 30), tail_range=(1, 5),
+                      shuffle_pages=False)
+
+
+def _status(fn):
+    with pytest.raises(B.BspError) as ei:
+        fn()
+    return ei.value.name, str(ei.value)
+
+
+def test_plan_rejects_bad_prompt_page_without_clamping():
+    inp = synth.make_beam_step(PLAN_CFG, 0)
+    plan = _host_plan(inp)
+    bt = inp.block_tables.copy()
+    bt[1, 0, 0] = inp.num_pages  # one past the pool
+    name, msg = _status(lambda: B.bsp_plan(plan, inp.batch, inp.beam, 1, inp.prefix_len,
+                                           inp.seq_len, bt))
+    assert name == "BSP_ERR_PAGE_INDEX" and "request 1" in msg
+    bt[1, 0, 0] = -1
+    assert _status(lambda: B.bsp_plan(plan, inp.batch, inp.beam, 1, inp.prefix_len,
+                                      inp.seq_len, bt))[0] == "BSP_ERR_PAGE_INDEX"
+
+
+def test_plan_rejects_bad_tail_page_of_any_beam():
+    inp = synth.make_beam_step(PLAN_CFG, 1)
+    plan = _host_plan(inp)
+    bt = inp.block_tables.copy()
+    b = 2
+    last_blk = (int(inp.seq_len[b]) - 1) // inp.page_size
+    bt[b, 3, last_blk] = inp.num_pages + 7
+    assert _status(lambda: B.bsp_plan(plan, inp.batch, inp.beam, 1, inp.prefix_len,
+                                      inp.seq_len, bt))[0] == "BSP_ERR_PAGE_INDEX"
+
+
+def test_plan_tail_overflow_in_fixed_mode():
+    inp = synth.make_beam_step(PLAN_CFG, 2)
+    T = int((inp.seq_len - inp.prefix_len).max())
+    ok = _host_plan(inp, max_tail=T)
+    B.bsp_plan(ok, inp.batch, inp.beam, 1, inp.prefix_len, inp.seq_len, inp.block_tables)
+    assert ok.tail_len == T
+    bad = _host_plan(inp, max_tail=T - 1)
+    name, msg = _status(lambda: B.bsp_plan(bad, inp.batch, inp.beam, 1, inp.prefix_len,
+                                           inp.seq_len, inp.block_tables))
+    assert name == "BSP_ERR_TAIL_OVERFLOW" and str(T) in msg
+
+
+def test_plan_length_checks_and_stale_plan():
+    inp = synth.make_beam_step(PLAN_CFG, 3)
+    plan = _host_plan(inp)
+    B.bsp_plan(plan, inp.batch, inp.beam, 1, inp.prefix_len, inp.seq_len, inp.block_tables)
+    assert plan.num_splits == 1
+    P = inp.prefix_len.copy()
+    P[0] = inp.seq_len[0] + 1  # prefix longer than the sequence
+    assert _status(lambda: B.bsp_plan(plan, inp.batch, inp.beam, 1, P, inp.seq_len,
+                                      inp.block_tables))[0] == "BSP_ERR_ARG"
+    # the failed call dropped the previous plan
+    assert plan.num_splits == -1
+    assert _status(lambda: B.bsp_debug_plan_tables(plan, inp.batch))[0] == "BSP_ERR_STALE_PLAN"
+    S = inp.seq_len.copy()
+    S[1] = inp.max_seq_len + 1
+    assert _status(lambda: B.bsp_plan(plan, inp.batch, inp.beam, 1, inp.prefix_len, S,
+                                      inp.block_tables))[0] == "BSP_ERR_ARG"
+    assert _status(lambda: B.bsp_plan(plan, inp.batch + 1, inp.beam, 1, inp.prefix_len,
+                                      inp.seq_len, inp.block_tables))[0] == "BSP_ERR_ARG"
+
+
+def test_kernel_entry_points_refuse_unplanned_plan_before_any_launch():
+    inp = synth.make_beam_step(PLAN_CFG, 4)
+    plan = _host_plan(inp)
+    fake = 1 << 20  # never dereferenced: the status is returned before any launch
+    assert _status(lambda: B.bsp_prefix_attn(plan, fake, fake, fake, fake, fake, stream=0))[0] \
+        == "BSP_ERR_STALE_PLAN"
+    assert _status(lambda: B.bsp_tail_attn(plan, fake, fake, fake, fake, fake, fake, fake,
+                                           stream=0))[0] == "BSP_ERR_STALE_PLAN"
+    assert _status(lambda: B.bsp_write_kv(plan, fake, fake, 128, fake, 1, fake, fake,
+                                          stream=0))[0] == "BSP_ERR_STALE_PLAN"
+    B.bsp_plan(plan, inp.batch, inp.beam, 1, inp.prefix_len, inp.seq_len, inp.block_tables)
+    # a host-only plan never launches
+    assert _status(lambda: B.bsp_prefix_attn(plan, fake, fake, fake, fake, fake, stream=0))[0] \
+        == "BSP_ERR_ARG"
+
+
+def test_plan_create_rejects_bad_geometry():
+    def create(**kw):
+        base = dict(num_q_heads=4, num_kv_heads=2, head_dim=128, page_size=32, num_pages=10,
+                    dtype="bf16")
+        base.update(kw)
+        return B.Plan(B.make_desc(**base), 1, 1, 4, 100, 1, host_only=True)
+    assert _status(lambda: create(head_dim=96))[0] == "BSP_ERR_UNSUPPORTED"
+    assert _status(lambda: create(page_size=24))[0] == "BSP_ERR_UNSUPPORTED"
+    assert _status(lambda: create(num_q_heads=3))[0] == "BSP_ERR_ARG"
+    assert _status(lambda: create(kv_split=100))[0] == "BSP_ERR_ARG"
+    bad = B.make_desc(4, 2, 128, 32, 10, "bf16")
+    bad.dtype = 7
+    assert _status(lambda: B.Plan(bad, 1, 1, 4, 100, 1, host_only=True))[0] == "BSP_ERR_DTYPE"
+    assert _status(lambda: B.Plan(B.make_desc(4, 2, 128, 32, 10, "bf16"), 1, 1, 2, 100, 1,
+                                  host_only=True))[0] == "BSP_ERR_ARG"
+
+
+def test_merge_argument_checks(lib):
+    fake = 1 << 20
+    assert _status(lambda: B.bsp_merge(4, 2, 6, 2, fake, fake, 48, 8, fake, "bf16",
+                                       stream=0))[0] == "BSP_ERR_ARG"  # head_dim % 4
+    assert _status(lambda: B.bsp_merge(4, 2, 8, 2, fake, fake, 10, 8, fake, "bf16",
+                                       stream=0))[0] == "BSP_ERR_ARG"  # stride < part
+    B.bsp_merge(0, 2, 8, 2, fake, fake, 64, 8, fake, "bf16", stream=0)  # empty: no launch
+
+
+def test_check_mode_requires_shared_prompt_blocks(monkeypatch):
+    monkeypatch.setenv("BSP_CHECK", "1")
+    inp = synth.make_beam_step(PLAN_CFG, 5, prefix_range=(24, 30))
+    plan = _host_plan(inp)
+    B.bsp_plan(plan, inp.batch, inp.beam, 1, inp.prefix_len, inp.seq_len, inp.block_tables)
+    bt = inp.block_tables.copy()
+    bt[0, 2, 0] = bt[0, 0, 1]  # beam 2 no longer shares prompt block 0
+    name, msg = _status(lambda: B.bsp_plan(plan, inp.batch, inp.beam, 1, inp.prefix_len,
+                                           inp.seq_len, bt))
+    assert name == "BSP_ERR_ARG" and "share prompt block" in msg
