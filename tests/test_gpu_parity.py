@@ -56,7 +56,7 @@ def test_merge_matches_oracle(out_dtype, n_parts):
     B.bsp_merge(rows, heads, D, n_parts, og, lg, rows * heads * D, rows * heads, out, out_dtype,
                 lout)
     torch.cuda.synchronize()
-    tol_o = 1e-5 if out_dtype == "f32" else 8e-3
+    tol_o = TOL[out_dtype][0]
     o_gpu = out.float().cpu().numpy()
     assert np.abs(o_gpu - ref_o).max() <= tol_o
     l_gpu = lout.cpu().numpy()
