@@ -40,36 +40,46 @@ import numpy as np
 DTYPES = ("f32", "f16", "bf16")
 
 
-def round_to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
+def _round_bf16_inplace(x: np.ndarray) -> None:
+    """Round-to-nearest-even of float32 values to bf16, in place, in chunks.
+
+    Finite values cannot wrap in uint32 (the largest magnitude rounds to an
+    infinity at most); NaNs are restored afterwards.
+    """
+    flat = x.reshape(-1)
+    bits = flat.view(np.uint32)
+    step = 1 << 18
+    for lo in range(0, flat.size, step):
+        f = flat[lo:lo + step]
+        nan = np.isnan(f)
+        u = bits[lo:lo + step]
+        lsb = u >> np.uint32(16)
+        lsb &= np.uint32(1)
+        u += np.uint32(0x7FFF)
+        u += lsb
+        u &= np.uint32(0xFFFF0000)
+        if nan.any():
+            f[nan] = np.float32(np.nan)
+
+
+def round_to_dtype(x: np.ndarray, dtype: str, inplace: bool = False) -> np.ndarray:
     """Round float32 draws once, to nearest-even, to the storage dtype.
 
     Returns float32 arrays whose every value is exactly representable in
     ``dtype`` so that a later cast to that dtype is exact.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
+    out = x if inplace else x.copy()
     if dtype == "f32":
-        return x
+        return out
     if dtype == "f16":
-        return x.astype(np.float16).astype(np.float32)
+        flat = out.reshape(-1)
+        step = 1 << 20
+        for lo in range(0, flat.size, step):
+            flat[lo:lo + step] = flat[lo:lo + step].astype(np.float16)
+        return out
     if dtype == "bf16":
-        # Round-to-nearest-even on the top 16 bits, in cache-sized chunks.
-        # Finite values cannot wrap in uint32 (the largest magnitude rounds to
-        # an infinity at most); NaNs are put back afterwards.
-        out = np.empty_like(x)
-        src = x.reshape(-1).view(np.uint32)
-        dst = out.reshape(-1).view(np.uint32)
-        step = 1 << 18
-        for lo in range(0, src.size, step):
-            u = src[lo:lo + step].copy()
-            lsb = u >> np.uint32(16)
-            lsb &= np.uint32(1)
-            u += np.uint32(0x7FFF)
-            u += lsb
-            u &= np.uint32(0xFFFF0000)
-            dst[lo:lo + step] = u
-            nan = np.isnan(x.reshape(-1)[lo:lo + step])
-            if nan.any():
-                out.reshape(-1)[lo:lo + step][nan] = np.float32(np.nan)
+        _round_bf16_inplace(out)
         return out
     raise ValueError(f"unknown dtype {dtype!r}")
 
@@ -150,13 +160,20 @@ class BeamStepInputs:
 
 
 def _pool_fill(rng, shape, garbage: str) -> np.ndarray:
+    """A pool of unreferenced-row garbage, filled in place page by page."""
+    out = np.empty(shape, dtype=np.float32)
     if garbage == "nan":
-        return np.full(shape, np.nan, dtype=np.float32)
-    if garbage == "normal":  # N(0, 100): standard deviation 10
-        return rng.standard_normal(shape, dtype=np.float32) * np.float32(10.0)
-    if garbage == "unit":
-        return rng.standard_normal(shape, dtype=np.float32)
-    raise ValueError(f"unknown garbage mode {garbage!r}")
+        out.fill(np.nan)
+        return out
+    if garbage not in ("normal", "unit"):
+        raise ValueError(f"unknown garbage mode {garbage!r}")
+    rows = max(1, (1 << 22) // max(1, int(np.prod(shape[1:]))))
+    for p0 in range(0, shape[0], rows):
+        chunk = out[p0:p0 + rows]
+        rng.standard_normal(dtype=np.float32, out=chunk)
+        if garbage == "normal":  # N(0, 100): standard deviation 10
+            chunk *= np.float32(10.0)
+    return out
 
 
 def make_beam_step(config, seed: int = 0, *, batch: Optional[int] = None,
@@ -171,7 +188,9 @@ def make_beam_step(config, seed: int = 0, *, batch: Optional[int] = None,
     Keyword overrides shrink or vary a config for tests (e.g. ``batch=2``) while
     keeping its other shapes and distributions. ``page_stride=2`` leaves every
     other page id unused (pages only at even ids). ``garbage`` fills
-    unreferenced pool rows: "normal" N(0, 100), "unit" N(0, 1), "nan".
+    unreferenced pool rows: "normal" N(0, 100), "unit" N(0, 1), "nan". With
+    "unit" (and no ``keep_logical``) the pool draw itself supplies the
+    referenced rows, which is much faster for the large configs.
     """
     spec = BEAM_CONFIGS[config] if isinstance(config, str) else config
     B = batch if batch is not None else spec.batch
@@ -216,17 +235,28 @@ def make_beam_step(config, seed: int = 0, *, batch: Optional[int] = None,
     v_pool = _pool_fill(rng, (num_pages, Hkv, ps, D), garbage)
 
     prompt_k, prompt_v, own_k, own_v = [], [], [], []
+    # With N(0, 1) garbage and no logical copies wanted, the pool draw itself
+    # supplies every referenced row: only the end of the prompt has to be made
+    # identical in every beam's own block (copied from beam 0's block).
+    fast = garbage == "unit" and not keep_logical
     for b in range(B):
+        nf, full_rows = int(n_full[b]), int(n_full[b]) * ps
+        rest = int(P[b]) - full_rows
+        if fast:
+            if rest and W > 1:
+                src = int(block_tables[b, 0, nf])
+                pages = block_tables[b, 1:, nf]
+                k_pool[pages, :, :rest, :] = k_pool[src, :, :rest, :][None]
+                v_pool[pages, :, :rest, :] = v_pool[src, :, :rest, :][None]
+            continue
         pk = rng.standard_normal((P[b], Hkv, D), dtype=np.float32)
         pv = rng.standard_normal((P[b], Hkv, D), dtype=np.float32)
         ok = rng.standard_normal((W, T[b], Hkv, D), dtype=np.float32)
         ov = rng.standard_normal((W, T[b], Hkv, D), dtype=np.float32)
-        nf, full_rows = int(n_full[b]), int(n_full[b]) * ps
         if nf:                  # full prompt blocks: one shared copy
             pages = block_tables[b, 0, :nf]
             k_pool[pages] = pk[:full_rows].reshape(nf, ps, Hkv, D).transpose(0, 2, 1, 3)
             v_pool[pages] = pv[:full_rows].reshape(nf, ps, Hkv, D).transpose(0, 2, 1, 3)
-        rest = int(P[b]) - full_rows
         if rest:                # end of the prompt: a copy in every beam's own block
             pages = block_tables[b, :, nf]
             k_pool[pages, :, :rest, :] = pk[full_rows:].transpose(1, 0, 2)[None]
@@ -255,9 +285,13 @@ def make_beam_step(config, seed: int = 0, *, batch: Optional[int] = None,
         blk, row = divmod(j, ps)
         for k in range(W):
             slots.append(int(block_tables[b, k, blk]) * ps + row)
-            k_new.append(own_k[b][k, T[b] - 1])
-            v_new.append(own_v[b][k, T[b] - 1])
-    if slots:
+            if not fast:
+                k_new.append(own_k[b][k, T[b] - 1])
+                v_new.append(own_v[b][k, T[b] - 1])
+    if fast:
+        k_new = rng.standard_normal((len(slots), Hkv, D), dtype=np.float32)
+        v_new = rng.standard_normal((len(slots), Hkv, D), dtype=np.float32)
+    elif slots:
         k_new = np.stack(k_new).astype(np.float32)
         v_new = np.stack(v_new).astype(np.float32)
     else:
@@ -267,11 +301,13 @@ def make_beam_step(config, seed: int = 0, *, batch: Optional[int] = None,
     q = rng.standard_normal((B, W, 1, Hq, D), dtype=np.float32)
 
     rd = lambda a: round_to_dtype(a, dt)  # noqa: E731
+    round_to_dtype(k_pool, dt, inplace=True)
+    round_to_dtype(v_pool, dt, inplace=True)
     out = BeamStepInputs(
         config=spec.name, dtype=dt, batch=B, beam=W, num_q_heads=Hq, num_kv_heads=Hkv,
         head_dim=D, page_size=ps, num_pages=num_pages, max_blocks=max_blocks,
         max_seq_len=max_seq_len, max_tail=spec.max_tail,
-        q=rd(q), k_pool=rd(k_pool), v_pool=rd(v_pool), block_tables=block_tables,
+        q=rd(q), k_pool=k_pool, v_pool=v_pool, block_tables=block_tables,
         cache_indirection=ci, prefix_len=P.astype(np.int32), seq_len=S.astype(np.int32),
         k_new=rd(k_new), v_new=rd(v_new), slots=np.asarray(slots, dtype=np.int32),
     )
