@@ -54,24 +54,75 @@ struct WorkItem {
   int k_lo, k_hi;  // key range of this item (keys >= k_hi are never read)
 };
 
-// Large row blocks need more than half of a SIMD's registers: those variants
-// run one workgroup per CU so accumulators can also live in AGPRs.
-template <int D, int MB>
-constexpr int prefix_min_blocks() { return MB * D >= 384 ? 1 : 2; }
+// Page ids of one request are staged in LDS in windows of this many pages, so
+// issuing a tile's loads never waits on a global page-id load.
+constexpr int kPageWin = 2048;
 
-template <typename T, int D, int MB, int KT>
+// XOR swizzle of the 16-byte chunks of an LDS key row (a function of the low 4
+// row bits): chunk c of row r is stored at chunk c ^ swz(r). It keeps both the
+// K-operand reads (16 consecutive rows, one chunk each) and the V transpose
+// reads (4 rows x 2 chunks per 16 lanes) on distinct LDS banks, and it lets
+// 1 KB direct-to-LDS loads fill rows without padding.
+template <int D>
+__device__ __forceinline__ int lds_swz(int r) {
+  const int a = ((r & 1) << 1) ^ ((r & 2) << 1) ^ ((r >> 3) & 1);
+  return a ^ ((r & 4) ? (D == 64 ? 3 : 9) : 0);
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (vmcnt only; LDS and export counters unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// 16-byte direct global-to-LDS load (one per lane; a wave fills 1 KB at
+// `lds_dst` + 16 * lane). Issued through inline asm so that the compiler does
+// not see an LDS-writing load: it would otherwise wait for every load in
+// flight before each LDS read. Ordering is explicit instead: wait_vmcnt()
+// for the tile, then a workgroup barrier, before any wave reads it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds_dst) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)lds_dst);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(m0), "v"(src) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Four consecutive keys' values of one column, transposed across 16 lanes:
+// lane (4e + q) of each 16-lane group reads 4 values of row `row_e` at column
+// `col4`; afterwards lane i holds the values of column (col4 base + i) of the
+// 4 rows of its group.
+__device__ __forceinline__ s16x4 lds_read_tr(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+}
+
+// Variants whose row blocks need more than half a SIMD's registers run one
+// workgroup per CU (accumulators may then live in AGPRs).
+template <int D, int MB>
+constexpr int prefix_min_blocks() { return MB * D >= 512 ? 1 : 2; }
+
+template <typename T, int D, int MB, int KT, int NST>
 __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma_kernel(PrefixParams p) {
   using V8 = typename Mfma<T>::V8;
-  constexpr int RS = D + 8;             // LDS row stride in elements (16-byte pad)
-  constexpr int NDS = D / 32;           // contraction steps of S^T
-  constexpr int NDB = D / 16;           // 16-row blocks of O^T
-  constexpr int NKB = KT / 16;          // 16-key blocks of S^T per tile
-  constexpr int NS2 = KT / 32;          // contraction steps of O^T per tile
-  constexpr int CPR = D / 8;            // 16-byte chunks per key row
-  constexpr int CPT = KT * CPR / 256;   // chunks per thread per tile (each of K, V)
-  static_assert(CPT >= 1 && KT * CPR % 256 == 0, "tile must split over 256 threads");
-  __shared__ __attribute__((aligned(16))) T lds_k[KT * RS];
-  __shared__ __attribute__((aligned(16))) T lds_v[KT * RS];
+  constexpr int NDS = D / 32;                       // contraction steps of S^T
+  constexpr int NDB = D / 16;                       // 16-row blocks of O^T
+  constexpr int NKB = KT / 16;                      // 16-key blocks of S^T per tile
+  constexpr int NS2 = KT / 32;                      // contraction steps of O^T per tile
+  constexpr int CPR = D / 8;                        // 16-byte chunks per key row
+  constexpr int TILE = KT * D;                      // elements of K (or V) per tile
+  constexpr int NI = TILE * (int)sizeof(T) / 4096;  // 1 KB loads per wave for K (and V)
+  constexpr int LPT = 2 * NI;                       // vector-memory ops per thread per tile
+  static_assert(NI >= 1 && TILE * sizeof(T) % 4096 == 0, "tile must split into 1 KB loads");
+  static_assert(NST >= 2 && NST <= 4 && (NST - 2) * LPT < 64, "pipeline depth");
+  __shared__ __attribute__((aligned(1024))) T lds_kv[NST][2][TILE];
+  __shared__ int lds_pages[kPageWin];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -97,7 +148,8 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
   const int M = p.W * p.q_len * p.group;
   const int row0 = w.qt * (64 * MB) + wave * (16 * MB);
   const bool wave_active = row0 < M;
-  const int ps_mask = (1 << p.page_shift) - 1;
+  const int shift = p.page_shift;
+  const int pmask = (1 << shift) - 1;
 
   // ---- query rows of this lane (B operand of S^T), causal limits
   V8 qv[MB][NDS];
@@ -126,6 +178,11 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
     }
   }
 
+  // The query loads must be complete before the tile loads start: the
+  // compiler does not count the inline-asm tile loads, so a wait it placed
+  // later for a query register would also wait for every tile in flight.
+  wait_vmcnt<0>();
+
   f32x4 oacc[NDB][MB];
   float mrow[MB], lrow[MB];
 #pragma unroll
@@ -138,131 +195,149 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
 
   const T* kpool = static_cast<const T*>(p.k_pool);
   const T* vpool = static_cast<const T*>(p.v_pool);
-  u32x4 pk[CPT], pv[CPT];
-
-  auto load_tile = [&](int t0) {
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int c = tid + u * 256;
-      const int key = c / CPR;
-      const int dc = c % CPR;
-      const int j = t0 + key;
-      pk[u] = u32x4{0u, 0u, 0u, 0u};
-      pv[u] = u32x4{0u, 0u, 0u, 0u};
-      if (j < w.k_hi) {
-        const int32_t page = p.pages[ri.page_off + (j >> p.page_shift)];
-        if (page >= 0 && page < p.num_pages) {
-          const int64_t off =
-              ((((int64_t)page * p.hkv + w.g) << p.page_shift) + (j & ps_mask)) * D + dc * 8;
-          pk[u] = *reinterpret_cast<const u32x4*>(kpool + off);
-          pv[u] = *reinterpret_cast<const u32x4*>(vpool + off);
-        } else if (dc == 0) {
-          record_fault(&p.hdr->error_bits, &p.hdr->fault_count, &p.hdr->first_value,
-                       kErrPrefixPage, page);
-        }
-      }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int c = tid + u * 256;
-      const int key = c / CPR;
-      const int dc = c % CPR;
-      *reinterpret_cast<u32x4*>(&lds_k[key * RS + dc * 8]) = pk[u];
-      *reinterpret_cast<u32x4*>(&lds_v[key * RS + dc * 8]) = pv[u];
-    }
-  };
-
   const float c2 = p.scale_log2e;
-  if (w.k_lo < w.k_hi) load_tile(w.k_lo);
-  for (int t0 = w.k_lo; t0 < w.k_hi; t0 += KT) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (t0 + KT < w.k_hi) load_tile(t0 + KT);
-    if (!wave_active) continue;
+  const int keys_per_win = kPageWin << shift;
 
-    // ---- S^T = K Q^T for this tile
-    f32x4 sacc[NKB][MB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < MB; ++qb) sacc[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const V8 a = *reinterpret_cast<const V8*>(&lds_k[(kb * 16 + l16) * RS + ds * 32 + l4 * 8]);
-#pragma unroll
-        for (int qb = 0; qb < MB; ++qb) sacc[kb][qb] = Mfma<T>::mma(a, qv[qb][ds], sacc[kb][qb]);
+  for (int w0 = (w.k_lo / keys_per_win) * keys_per_win; w0 < w.k_hi; w0 += keys_per_win) {
+    const int seg_lo = max(w.k_lo, w0);
+    const int seg_hi = min(w.k_hi, w0 + keys_per_win);
+    const int pg0 = w0 >> shift;
+    const int npg = ((seg_hi - 1) >> shift) - pg0 + 1;
+    __syncthreads();  // every wave is done with the previous window
+    for (int i = tid; i < npg; i += 256) {
+      int32_t page = p.pages[ri.page_off + pg0 + i];
+      if (page < 0 || page >= p.num_pages) {  // the plan validated these; flag corruption
+        record_fault(&p.hdr->error_bits, &p.hdr->fault_count, &p.hdr->first_value,
+                     kErrPrefixPage, page);
+        page = 0;
       }
+      lds_pages[i] = page;
     }
+    wait_vmcnt<0>();
+    __syncthreads();
 
-    // ---- masking and online softmax, per query block
-    const bool full = (t0 + KT <= w.k_hi) && !p.causal;
+    // Issue the direct-to-LDS loads of one tile into one stage. Rows past the
+    // key range re-read the tile's first row; their scores are masked to -inf
+    // so they add exactly zero.
+    auto issue = [&](int tile, int stage) {
+      const int t0 = seg_lo + tile * KT;
 #pragma unroll
-    for (int qb = 0; qb < MB; ++qb) {
-      float mx = -INFINITY;
+      for (int i = 0; i < NI; ++i) {
+        const int chunk = (wave * NI + i) * 64 + lane;
+        const int r = chunk / CPR;
+        const int c = (chunk % CPR) ^ lds_swz<D>(r);
+        int j = t0 + r;
+        if (j >= seg_hi) j = t0;
+        const int page = lds_pages[(j >> shift) - pg0];
+        const int64_t off = ((((int64_t)page * p.hkv + w.g) << shift) + (j & pmask)) * D + c * 8;
+        T* dk = &lds_kv[stage][0][(wave * NI + i) * (1024 / (int)sizeof(T))];
+        T* dv = &lds_kv[stage][1][(wave * NI + i) * (1024 / (int)sizeof(T))];
+        lds_dma16(kpool + off, dk);
+        lds_dma16(vpool + off, dv);
+      }
+    };
+
+    const int nt = (seg_hi - seg_lo + KT - 1) / KT;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+    for (int s = 0; s < NST - 1; ++s)
+      if (s < nt) issue(s, s);
+
+    for (int t = 0; t < nt; ++t) {
+      // Tile t's loads are done once at most (tiles issued after it) * LPT are in flight.
+      const int ahead = min(NST - 2, nt - 1 - t);
+      if (ahead >= 2) wait_vmcnt<(NST >= 4 ? 2 : 0) * LPT>();
+      else if (ahead == 1) wait_vmcnt<LPT>();
+      else wait_vmcnt<0>();
+      __syncthreads();  // all threads' loads of tile t landed; tile t-1's stage is free
+      if (t + NST - 1 < nt) issue(t + NST - 1, (t + NST - 1) % NST);
+      if (!wave_active) continue;
+      const T* lk = lds_kv[t % NST][0];
+      const T* lv = lds_kv[t % NST][1];
+      const int t0 = seg_lo + t * KT;
+
+      // ---- S^T = K Q^T
+      f32x4 sacc[NKB][MB];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float s = sacc[kb][qb][e];
-          if (!full) {
-            const int j = t0 + kb * 16 + l4 * 4 + e;
-            if (j >= w.k_hi || j > climit[qb]) s = -INFINITY;
-          }
-          sacc[kb][qb][e] = s;
-          mx = fmaxf(mx, s);
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < MB; ++qb) sacc[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const int r = kb * 16 + l16;
+          const V8 a = *reinterpret_cast<const V8*>(&lk[r * D + (((ds * 4 + l4) ^ lds_swz<D>(r)) << 3)]);
+#pragma unroll
+          for (int qb = 0; qb < MB; ++qb) sacc[kb][qb] = Mfma<T>::mma(a, qv[qb][ds], sacc[kb][qb]);
         }
       }
-      mx = fmaxf(mx, xor16(mx));
-      mx = fmaxf(mx, xor32(mx));
-      const float m_new = fmaxf(mrow[qb], mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2((mrow[qb] - m_use) * c2);
-      const float moff = -m_use * c2;
-      mrow[qb] = m_new;
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float pr = fast_exp2(fmaf(sacc[kb][qb][e], c2, moff));
-          sacc[kb][qb][e] = pr;
-          rs += pr;
-        }
-      }
-      lrow[qb] = fmaf(lrow[qb], alpha, rs);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db][qb] *= alpha;
-    }
 
-    // ---- O^T += V^T P^T
-#pragma unroll
-    for (int s2 = 0; s2 < NS2; ++s2) {
-      V8 pb[MB];
+      // ---- masking and online softmax, per query block
+      const bool full = (t0 + KT <= w.k_hi) && !p.causal;
 #pragma unroll
       for (int qb = 0; qb < MB; ++qb) {
+        float mx = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pb[qb][e] = Traits<T>::from_f(sacc[2 * s2][qb][e]);
-          pb[qb][4 + e] = Traits<T>::from_f(sacc[2 * s2 + 1][qb][e]);
+        for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float s = sacc[kb][qb][e];
+            if (!full) {
+              const int j = t0 + kb * 16 + l4 * 4 + e;
+              if (j >= w.k_hi || j > climit[qb]) s = -INFINITY;
+            }
+            sacc[kb][qb][e] = s;
+            mx = fmaxf(mx, s);
+          }
         }
+        mx = fmaxf(mx, xor16(mx));
+        mx = fmaxf(mx, xor32(mx));
+        const float m_new = fmaxf(mrow[qb], mx);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = fast_exp2((mrow[qb] - m_use) * c2);
+        const float moff = -m_use * c2;
+        mrow[qb] = m_new;
+        float rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float pr = fast_exp2(fmaf(sacc[kb][qb][e], c2, moff));
+            sacc[kb][qb][e] = pr;
+            rs += pr;
+          }
+        }
+        lrow[qb] = fmaf(lrow[qb], alpha, rs);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[db][qb] *= alpha;
       }
-      const T* v0 = &lds_v[(32 * s2 + 4 * l4) * RS + l16];
-      const T* v1 = &lds_v[(32 * s2 + 16 + 4 * l4) * RS + l16];
+
+      // ---- O^T += V^T P^T (V^T operand by transpose reads)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        V8 a;
+      for (int s2 = 0; s2 < NS2; ++s2) {
+        V8 pb[MB];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a[e] = v0[e * RS + db * 16];
-          a[4 + e] = v1[e * RS + db * 16];
+        for (int qb = 0; qb < MB; ++qb) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pb[qb][e] = Traits<T>::from_f(sacc[2 * s2][qb][e]);
+            pb[qb][4 + e] = Traits<T>::from_f(sacc[2 * s2 + 1][qb][e]);
+          }
         }
+        const int ra = 32 * s2 + 4 * l4 + (l16 >> 2);   // row read by this lane (+16 for the upper half)
+        const int swa = lds_swz<D>(ra);
 #pragma unroll
-        for (int qb = 0; qb < MB; ++qb) oacc[db][qb] = Mfma<T>::mma(a, pb[qb], oacc[db][qb]);
+        for (int db = 0; db < NDB; ++db) {
+          const int col = db * 16 + 4 * (l16 & 3);
+          const int off = (((col >> 3) ^ swa) << 3) + (col & 7);
+          // Assemble the operand from whole 32-bit words: building it from
+          // 16-bit elements gets miscompiled into duplicated halves.
+          const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr(&lv[ra * D + off]));
+          const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr(&lv[(ra + 16) * D + off]));
+          const V8 a = __builtin_bit_cast(V8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+          for (int qb = 0; qb < MB; ++qb) oacc[db][qb] = Mfma<T>::mma(a, pb[qb], oacc[db][qb]);
+        }
       }
     }
   }
@@ -398,21 +473,22 @@ int prefix_rows_per_tile(int dtype, int head_dim, int rows_per_req) {
   return 64 * pick_mb(head_dim, rows_per_req);
 }
 
+// Tile size and pipeline depth per head_dim: 64 KB of K/V stages per workgroup.
 template <typename T>
 static void launch_mfma(const PrefixParams& p, int head_dim, int mb, unsigned blocks,
                         hipStream_t s) {
-#define BSP_PFX(DD, MBB, KTT) prefix_mfma_kernel<T, DD, MBB, KTT><<<blocks, 256, 0, s>>>(p)
+#define BSP_PFX(DD, MBB, KTT, NS) prefix_mfma_kernel<T, DD, MBB, KTT, NS><<<blocks, 256, 0, s>>>(p)
   if (head_dim == 64) {
-    if (mb == 1) BSP_PFX(64, 1, 64);
-    else if (mb == 2) BSP_PFX(64, 2, 64);
-    else BSP_PFX(64, 3, 64);
+    if (mb == 1) BSP_PFX(64, 1, 64, 4);
+    else if (mb == 2) BSP_PFX(64, 2, 64, 4);
+    else BSP_PFX(64, 3, 64, 4);
   } else if (head_dim == 128) {
-    if (mb == 1) BSP_PFX(128, 1, 64);
-    else if (mb == 2) BSP_PFX(128, 2, 64);
-    else BSP_PFX(128, 3, 64);
+    if (mb == 1) BSP_PFX(128, 1, 32, 4);
+    else if (mb == 2) BSP_PFX(128, 2, 32, 4);
+    else BSP_PFX(128, 3, 32, 4);
   } else {
-    if (mb == 1) BSP_PFX(256, 1, 32);
-    else BSP_PFX(256, 2, 32);
+    if (mb == 1) BSP_PFX(256, 1, 32, 2);
+    else BSP_PFX(256, 2, 32, 4);
   }
 #undef BSP_PFX
 }
