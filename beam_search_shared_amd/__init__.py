@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     bsp_check,
     bsp_debug_plan_tables,
     bsp_debug_tail_slots,
+    bsp_decode_step,
     bsp_merge,
     bsp_naive_beam_attn,
     bsp_plan,

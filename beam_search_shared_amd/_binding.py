@@ -79,6 +79,7 @@ _SIGS = {
     "bsp_tail_attn": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "bsp_merge": (_I32, [_I32, _I32, _I32, _I32, _P, _P, _I64, _I64, _P, _I32, _P, _P]),
     "bsp_naive_beam_attn": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "bsp_decode_step": (_I32, [_P, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "bsp_check": (_I32, [_P, _P]),
     "bsp_debug_plan_tables": (_I32, [_P, _P, _P, _P, _P, _P]),
     "bsp_debug_tail_slots": (_I32, [_P, _P, _P, _P, _P]),
@@ -240,6 +241,14 @@ def bsp_naive_beam_attn(plan: Plan, q, k_pool, v_pool, block_tables, cache_indir
     _check(load_library().bsp_naive_beam_attn(plan.handle, _ptr(q), _ptr(k_pool), _ptr(v_pool),
                                               _ptr(block_tables), _ptr(cache_indirection),
                                               _ptr(o_out), _ptr(lse_out), _stream(stream)))
+
+
+def bsp_decode_step(plan: Plan, q, k_new, v_new, new_row_stride: int, k_pool, v_pool,
+                    block_tables, cache_indirection, o_out, lse_out=None, stream=None) -> None:
+    _check(load_library().bsp_decode_step(plan.handle, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                          new_row_stride, _ptr(k_pool), _ptr(v_pool),
+                                          _ptr(block_tables), _ptr(cache_indirection),
+                                          _ptr(o_out), _ptr(lse_out), _stream(stream)))
 
 
 def bsp_check(plan: Plan, stream=None) -> None:

@@ -441,6 +441,69 @@ bsp_status_t bsp_prefix_attn(bsp_plan_t pl, const void* q, const void* k_pool, c
                       "prefix launch", stream);
 }
 
+bsp_status_t bsp_decode_step(bsp_plan_t pl, const void* q, const void* k_new, const void* v_new,
+                             int64_t new_row_stride, void* k_pool, void* v_pool,
+                             const int32_t* block_tables_d, const int32_t* cache_indirection_d,
+                             void* o_out, float* lse_out, hipStream_t stream) {
+  bsp_status_t st = check_device_ready(pl);
+  if (st != BSP_OK) return st;
+  const bsp_layer_desc_t& d = pl->desc;
+  if (d.dtype == BSP_F32)
+    return fail(BSP_ERR_UNSUPPORTED, "bsp_decode_step runs bf16/f16; use the separate calls for f32");
+  if (pl->q_len != 1) return fail(BSP_ERR_UNSUPPORTED, "bsp_decode_step needs q_len == 1");
+  if (d.key_bucket > 0) return fail(BSP_ERR_UNSUPPORTED, "bsp_decode_step is beam mode only");
+  if (d.kv_split > 0) return fail(BSP_ERR_UNSUPPORTED, "bsp_decode_step takes no kv_split");
+  if (!q || !k_new || !v_new || !k_pool || !v_pool || !block_tables_d || !cache_indirection_d ||
+      !o_out)
+    return fail(BSP_ERR_ARG, "null pointer");
+  const int vec = 8;  // 16 bytes of 2-byte elements
+  if (new_row_stride < (int64_t)d.num_kv_heads * d.head_dim || new_row_stride % vec != 0)
+    return fail(BSP_ERR_ARG, "new_row_stride %lld must be >= %d and a multiple of %d",
+                (long long)new_row_stride, d.num_kv_heads * d.head_dim, vec);
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) ||
+      !aligned16(v_pool) || (reinterpret_cast<uintptr_t>(o_out) & 7u) != 0)
+    return fail(BSP_ERR_ARG, "q, k_new, v_new and the pools must be 16-byte aligned, o_out 8-byte");
+  bsp::PrefixParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = q;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.req = dev_req(pl);
+  p.pages = dev_pages(pl);
+  p.hdr = dev_header(pl);
+  p.B = pl->B;
+  p.W = pl->W;
+  p.q_len = 1;
+  p.hq = d.num_q_heads;
+  p.hkv = d.num_kv_heads;
+  p.group = d.num_q_heads / d.num_kv_heads;
+  p.page_shift = pl->page_shift;
+  p.num_pages = d.num_pages;
+  p.n_split = 1;
+  p.split_keys = 0;
+  const int rows_per_tile = bsp::prefix_rows_per_tile(d.dtype, d.head_dim, pl->rows_per_req);
+  p.n_qtiles = (int32_t)ceil_div(pl->rows_per_req, rows_per_tile);
+  p.causal = 0;
+  p.rows_total = pl->B * pl->W;
+  p.scale = d.sm_scale;
+  p.scale_log2e = d.sm_scale * 1.4426950408889634f;
+  bsp::FusedParams f;
+  f.k_new = k_new;
+  f.v_new = v_new;
+  f.new_stride = new_row_stride;
+  f.k_pool_w = k_pool;
+  f.v_pool_w = v_pool;
+  f.block_tables = block_tables_d;
+  f.ci = cache_indirection_d;
+  f.max_blocks = pl->max_blocks;
+  f.max_seq_len = pl->max_seq_len;
+  f.o_out = o_out;
+  f.lse_out = lse_out;
+  return after_launch(
+      pl, bsp::launch_decode_step(p, f, d.dtype, d.head_dim, pl->rows_per_req, stream),
+      "decode step launch", stream);
+}
+
 static bsp::TailParams tail_params(const bsp_plan_s* pl, const void* q, const void* k_pool,
                                    const void* v_pool, const int32_t* bt, const int32_t* ci) {
   const bsp_layer_desc_t& d = pl->desc;

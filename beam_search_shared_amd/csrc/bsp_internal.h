@@ -81,6 +81,21 @@ struct PrefixParams {
   float scale_log2e;    // scale * log2(e)
 };
 
+// Extra inputs of the fused decode step (prefix + tail + current-token write
+// in one launch; q_len 1, beam mode).
+struct FusedParams {
+  const void* k_new;            // current token of every beam, [B*W][Hkv*D] with row stride
+  const void* v_new;
+  int64_t new_stride;           // elements between consecutive beams' rows
+  void* k_pool_w;               // the pools again, writable (the token write)
+  void* v_pool_w;
+  const int32_t* block_tables;  // device [B][W][max_blocks]
+  const int32_t* ci;            // device [B][W][max_seq_len]
+  int32_t max_blocks, max_seq_len;
+  void* o_out;                  // dtype [B*W][Hq][D]
+  float* lse_out;               // [B*W][Hq] or null
+};
+
 struct TailParams {
   const void* q;
   const void* k_pool;
@@ -114,6 +129,8 @@ struct MergeParams {
 hipError_t launch_write_kv(const WriteKvParams& p, int dtype, hipStream_t s);
 hipError_t launch_prefix(const PrefixParams& p, int dtype, int head_dim, int rows_per_req,
                          hipStream_t s);
+hipError_t launch_decode_step(const PrefixParams& p, const FusedParams& f, int dtype,
+                              int head_dim, int rows_per_req, hipStream_t s);
 // Rows per workgroup the prefix kernel picks for this shape (so the host can
 // size the grid before launching).
 int prefix_rows_per_tile(int dtype, int head_dim, int rows_per_req);

@@ -56,7 +56,10 @@ struct WorkItem {
 
 // Page ids of one request are staged in LDS in windows of this many pages, so
 // issuing a tile's loads never waits on a global page-id load.
-constexpr int kPageWin = 2048;
+constexpr int kPageWin = 1024;
+// Resolved tail slots of the fused step, per (beam of this query tile, tail
+// position); larger tails are resolved on the fly.
+constexpr int kTailSlots = 3072;
 
 // XOR swizzle of the 16-byte chunks of an LDS key row (a function of the low 4
 // row bits): chunk c of row r is stored at chunk c ^ swz(r). It keeps both the
@@ -108,8 +111,33 @@ __device__ __forceinline__ s16x4 lds_read_tr(const void* p) {
 template <int D, int MB>
 constexpr int prefix_min_blocks() { return MB * D >= 512 ? 1 : 2; }
 
-template <typename T, int D, int MB, int KT, int NST>
-__global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma_kernel(PrefixParams p) {
+// Tail slot encoding: >= 0 pool row index ((page * Hkv + g) * page_size + row);
+// -1 an invalid index (skipped); <= -2 the current token of beam (-entry - 2),
+// read from the new-token rows instead of the pool.
+__device__ __forceinline__ int32_t resolve_fused_slot(const PrefixParams& p, const FusedParams& f,
+                                                      int b, int kk, int g, int j, int jcur) {
+  const int32_t src = f.ci[((int64_t)b * p.W + kk) * f.max_seq_len + j];
+  if (src < 0 || src >= p.W) {
+    record_fault(&p.hdr->error_bits, &p.hdr->fault_count, &p.hdr->first_value, kErrTailParent, src);
+    return -1;
+  }
+  if (j == jcur) return -2 - src;
+  const int32_t page = f.block_tables[((int64_t)b * p.W + src) * f.max_blocks + (j >> p.page_shift)];
+  if (page < 0 || page >= p.num_pages) {
+    record_fault(&p.hdr->error_bits, &p.hdr->fault_count, &p.hdr->first_value, kErrTailPage, page);
+    return -1;
+  }
+  return ((page * p.hkv + g) << p.page_shift) + (j & ((1 << p.page_shift) - 1));
+}
+
+// FUSED = false: bsp_prefix_attn (fp32 partial state per key split).
+// FUSED = true: bsp_decode_step, one launch per layer step: the workgroup of
+// (request, KV head) also writes its beams' current tokens, then after the
+// shared keys attends each beam's tail (gathered through cache_indirection) in
+// the same online softmax and writes the final output in the storage dtype.
+template <typename T, int D, int MB, int KT, int NST, bool FUSED>
+__global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma_kernel(PrefixParams p,
+                                                                                          FusedParams f) {
   using V8 = typename Mfma<T>::V8;
   constexpr int NDS = D / 32;                       // contraction steps of S^T
   constexpr int NDB = D / 16;                       // 16-row blocks of O^T
@@ -123,6 +151,7 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
   static_assert(NST >= 2 && NST <= 4 && (NST - 2) * LPT < 64, "pipeline depth");
   __shared__ __attribute__((aligned(1024))) T lds_kv[NST][2][TILE];
   __shared__ int lds_pages[kPageWin];
+  __shared__ int lds_tail[FUSED ? kTailSlots : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -150,6 +179,48 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
   const bool wave_active = row0 < M;
   const int shift = p.page_shift;
   const int pmask = (1 << shift) - 1;
+
+  // ---- fused step: write this tile's beams' current tokens, resolve tail slots
+  const int rt = 64 * MB;                       // query rows per workgroup
+  const int kb_first = (w.qt * rt) / p.group;   // beams with a row in this tile
+  const int kb_last = min(p.W - 1, ((w.qt + 1) * rt - 1) / p.group);
+  const int nbt = kb_last - kb_first + 1;
+  bool tail_in_lds = false;
+  if constexpr (FUSED) {
+    const int n_tail = ri.tail;
+    const int jcur = ri.seq - 1;
+    if (n_tail > 0) {
+      // a beam's token is written by the tile holding its first row
+      const int kw_lo = (w.qt * rt + p.group - 1) / p.group;
+      const int kw_hi = min(p.W, ((w.qt + 1) * rt + p.group - 1) / p.group);
+      for (int task = tid; task < (kw_hi - kw_lo) * CPR; task += 256) {
+        const int kk = kw_lo + task / CPR;
+        const int c = task % CPR;
+        const int32_t page =
+            f.block_tables[((int64_t)w.b * p.W + kk) * f.max_blocks + (jcur >> shift)];
+        if (page < 0 || page >= p.num_pages) {
+          if (c == 0)
+            record_fault(&p.hdr->error_bits, &p.hdr->fault_count, &p.hdr->first_value,
+                         kErrTailPage, page);
+          continue;
+        }
+        const int64_t src = ((int64_t)w.b * p.W + kk) * f.new_stride + (int64_t)w.g * D + c * 8;
+        const int64_t dst = ((((int64_t)page * p.hkv + w.g) << shift) + (jcur & pmask)) * D + c * 8;
+        *reinterpret_cast<u32x4*>(static_cast<T*>(f.k_pool_w) + dst) =
+            *reinterpret_cast<const u32x4*>(static_cast<const T*>(f.k_new) + src);
+        *reinterpret_cast<u32x4*>(static_cast<T*>(f.v_pool_w) + dst) =
+            *reinterpret_cast<const u32x4*>(static_cast<const T*>(f.v_new) + src);
+      }
+      tail_in_lds = nbt * n_tail <= kTailSlots;
+      if (tail_in_lds) {
+        for (int task = tid; task < nbt * n_tail; task += 256) {
+          const int kk = kb_first + task / n_tail;
+          const int t = task % n_tail;
+          lds_tail[task] = resolve_fused_slot(p, f, w.b, kk, w.g, ri.prefix + t, jcur);
+        }
+      }
+    }
+  }
 
   // ---- query rows of this lane (B operand of S^T), causal limits
   V8 qv[MB][NDS];
@@ -342,7 +413,112 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
     }
   }
 
-  // ---- epilogue: normalise and write the partial state
+  // ---- fused step: each beam's tail joins the same online softmax
+  if constexpr (FUSED) {
+    const int n_tail = ri.tail;
+    __syncthreads();  // tail slot table written (the key loop may have had no tiles)
+    if (n_tail > 0 && wave_active) {
+      const int jcur = ri.seq - 1;
+      constexpr int TC = 2;  // tail keys in flight together
+#pragma unroll
+      for (int qb = 0; qb < MB; ++qb) {
+        const int r = row0 + qb * 16 + l16;
+        const bool row_ok = r < M;
+        const int kbeam = row_ok ? r / p.group : kb_first;
+        const int h = w.g * p.group + (row_ok ? r % p.group : 0);
+        // this lane's columns of O^T: d = db * 16 + 4 * l4 + i (query kept packed)
+        u32x2 qraw[NDB];
+        {
+          const T* qr = static_cast<const T*>(p.q) + (((int64_t)w.b * p.W + kbeam) * p.hq + h) * D + 4 * l4;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) qraw[db] = *reinterpret_cast<const u32x2*>(qr + db * 16);
+        }
+        for (int t0 = 0; t0 < n_tail; t0 += TC) {
+          const T* kr[TC];
+          const T* vr[TC];
+          bool ok[TC];
+#pragma unroll
+          for (int c = 0; c < TC; ++c) {
+            const int t = t0 + c;
+            int32_t e = -1;
+            if (t < n_tail && row_ok)
+              e = tail_in_lds ? lds_tail[(kbeam - kb_first) * n_tail + t]
+                              : resolve_fused_slot(p, f, w.b, kbeam, w.g, ri.prefix + t, jcur);
+            ok[c] = e != -1;
+            if (e >= 0) {
+              kr[c] = kpool + (int64_t)e * D + 4 * l4;
+              vr[c] = vpool + (int64_t)e * D + 4 * l4;
+            } else {  // the current token of beam -e-2 (or a skipped key: any valid row)
+              const int src = e <= -2 ? -2 - e : 0;
+              const int64_t o = ((int64_t)w.b * p.W + src) * f.new_stride + (int64_t)w.g * D + 4 * l4;
+              kr[c] = static_cast<const T*>(f.k_new) + o;
+              vr[c] = static_cast<const T*>(f.v_new) + o;
+            }
+          }
+          // scores of the TC keys
+          float pr[TC], alpha = 1.f;
+          {
+            u32x2 kraw[TC][NDB];
+#pragma unroll
+            for (int c = 0; c < TC; ++c)
+#pragma unroll
+              for (int db = 0; db < NDB; ++db) kraw[c][db] = *reinterpret_cast<const u32x2*>(kr[c] + db * 16);
+            float sc[TC];
+#pragma unroll
+            for (int c = 0; c < TC; ++c) {
+              float part = 0.f;
+#pragma unroll
+              for (int db = 0; db < NDB; ++db) {
+                const T* ke = reinterpret_cast<const T*>(&kraw[c][db]);
+                const T* qe = reinterpret_cast<const T*>(&qraw[db]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) part = fmaf(Traits<T>::to_f(qe[i]), Traits<T>::to_f(ke[i]), part);
+              }
+              part += xor16(part);
+              part += xor32(part);
+              sc[c] = ok[c] ? part : -INFINITY;
+            }
+            float mx = sc[0];
+#pragma unroll
+            for (int c = 1; c < TC; ++c) mx = fmaxf(mx, sc[c]);
+            const float m_new = fmaxf(mrow[qb], mx);
+            const float m_use = m_new == -INFINITY ? 0.f : m_new;
+            alpha = fast_exp2((mrow[qb] - m_use) * c2);
+            float psum = 0.f;
+#pragma unroll
+            for (int c = 0; c < TC; ++c) {
+              pr[c] = fast_exp2((sc[c] - m_use) * c2);
+              psum += pr[c];
+            }
+            mrow[qb] = m_new;
+            // lrow holds this lane's share of the row sum: add each key once
+            lrow[qb] = fmaf(lrow[qb], alpha, l4 == 0 ? psum : 0.f);
+          }
+          // values of the TC keys
+          {
+            u32x2 vraw[TC][NDB];
+#pragma unroll
+            for (int c = 0; c < TC; ++c)
+#pragma unroll
+              for (int db = 0; db < NDB; ++db) vraw[c][db] = *reinterpret_cast<const u32x2*>(vr[c] + db * 16);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                float acc = oacc[db][qb][i] * alpha;
+#pragma unroll
+                for (int c = 0; c < TC; ++c)
+                  acc = fmaf(pr[c], Traits<T>::to_f(reinterpret_cast<const T*>(&vraw[c][db])[i]), acc);
+                oacc[db][qb][i] = acc;
+              }
+            }
+          }
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: normalise and write the partial state (or the final output)
 #pragma unroll
   for (int qb = 0; qb < MB; ++qb) {
     float lt = lrow[qb];
@@ -355,13 +531,27 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
     const int i = t % p.q_len;
     const int kbeam = t / p.q_len;
     const int64_t grow = ((int64_t)w.b * p.W + kbeam) * p.q_len + i;
-    const int64_t ohead = ((int64_t)w.split * p.rows_total + grow) * p.hq + w.g * p.group + hh;
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    float* op = p.o_part + ohead * D + l4 * 4;
+    const float lse = lt > 0.f ? mrow[qb] * p.scale + __logf(lt) : -INFINITY;
+    if constexpr (FUSED) {
+      const int64_t ohead = grow * p.hq + w.g * p.group + hh;
+      T* op = static_cast<T*>(f.o_out) + ohead * D + l4 * 4;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-      *reinterpret_cast<f32x4*>(op + db * 16) = oacc[db][qb] * inv;
-    if (l4 == 0) p.lse_part[ohead] = lt > 0.f ? mrow[qb] * p.scale + __logf(lt) : -INFINITY;
+      for (int db = 0; db < NDB; ++db) {
+        T e4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) e4[e] = Traits<T>::from_f(oacc[db][qb][e] * inv);
+        *reinterpret_cast<u32x2*>(op + db * 16) = __builtin_bit_cast(u32x2, e4);
+      }
+      if (l4 == 0 && f.lse_out != nullptr) f.lse_out[ohead] = lse;
+    } else {
+      const int64_t ohead = ((int64_t)w.split * p.rows_total + grow) * p.hq + w.g * p.group + hh;
+      float* op = p.o_part + ohead * D + l4 * 4;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        *reinterpret_cast<f32x4*>(op + db * 16) = oacc[db][qb] * inv;
+      if (l4 == 0) p.lse_part[ohead] = lse;
+    }
   }
 }
 
@@ -474,10 +664,11 @@ int prefix_rows_per_tile(int dtype, int head_dim, int rows_per_req) {
 }
 
 // Tile size and pipeline depth per head_dim: 64 KB of K/V stages per workgroup.
-template <typename T>
-static void launch_mfma(const PrefixParams& p, int head_dim, int mb, unsigned blocks,
-                        hipStream_t s) {
-#define BSP_PFX(DD, MBB, KTT, NS) prefix_mfma_kernel<T, DD, MBB, KTT, NS><<<blocks, 256, 0, s>>>(p)
+template <typename T, bool FUSED>
+static void launch_mfma(const PrefixParams& p, const FusedParams& f, int head_dim, int mb,
+                        unsigned blocks, hipStream_t s) {
+#define BSP_PFX(DD, MBB, KTT, NS) \
+  prefix_mfma_kernel<T, DD, MBB, KTT, NS, FUSED><<<blocks, 256, 0, s>>>(p, f)
   if (head_dim == 64) {
     if (mb == 1) BSP_PFX(64, 1, 64, 4);
     else if (mb == 2) BSP_PFX(64, 2, 64, 4);
@@ -503,9 +694,20 @@ hipError_t launch_prefix(const PrefixParams& p, int dtype, int head_dim, int row
     else prefix_simt_kernel<256><<<blocks, 256, 0, s>>>(p);
   } else {
     const int mb = pick_mb(head_dim, rows_per_req);
-    if (dtype == BSP_F16) launch_mfma<_Float16>(p, head_dim, mb, blocks, s);
-    else launch_mfma<__bf16>(p, head_dim, mb, blocks, s);
+    const FusedParams none{};
+    if (dtype == BSP_F16) launch_mfma<_Float16, false>(p, none, head_dim, mb, blocks, s);
+    else launch_mfma<__bf16, false>(p, none, head_dim, mb, blocks, s);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_step(const PrefixParams& p, const FusedParams& f, int dtype,
+                              int head_dim, int rows_per_req, hipStream_t s) {
+  const unsigned blocks = (unsigned)(p.B * p.hkv * p.n_qtiles);
+  if (blocks == 0) return hipSuccess;
+  const int mb = pick_mb(head_dim, rows_per_req);
+  if (dtype == BSP_F16) launch_mfma<_Float16, true>(p, f, head_dim, mb, blocks, s);
+  else launch_mfma<__bf16, true>(p, f, head_dim, mb, blocks, s);
   return hipGetLastError();
 }
 

@@ -8,6 +8,7 @@ libbsp's kernels. A beam step is
     bsp_tail_attn    each beam's tail through cache_indirection
     bsp_merge        exact LSE merge of the two partial states
 
+or, fused into one launch, ``bsp_decode_step``;
 and a cached-prefix call (beam 1) is
 
     bsp_write_kv     this call's rows -> scratch pages
@@ -63,6 +64,8 @@ class BeamStepDevice:
     lse_part: torch.Tensor   # float [2, rows, Hq]
     out: torch.Tensor        # dtype [rows, Hq, D]
     lse_out: torch.Tensor    # float [rows, Hq]
+    k_new_beams: torch.Tensor = None  # dtype [B*W, Hkv, D]: current token by beam (fused step)
+    v_new_beams: torch.Tensor = None
 
     @property
     def rows(self) -> int:
@@ -79,6 +82,15 @@ def upload_beam_step(inp, device="cuda", max_tail: Optional[int] = None,
                   max_blocks_per_seq=inp.max_blocks, max_seq_len=inp.max_seq_len, max_q_len=1)
     rows, Hq, D = inp.batch * inp.beam, inp.num_q_heads, inp.head_dim
     f32 = dict(device=device, dtype=torch.float32)
+    # The fused step reads every beam's current token as row b * W + k; the
+    # generator lists them only for requests with a tail, request-major.
+    beam_rows = [b * inp.beam + k for b in range(inp.batch) if inp.tail_len[b] > 0
+                 for k in range(inp.beam)]
+    knb = np.zeros((rows, inp.num_kv_heads, D), np.float32)
+    vnb = np.zeros((rows, inp.num_kv_heads, D), np.float32)
+    if beam_rows:
+        knb[beam_rows] = inp.k_new
+        vnb[beam_rows] = inp.v_new
     return BeamStepDevice(
         dtype=inp.dtype, batch=inp.batch, beam=inp.beam, num_q_heads=Hq,
         num_kv_heads=inp.num_kv_heads, head_dim=D, plan=plan,
@@ -97,6 +109,8 @@ def upload_beam_step(inp, device="cuda", max_tail: Optional[int] = None,
         lse_part=torch.zeros((2, rows, Hq), **f32),
         out=torch.zeros((rows, Hq, D), device=device, dtype=TORCH_DTYPE[inp.dtype]),
         lse_out=torch.zeros((rows, Hq), **f32),
+        k_new_beams=to_device(knb, inp.dtype, device),
+        v_new_beams=to_device(vnb, inp.dtype, device),
     )
 
 
@@ -122,6 +136,13 @@ def run_beam_step(s: BeamStepDevice, stream=None, write: bool = True) -> None:
     B.bsp_merge(rows, s.num_q_heads, s.head_dim, 2, s.o_part, s.lse_part,
                 rows * s.num_q_heads * s.head_dim, rows * s.num_q_heads, s.out, s.dtype,
                 s.lse_out, stream)
+
+
+def run_decode_step(s: BeamStepDevice, stream=None) -> None:
+    """The whole step in one launch (bsp_decode_step): token write + prefix + tail."""
+    B.bsp_decode_step(s.plan, s.q, s.k_new_beams, s.v_new_beams, s.num_kv_heads * s.head_dim,
+                      s.k_pool, s.v_pool, s.block_tables, s.cache_indirection, s.out,
+                      s.lse_out, stream)
 
 
 @dataclass

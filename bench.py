@@ -1,14 +1,18 @@
 """Benchmark: one cascade beam-decode attention step per layer on one MI355X.
 
-A step is bsp_write_kv (current tokens) + bsp_prefix_attn + bsp_tail_attn +
-bsp_merge over all B*W beams of one layer. Consecutive timed steps rotate over
+A step is one bsp_decode_step launch over all B*W beams of one layer: the
+current-token KV write, the shared prompt attended once per request and every
+beam's tail, merged in one online softmax. The same step as four launches
+(bsp_write_kv + bsp_prefix_attn + bsp_tail_attn + bsp_merge) and the per-beam
+comparator are timed beside it. Consecutive timed steps rotate over
 several layers, each with its own KV pool, query and new-token buffers, so
 every step reads its prompt pages from HBM rather than from the 256 MB
 last-level cache (as consecutive layers of a model would). Inputs are seeded
 synthetic draws already resident in HBM when the timed region starts.
 
-Prints one JSON line. The dominant kernel's roofline entry uses HIP events
-recorded on the launch stream around every timed launch of it.
+Prints one JSON line. The roofline entry is the step kernel: its algorithmic
+bytes per launch over its average duration from HIP events recorded on the
+launch stream around every timed launch.
 """
 
 from __future__ import annotations
@@ -115,6 +119,8 @@ def main() -> None:
                     help="rotating layer copies (0: enough to exceed 1 GB of KV)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--naive", action="store_true", help="also time the per-beam comparator")
+    ap.add_argument("--skip-unfused", action="store_true",
+                    help="do not time the four-launch (unfused) step beside the fused one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -135,7 +141,7 @@ def main() -> None:
     B.load_library()
     dev = "cuda"
     inp = synth.make_beam_step(args.config, args.seed, garbage="unit")
-    step_bytes, prefix_bytes = algorithmic_bytes(inp)
+    step_bytes, _ = algorithmic_bytes(inp)
     base = S.upload_beam_step(inp, dev)
     pool_bytes = base.k_pool.numel() * base.k_pool.element_size() * 2
     layers = args.layers or max(2, int(np.ceil(1.0e9 / pool_bytes)))
@@ -147,6 +153,8 @@ def main() -> None:
         c.v_pool = base.v_pool.clone()
         c.k_new = base.k_new.clone()
         c.v_new = base.v_new.clone()
+        c.k_new_beams = base.k_new_beams.clone()
+        c.v_new_beams = base.v_new_beams.clone()
         copies.append(c)
     t_plan = time.perf_counter()
     S.plan_beam_step(base)
@@ -154,23 +162,33 @@ def main() -> None:
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
 
-    def one(i, timed_ev=None):
+    def fused(i, ev=None):
         c = copies[i % layers]
-        S.write_current_tokens(c)
-        if timed_ev is not None:
-            timed_ev[0].record(stream)
-        B.bsp_prefix_attn(c.plan, c.q, c.k_pool, c.v_pool, c.o_part[0], c.lse_part[0])
-        if timed_ev is not None:
-            timed_ev[1].record(stream)
-        B.bsp_tail_attn(c.plan, c.q, c.k_pool, c.v_pool, c.block_tables, c.cache_indirection,
-                        c.o_part[1], c.lse_part[1])
-        rows = c.rows
-        B.bsp_merge(rows, c.num_q_heads, c.head_dim, 2, c.o_part, c.lse_part,
-                    rows * c.num_q_heads * c.head_dim, rows * c.num_q_heads, c.out, c.dtype,
-                    c.lse_out)
+        if ev is not None:
+            ev[0].record(stream)
+        S.run_decode_step(c)
+        if ev is not None:
+            ev[1].record(stream)
+
+    def unfused(i):
+        S.run_beam_step(copies[i % layers])
+
+    def timed(fn, steps, warmup, events):
+        for i in range(warmup):
+            fn(i)
+        B.bsp_check(base.plan)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)] if events else None
+        t0 = time.perf_counter()
+        for i in range(steps):
+            fn(i, ev[i]) if events else fn(i)
+        torch.cuda.synchronize()
+        sec = time.perf_counter() - t0
+        B.bsp_check(base.plan)
+        launch_ms = float(np.mean([a.elapsed_time(b) for a, b in ev])) if events else None
+        return sec, launch_ms
 
     if args.calibrate_copy:
         n = args.calibrate_copy << 20
@@ -180,40 +198,29 @@ def main() -> None:
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for i in range(args.warmup):
-        one(i)
-    B.bsp_check(base.plan)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        one(i, ev[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    B.bsp_check(base.plan)
-    sec = t1 - t0
+
+    # the timed step: bsp_decode_step, one launch per layer step
+    sec, fused_ms = timed(fused, args.steps, args.warmup, True)
     ms_per_step = sec / args.steps * 1e3
-    prefix_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    achieved = prefix_bytes / (prefix_ms * 1e-3) / 1e9
+    achieved = step_bytes / (fused_ms * 1e-3) / 1e9
 
     extra = {}
+    if not args.skip_unfused:
+        n_unf = max(10, args.steps // 4)
+        usec, _ = timed(unfused, n_unf, 5, False)
+        extra["unfused_4_launch_ms_per_step"] = usec / n_unf * 1e3
     if args.naive:
         out = torch.empty_like(base.out)
-        for i in range(3):
-            c = copies[i % layers]
-            B.bsp_naive_beam_attn(c.plan, c.q, c.k_pool, c.v_pool, c.block_tables,
-                                  c.cache_indirection, out)
-        torch.cuda.synchronize()
-        n_naive = max(3, min(20, args.steps // 10))
-        ta = time.perf_counter()
-        for i in range(n_naive):
+
+        def naive(i):
             c = copies[i % layers]
             S.write_current_tokens(c)
             B.bsp_naive_beam_attn(c.plan, c.q, c.k_pool, c.v_pool, c.block_tables,
                                   c.cache_indirection, out)
-        torch.cuda.synchronize()
-        naive_ms = (time.perf_counter() - ta) / n_naive * 1e3
-        extra["naive_per_beam_ms_per_step"] = naive_ms
-        extra["cascade_speedup_vs_naive"] = naive_ms / ms_per_step
+        n_naive = max(3, min(20, args.steps // 10))
+        nsec, _ = timed(naive, n_naive, 2, False)
+        extra["naive_per_beam_ms_per_step"] = nsec / n_naive * 1e3
+        extra["cascade_speedup_vs_naive"] = extra["naive_per_beam_ms_per_step"] / ms_per_step
 
     result = {
         "metric": METRIC,
@@ -233,6 +240,7 @@ def main() -> None:
             "name": args.config,
             "batch": inp.batch,
             "beam": inp.beam,
+            "step": "bsp_decode_step (current-token write + shared prefix + tails, one launch)",
             "layers_rotated": layers,
             "step_alg_bytes": step_bytes,
             "step_alg_gbps": step_bytes / (ms_per_step * 1e-3) / 1e9,
@@ -240,15 +248,15 @@ def main() -> None:
             **extra,
         },
         "roofline": {
-            "kernel": "prefix_mfma_kernel (bsp_prefix_attn)",
+            "kernel": "prefix_mfma_kernel<FUSED> (bsp_decode_step)",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": None,
-            "alg_bytes_per_launch": prefix_bytes,
-            "avg_launch_us": prefix_ms * 1e3,
+            "alg_bytes_per_launch": step_bytes,
+            "avg_launch_us": fused_ms * 1e3,
         },
     }
     if not args.no_cpu_baseline:

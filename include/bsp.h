@@ -220,6 +220,31 @@ bsp_status_t bsp_merge(int32_t rows, int32_t heads, int32_t head_dim, int32_t n_
                        float* lse_out, hipStream_t stream);
 
 /*
+ * The whole beam decode step of one layer in one launch (the fused form of
+ * bsp_write_kv + bsp_prefix_attn + bsp_tail_attn + bsp_merge; PR #21738,
+ * fused-tail commit: the current-token KV write, the tail attention through
+ * cache_indirection and the merge with the prefix run as one launch per
+ * layer). For each request and KV head one workgroup writes its beams'
+ * current tokens into their pages, attends every beam's query rows to the
+ * shared prompt and then to the beam's own tail in the same online softmax
+ * (so the merge is exact and no partial state leaves the kernel), and writes
+ * the final output. The tail position S_b - 1 (the current token) is read from
+ * k_new/v_new of the parent beam, never from the pool being written.
+ *   q              [B, W, 1, Hq, D] (plan q_len must be 1; beam mode; no kv_split)
+ *   k_new, v_new   current token of every beam: row (b * W + k) at element
+ *                  (b * W + k) * new_row_stride, [Hkv][D] contiguous, 16-byte
+ *                  aligned; rows of requests without a tail are not read
+ *   k_pool, v_pool written at each beam's slot for position S_b - 1
+ *   o_out          dtype [B * W][Hq][D]; lse_out float [B * W][Hq] or null
+ * bf16/f16 only (BSP_ERR_UNSUPPORTED for f32: use the separate calls).
+ */
+bsp_status_t bsp_decode_step(bsp_plan_t plan, const void* q, const void* k_new,
+                             const void* v_new, int64_t new_row_stride, void* k_pool,
+                             void* v_pool, const int32_t* block_tables_d,
+                             const int32_t* cache_indirection_d, void* o_out, float* lse_out,
+                             hipStream_t stream);
+
+/*
  * Comparator, not part of the cascade: per-beam attention over each beam's
  * whole sequence, reading the shared prompt once per (beam, KV head) through
  * the beam's own block table, as the decode kernel that the cascade replaces

@@ -294,3 +294,103 @@ def test_full_size_qwen3_0p6b_sampled():
         fo, fl = oracle.beam_attention_one(ref, b, k)
         assert np.abs(out[b, k] - fo[0]).max() <= to
         assert np.abs(lse[b, k] - fl[0]).max() <= tl
+
+
+# ------------------------------------------- fused decode step (one launch)
+
+def _run_fused_and_check(inp, what, max_tail=None):
+    s = S.upload_beam_step(inp, DEV, max_tail=max_tail)
+    S.plan_beam_step(s)
+    S.run_decode_step(s)
+    B.bsp_check(s.plan)
+    torch.cuda.synchronize()
+    ref = _applied(inp)
+    # the token write is bit-exact
+    assert torch.equal(s.k_pool.cpu(), S.to_device(ref.k_pool, inp.dtype, "cpu")), what
+    assert torch.equal(s.v_pool.cpu(), S.to_device(ref.v_pool, inp.dtype, "cpu")), what
+    fo, fl = oracle.beam_decode_attention(ref)
+    return assert_close(s.out, s.lse_out, fo, fl, inp.dtype, f"{what} fused output")
+
+
+FUSED_CASES = [c for c in STEP_CASES if "f32" not in c]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES)
+@pytest.mark.parametrize("seed", [0, 1])
+def test_decode_step_matches_oracle(case, seed):
+    kw = dict(STEP_CASES[case])
+    cfg = kw.pop("cfg")
+    inp = synth.make_beam_step(cfg, seed, **kw)
+    say(f"fused step {case} seed={seed} P={inp.prefix_len.tolist()} T={inp.tail_len.tolist()}")
+    mt = 8 if "fixed_tail" in case else None
+    say(f"  max |dO| = {_run_fused_and_check(inp, case, max_tail=mt):.3g}")
+
+
+@pytest.mark.parametrize("case", list(GROUP_CASES))
+def test_decode_step_group_sizes(case):
+    g, dt = GROUP_CASES[case]
+    cfg = BeamConfig(case, 2, 7, 2 * g, 2, 128, dt, 16, (70, 150), (0, 5), True)
+    say(f"fused group size {g} {dt}")
+    _run_fused_and_check(synth.make_beam_step(cfg, 12), case)
+
+
+@pytest.mark.parametrize("G,W,dt", [(5, 90, "bf16"), (4, 100, "f16"), (2, 150, "bf16")])
+def test_decode_step_query_tiles(G, W, dt):
+    """W * G above one workgroup's 192 rows: several query tiles per (request, KV head),
+    beams straddling tiles when 192 % G != 0; every token written exactly once."""
+    cfg = BeamConfig("qtiles", 2, W, 2 * G, 2, 64, dt, 16, (40, 90), (1, 6), True)
+    inp = synth.make_beam_step(cfg, 3)
+    say(f"fused query tiles G={G} W={W} rows={W * G}")
+    _run_fused_and_check(inp, f"qtiles G={G}")
+
+
+def test_decode_step_long_tails_resolved_on_the_fly():
+    """More tail slots per tile than the LDS table holds (192 beams x 20 positions)."""
+    cfg = BeamConfig("longtail", 1, 192, 2, 2, 64, "bf16", 16, (30, 60), (17, 20), True)
+    inp = synth.make_beam_step(cfg, 4)
+    say(f"fused long tails T={inp.tail_len.tolist()}")
+    _run_fused_and_check(inp, "long tails")
+
+
+def test_decode_step_rejects_unsupported():
+    inp = synth.make_beam_step("tiny", 0)
+    s = S.upload_beam_step(inp, DEV)
+    S.plan_beam_step(s)
+    with pytest.raises(B.BspError) as ei:
+        S.run_decode_step(s)
+    assert ei.value.name == "BSP_ERR_UNSUPPORTED"
+
+
+def test_decode_step_bad_parent_is_skipped_and_reported():
+    inp = synth.make_beam_step("qwen3_0p6b", 6, batch=2, tail_range=(3, 4))
+    s = S.upload_beam_step(inp, DEV)
+    S.plan_beam_step(s)
+    P = int(inp.prefix_len[0])
+    s.cache_indirection[0, 2, P] = -3
+    S.run_decode_step(s)
+    with pytest.raises(B.BspError) as ei:
+        B.bsp_check(s.plan)
+    assert ei.value.name == "BSP_ERR_DEVICE_INDEX"
+    assert not torch.isnan(s.out.float()).any()
+
+
+def test_full_size_wide_beam_fused_sampled():
+    """128 requests x 96 beams, bf16, shuffled pages, the fused step the bench times."""
+    inp = synth.make_beam_step("wide_beam", 0, garbage="unit")
+    say(f"full-size wide_beam: pages={inp.num_pages}")
+    s = S.upload_beam_step(inp, DEV)
+    S.plan_beam_step(s)
+    S.run_decode_step(s)
+    B.bsp_check(s.plan)
+    torch.cuda.synchronize()
+    ref = _applied(inp)
+    rng = np.random.default_rng(1)
+    picks = [(int(b), int(k)) for b, k in zip(rng.integers(0, 128, 12), rng.integers(0, 96, 12))]
+    picks += [(0, 0), (127, 95)]
+    out = s.out.float().cpu().numpy().reshape(128, 96, 16, 128)
+    lse = s.lse_out.cpu().numpy().reshape(128, 96, 16)
+    to, tl = TOL["bf16"]
+    for b, k in picks:
+        fo, fl = oracle.beam_attention_one(ref, b, k)
+        assert np.abs(out[b, k] - fo[0]).max() <= to
+        assert np.abs(lse[b, k] - fl[0]).max() <= tl
