@@ -500,7 +500,7 @@ bsp_status_t bsp_decode_step(bsp_plan_t pl, const void* q, const void* k_new, co
   f.o_out = o_out;
   f.lse_out = lse_out;
   return after_launch(
-      pl, bsp::launch_decode_step(p, f, d.dtype, d.head_dim, pl->rows_per_req, stream),
+      pl, bsp::launch_decode_step(p, f, d.dtype, d.head_dim, pl->rows_per_req, pl->tail_pad, stream),
       "decode step launch", stream);
 }
 

@@ -130,7 +130,7 @@ hipError_t launch_write_kv(const WriteKvParams& p, int dtype, hipStream_t s);
 hipError_t launch_prefix(const PrefixParams& p, int dtype, int head_dim, int rows_per_req,
                          hipStream_t s);
 hipError_t launch_decode_step(const PrefixParams& p, const FusedParams& f, int dtype,
-                              int head_dim, int rows_per_req, hipStream_t s);
+                              int head_dim, int rows_per_req, int tail_pad, hipStream_t s);
 // Rows per workgroup the prefix kernel picks for this shape (so the host can
 // size the grid before launching).
 int prefix_rows_per_tile(int dtype, int head_dim, int rows_per_req);

@@ -85,6 +85,33 @@ __device__ __forceinline__ float wave_max(float x) {
 __device__ __forceinline__ float xor16(float x) { return __shfl_xor(x, 16, 64); }
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// Max / sum of the four lanes {l, l^16, l^32, l^48}, every one of them getting
+// the same value. The permlane swaps hand each lane its partner's value in a
+// single VALU operation (no LDS round trip): a swap of x with itself across
+// 16-lane rows (or 32-lane halves) leaves x in one result register and the
+// partner's x in the other, in an order that depends on the lane, so only
+// order-free combinations (max, and the commutative sum of two terms) are taken.
+// The halves are converted through by-value helpers: a bit cast applied
+// directly to an element of the returned vector reads element 0.
+__device__ __forceinline__ float u2f(unsigned u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ unsigned f2u(float f) { return __builtin_bit_cast(unsigned, f); }
+__device__ __forceinline__ float max4x16(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
+  const unsigned a0 = a[0], a1 = a[1];
+  x = fmaxf(u2f(a0), u2f(a1));
+  const auto b = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+  const unsigned b0 = b[0], b1 = b[1];
+  return fmaxf(u2f(b0), u2f(b1));
+}
+__device__ __forceinline__ float sum4x16(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
+  const unsigned a0 = a[0], a1 = a[1];
+  x = u2f(a0) + u2f(a1);
+  const auto b = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+  const unsigned b0 = b[0], b1 = b[1];
+  return u2f(b0) + u2f(b1);
+}
+
 __device__ __forceinline__ void record_fault(int32_t* bits, int32_t* count, int32_t* first,
                                              int32_t bit, int32_t value) {
   // Vector-memory atomics on the caller's workspace.

@@ -60,6 +60,8 @@ constexpr int kPageWin = 1024;
 // Resolved tail slots of the fused step, per (beam of this query tile, tail
 // position); larger tails are resolved on the fly.
 constexpr int kTailSlots = 3072;
+// Lazy rescaling threshold of the online softmax, in base-2 exponent units.
+constexpr float kLazyLog2 = 8.f;
 
 // XOR swizzle of the 16-byte chunks of an LDS key row (a function of the low 4
 // row bits): chunk c of row r is stored at chunk c ^ swz(r). It keeps both the
@@ -92,6 +94,20 @@ __device__ __forceinline__ void lds_dma16(const void* src, void* lds_dst) {
       (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)lds_dst);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                :: "s"(m0), "v"(src) : "memory", "m0");
+}
+// The same with a wave-uniform 64-bit base and a per-lane 32-bit byte offset
+// (the scalar-base form of the load: no per-lane 64-bit address arithmetic).
+__device__ __forceinline__ void lds_dma16_s(const void* base, unsigned voff, void* lds_dst) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)lds_dst);
+  // readfirstlane yields a signed int: widen through unsigned, or a low word
+  // with bit 31 set would be sign-extended over the high word.
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint64_t lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)b);
+  const uint64_t hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(b >> 32));
+  const uint64_t sb = lo | (hi << 32);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(m0), "v"(voff), "s"(sb) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -130,14 +146,18 @@ __device__ __forceinline__ int32_t resolve_fused_slot(const PrefixParams& p, con
   return ((page * p.hkv + g) << p.page_shift) + (j & ((1 << p.page_shift) - 1));
 }
 
-// FUSED = false: bsp_prefix_attn (fp32 partial state per key split).
-// FUSED = true: bsp_decode_step, one launch per layer step: the workgroup of
-// (request, KV head) also writes its beams' current tokens, then after the
-// shared keys attends each beam's tail (gathered through cache_indirection) in
-// the same online softmax and writes the final output in the storage dtype.
-template <typename T, int D, int MB, int KT, int NST, bool FUSED>
+// MODE 0: bsp_prefix_attn (fp32 partial state per key split).
+// MODE 1 and 2: bsp_decode_step, one launch per layer step: the workgroup of
+// (request, KV head, query tile) also writes its beams' current tokens and
+// attends each beam's tail (gathered through cache_indirection) in the same
+// online softmax as the shared keys, then writes the final output in the
+// storage dtype. MODE 1 resolves the tail slots into an LDS table and streams
+// the tail rows through the tile pipeline after the shared keys; MODE 2, for
+// tails too long for that table, gathers them key by key afterwards.
+template <typename T, int D, int MB, int KT, int NST, int MODE>
 __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma_kernel(PrefixParams p,
                                                                                           FusedParams f) {
+  constexpr bool FUSED = MODE != 0;
   using V8 = typename Mfma<T>::V8;
   constexpr int NDS = D / 32;                       // contraction steps of S^T
   constexpr int NDB = D / 16;                       // 16-row blocks of O^T
@@ -151,11 +171,11 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
   static_assert(NST >= 2 && NST <= 4 && (NST - 2) * LPT < 64, "pipeline depth");
   __shared__ __attribute__((aligned(1024))) T lds_kv[NST][2][TILE];
   __shared__ int lds_pages[kPageWin];
-  __shared__ int lds_tail[FUSED ? kTailSlots : 1];
+  __shared__ int lds_tail[MODE == 1 ? kTailSlots : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform by construction
   const int l16 = lane & 15;
   const int l4 = lane >> 4;
 
@@ -185,38 +205,56 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
   const int kb_first = (w.qt * rt) / p.group;   // beams with a row in this tile
   const int kb_last = min(p.W - 1, ((w.qt + 1) * rt - 1) / p.group);
   const int nbt = kb_last - kb_first + 1;
-  bool tail_in_lds = false;
   if constexpr (FUSED) {
     const int n_tail = ri.tail;
     const int jcur = ri.seq - 1;
     if (n_tail > 0) {
-      // a beam's token is written by the tile holding its first row
-      const int kw_lo = (w.qt * rt + p.group - 1) / p.group;
-      const int kw_hi = min(p.W, ((w.qt + 1) * rt + p.group - 1) / p.group);
-      for (int task = tid; task < (kw_hi - kw_lo) * CPR; task += 256) {
-        const int kk = kw_lo + task / CPR;
-        const int c = task % CPR;
-        const int32_t page =
-            f.block_tables[((int64_t)w.b * p.W + kk) * f.max_blocks + (jcur >> shift)];
-        if (page < 0 || page >= p.num_pages) {
-          if (c == 0)
-            record_fault(&p.hdr->error_bits, &p.hdr->fault_count, &p.hdr->first_value,
-                         kErrTailPage, page);
-          continue;
-        }
-        const int64_t src = ((int64_t)w.b * p.W + kk) * f.new_stride + (int64_t)w.g * D + c * 8;
-        const int64_t dst = ((((int64_t)page * p.hkv + w.g) << shift) + (jcur & pmask)) * D + c * 8;
-        *reinterpret_cast<u32x4*>(static_cast<T*>(f.k_pool_w) + dst) =
-            *reinterpret_cast<const u32x4*>(static_cast<const T*>(f.k_new) + src);
-        *reinterpret_cast<u32x4*>(static_cast<T*>(f.v_pool_w) + dst) =
-            *reinterpret_cast<const u32x4*>(static_cast<const T*>(f.v_new) + src);
-      }
-      tail_in_lds = nbt * n_tail <= kTailSlots;
-      if (tail_in_lds) {
-        for (int task = tid; task < nbt * n_tail; task += 256) {
-          const int kk = kb_first + task / n_tail;
-          const int t = task % n_tail;
-          lds_tail[task] = resolve_fused_slot(p, f, w.b, kk, w.g, ri.prefix + t, jcur);
+      // MODE 1: resolve the tail slots of this tile's beams into the LDS table
+      // (the host checked that it holds them), several per thread at a time:
+      // all parent lookups, then all page lookups.
+      if constexpr (MODE == 1) {
+        const int n_sl = nbt * n_tail;
+        constexpr int TR = 4;
+        for (int base = 0; base < n_sl; base += 256 * TR) {
+          int32_t src[TR], page[TR];
+#pragma unroll
+          for (int i = 0; i < TR; ++i) {
+            const int task = base + i * 256 + tid;
+            src[i] = -1;
+            if (task < n_sl) {
+              const int kk = kb_first + task / n_tail;
+              src[i] = f.ci[((int64_t)w.b * p.W + kk) * f.max_seq_len + ri.prefix + task % n_tail];
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < TR; ++i) {
+            const int task = base + i * 256 + tid;
+            const int j = ri.prefix + task % n_tail;
+            page[i] = -1;
+            if (task < n_sl && src[i] >= 0 && src[i] < p.W && j != jcur)
+              page[i] = f.block_tables[((int64_t)w.b * p.W + src[i]) * f.max_blocks + (j >> shift)];
+          }
+#pragma unroll
+          for (int i = 0; i < TR; ++i) {
+            const int task = base + i * 256 + tid;
+            if (task >= n_sl) continue;
+            const int j = ri.prefix + task % n_tail;
+            int32_t e;
+            if (src[i] < 0 || src[i] >= p.W) {
+              record_fault(&p.hdr->error_bits, &p.hdr->fault_count, &p.hdr->first_value,
+                           kErrTailParent, src[i]);
+              e = -1;
+            } else if (j == jcur) {
+              e = -2 - src[i];
+            } else if (page[i] < 0 || page[i] >= p.num_pages) {
+              record_fault(&p.hdr->error_bits, &p.hdr->fault_count, &p.hdr->first_value,
+                           kErrTailPage, page[i]);
+              e = -1;
+            } else {
+              e = ((page[i] * p.hkv + w.g) << shift) + (j & pmask);
+            }
+            lds_tail[task] = e;
+          }
         }
       }
     }
@@ -269,29 +307,195 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
   const float c2 = p.scale_log2e;
   const int keys_per_win = kPageWin << shift;
 
-  for (int w0 = (w.k_lo / keys_per_win) * keys_per_win; w0 < w.k_hi; w0 += keys_per_win) {
-    const int seg_lo = max(w.k_lo, w0);
-    const int seg_hi = min(w.k_hi, w0 + keys_per_win);
-    const int pg0 = w0 >> shift;
-    const int npg = ((seg_hi - 1) >> shift) - pg0 + 1;
-    __syncthreads();  // every wave is done with the previous window
-    for (int i = tid; i < npg; i += 256) {
-      int32_t page = p.pages[ri.page_off + pg0 + i];
-      if (page < 0 || page >= p.num_pages) {  // the plan validated these; flag corruption
-        record_fault(&p.hdr->error_bits, &p.hdr->fault_count, &p.hdr->first_value,
-                     kErrPrefixPage, page);
-        page = 0;
+  // One tile against the query blocks of this wave: S^T = K Q^T, masking,
+  // online softmax, O^T += V^T P^T. `act(qb)` (wave-uniform) skips query
+  // blocks the tile cannot touch; `visible(qb, kk)` is the mask of key kk of
+  // the tile for this lane's query row of block qb, consulted only when
+  // `full` is false.
+  auto attend_tile = [&](const T* lk, const T* lv, bool full, auto&& act, auto&& visible) {
+    // ---- S^T = K Q^T
+    f32x4 sacc[NKB][MB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < MB; ++qb) sacc[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int r = kb * 16 + l16;
+        const V8 a = *reinterpret_cast<const V8*>(&lk[r * D + (((ds * 4 + l4) ^ lds_swz<D>(r)) << 3)]);
+#pragma unroll
+        for (int qb = 0; qb < MB; ++qb)
+          if (act(qb)) sacc[kb][qb] = Mfma<T>::mma(a, qv[qb][ds], sacc[kb][qb]);
       }
-      lds_pages[i] = page;
     }
-    wait_vmcnt<0>();
-    __syncthreads();
 
-    // Issue the direct-to-LDS loads of one tile into one stage. Rows past the
-    // key range re-read the tile's first row; their scores are masked to -inf
-    // so they add exactly zero.
+    // ---- masking and online softmax, per query block. A row's reference
+    // max m is raised only when the tile's max passes it by more than
+    // kLazyLog2 (base-2 units); otherwise O and l keep their scale and the
+    // tile's probabilities stay below 2^kLazyLog2, far inside the bf16/f16
+    // range. The log-sum-exp is taken against the same m, so the result is
+    // that of the exact running-max update.
+#pragma unroll
+    for (int qb = 0; qb < MB; ++qb) {
+      if (!act(qb)) continue;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float sv = sacc[kb][qb][e];
+          if (!full && !visible(qb, kb * 16 + l4 * 4 + e)) sv = -INFINITY;
+          sacc[kb][qb][e] = sv;
+          mx = fmaxf(mx, sv);
+        }
+      }
+      mx = max4x16(mx);
+      // NaN (both -inf: nothing visible yet) compares false
+      const bool grow = (mx - mrow[qb]) * c2 > kLazyLog2;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float m_new = fmaxf(mrow[qb], mx);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = fast_exp2((mrow[qb] - m_use) * c2);
+        mrow[qb] = m_new;
+        lrow[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[db][qb] *= alpha;
+      }
+      const float moff = mrow[qb] == -INFINITY ? 0.f : -mrow[qb] * c2;
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float pr = fast_exp2(fmaf(sacc[kb][qb][e], c2, moff));
+          sacc[kb][qb][e] = pr;
+          rs += pr;
+        }
+      }
+      lrow[qb] += rs;
+    }
+
+    // ---- O^T += V^T P^T (V^T operand by transpose reads)
+#pragma unroll
+    for (int s2 = 0; s2 < NS2; ++s2) {
+      V8 pb[MB];
+#pragma unroll
+      for (int qb = 0; qb < MB; ++qb) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pb[qb][e] = Traits<T>::from_f(sacc[2 * s2][qb][e]);
+          pb[qb][4 + e] = Traits<T>::from_f(sacc[2 * s2 + 1][qb][e]);
+        }
+      }
+      const int ra = 32 * s2 + 4 * l4 + (l16 >> 2);   // row read by this lane (+16 for the upper half)
+      const int swa = lds_swz<D>(ra);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int col = db * 16 + 4 * (l16 & 3);
+        const int off = (((col >> 3) ^ swa) << 3) + (col & 7);
+        // The operand is assembled from whole 32-bit words of the two reads.
+        const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr(&lv[ra * D + off]));
+        const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr(&lv[(ra + 16) * D + off]));
+        const V8 a = __builtin_bit_cast(V8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+        for (int qb = 0; qb < MB; ++qb)
+          if (act(qb)) oacc[db][qb] = Mfma<T>::mma(a, pb[qb], oacc[db][qb]);
+      }
+    }
+  };
+
+  // ---- fused step, tails from the slot table: after the shared keys, the
+  // tails of this tile's beams follow as more tiles of the same load
+  // pipeline, row u = (beam - kb_first) * n_tail + position. A tail key is
+  // visible only to its own beam's query rows.
+  const int n_tail = FUSED ? ri.tail : 0;
+  const int n_tail_keys = MODE == 1 ? nbt * n_tail : 0;
+  const int ntt = (n_tail_keys + KT - 1) / KT;
+  int tail_lo[MB];  // this lane's rows of the slot table: [tail_lo, tail_lo + n_tail)
+#pragma unroll
+  for (int qb = 0; qb < MB; ++qb) {
+    const int r = row0 + qb * 16 + l16;
+    tail_lo[qb] = r < M ? (r / p.group - kb_first) * n_tail : -KT - n_tail;
+  }
+  // a finite row for tail rows that carry no key (padding, invalid slots)
+  const int64_t pad_row = ((int64_t)w.b * p.W + kb_first) * f.new_stride + (int64_t)w.g * D;
+
+  const int win_first = w.k_lo / keys_per_win;
+  const int n_win = w.k_hi > w.k_lo ? (w.k_hi - 1) / keys_per_win - win_first + 1 : 0;
+  const int n_win_iter = max(n_win, ntt > 0 ? 1 : 0);
+
+  for (int wi = 0; wi < n_win_iter; ++wi) {
+    const bool has_prompt = wi < n_win;
+    const int w0 = (win_first + wi) * keys_per_win;
+    const int seg_lo = has_prompt ? max(w.k_lo, w0) : 0;
+    const int seg_hi = has_prompt ? min(w.k_hi, w0 + keys_per_win) : 0;
+    const int pg0 = w0 >> shift;
+    __syncthreads();  // every wave is done with the previous window; slot table visible
+    if (has_prompt) {
+      const int npg = ((seg_hi - 1) >> shift) - pg0 + 1;
+      for (int i = tid; i < npg; i += 256) {
+        int32_t page = p.pages[ri.page_off + pg0 + i];
+        if (page < 0 || page >= p.num_pages) {  // the plan validated these; flag corruption
+          record_fault(&p.hdr->error_bits, &p.hdr->fault_count, &p.hdr->first_value,
+                       kErrPrefixPage, page);
+          page = 0;
+        }
+        lds_pages[i] = page;
+      }
+      wait_vmcnt<0>();
+      __syncthreads();
+    }
+    const int ntp = has_prompt ? (seg_hi - seg_lo + KT - 1) / KT : 0;
+    const int nt = ntp + (wi == n_win_iter - 1 ? ntt : 0);
+
+    // Issue the direct-to-LDS loads of one tile into one stage.
     auto issue = [&](int tile, int stage) {
+      if (MODE == 1 && tile >= ntp) {
+        const int ub = (tile - ntp) * KT;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int chunk = (wave * NI + i) * 64 + lane;
+          const int r = chunk / CPR;
+          const int c = (chunk % CPR) ^ lds_swz<D>(r);
+          const int u = ub + r;
+          const int32_t e = u < n_tail_keys ? lds_tail[u] : -1;
+          const T* ksrc;
+          const T* vsrc;
+          if (e >= 0) {
+            ksrc = kpool + (int64_t)e * D + c * 8;
+            vsrc = vpool + (int64_t)e * D + c * 8;
+          } else {
+            const int64_t o = e <= -2 ? ((int64_t)w.b * p.W + (-2 - e)) * f.new_stride + (int64_t)w.g * D
+                                      : pad_row;
+            ksrc = static_cast<const T*>(f.k_new) + o + c * 8;
+            vsrc = static_cast<const T*>(f.v_new) + o + c * 8;
+          }
+          lds_dma16(ksrc, &lds_kv[stage][0][(wave * NI + i) * (1024 / (int)sizeof(T))]);
+          lds_dma16(vsrc, &lds_kv[stage][1][(wave * NI + i) * (1024 / (int)sizeof(T))]);
+        }
+        return;
+      }
       const int t0 = seg_lo + tile * KT;
+      if ((t0 & pmask) + KT <= pmask + 1) {
+        // The tile lies in one page: one scalar base per pool, and each lane
+        // adds its fixed offset (rows past the key range re-read row t0).
+        const int page = __builtin_amdgcn_readfirstlane(lds_pages[(t0 >> shift) - pg0]);
+        const int64_t base = ((((int64_t)page * p.hkv + w.g) << shift) + (t0 & pmask)) * D;
+        const T* kb = kpool + base;
+        const T* vb = vpool + base;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int chunk = (wave * NI + i) * 64 + lane;
+          const int r = chunk / CPR;
+          const int c = (chunk % CPR) ^ lds_swz<D>(r);
+          const unsigned voff = (unsigned)(((t0 + r < seg_hi ? r : 0) * D + c * 8) * (int)sizeof(T));
+          lds_dma16_s(kb, voff, &lds_kv[stage][0][(wave * NI + i) * (1024 / (int)sizeof(T))]);
+          lds_dma16_s(vb, voff, &lds_kv[stage][1][(wave * NI + i) * (1024 / (int)sizeof(T))]);
+        }
+        return;
+      }
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int chunk = (wave * NI + i) * 64 + lane;
@@ -301,19 +505,13 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
         if (j >= seg_hi) j = t0;
         const int page = lds_pages[(j >> shift) - pg0];
         const int64_t off = ((((int64_t)page * p.hkv + w.g) << shift) + (j & pmask)) * D + c * 8;
-        T* dk = &lds_kv[stage][0][(wave * NI + i) * (1024 / (int)sizeof(T))];
-        T* dv = &lds_kv[stage][1][(wave * NI + i) * (1024 / (int)sizeof(T))];
-        lds_dma16(kpool + off, dk);
-        lds_dma16(vpool + off, dv);
+        lds_dma16(kpool + off, &lds_kv[stage][0][(wave * NI + i) * (1024 / (int)sizeof(T))]);
+        lds_dma16(vpool + off, &lds_kv[stage][1][(wave * NI + i) * (1024 / (int)sizeof(T))]);
       }
     };
 
-    const int nt = (seg_hi - seg_lo + KT - 1) / KT;
-#pragma unroll
-    for (int s = 0; s < NST - 1; ++s)
-      if (s < nt) issue(s, s);
-
-    for (int t = 0; t < nt; ++t) {
+    // Wait for tile t, then reuse the stage of tile t-1 for tile t+NST-1.
+    auto advance = [&](int t) {
       // Tile t's loads are done once at most (tiles issued after it) * LPT are in flight.
       const int ahead = min(NST - 2, nt - 1 - t);
       if (ahead >= 2) wait_vmcnt<(NST >= 4 ? 2 : 0) * LPT>();
@@ -321,102 +519,48 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
       else wait_vmcnt<0>();
       __syncthreads();  // all threads' loads of tile t landed; tile t-1's stage is free
       if (t + NST - 1 < nt) issue(t + NST - 1, (t + NST - 1) % NST);
+    };
+
+#pragma unroll
+    for (int st = 0; st < NST - 1; ++st)
+      if (st < nt) issue(st, st);
+
+    for (int t = 0; t < ntp; ++t) {
+      advance(t);
       if (!wave_active) continue;
-      const T* lk = lds_kv[t % NST][0];
-      const T* lv = lds_kv[t % NST][1];
       const int t0 = seg_lo + t * KT;
-
-      // ---- S^T = K Q^T
-      f32x4 sacc[NKB][MB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < MB; ++qb) sacc[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const int r = kb * 16 + l16;
-          const V8 a = *reinterpret_cast<const V8*>(&lk[r * D + (((ds * 4 + l4) ^ lds_swz<D>(r)) << 3)]);
-#pragma unroll
-          for (int qb = 0; qb < MB; ++qb) sacc[kb][qb] = Mfma<T>::mma(a, qv[qb][ds], sacc[kb][qb]);
-        }
-      }
-
-      // ---- masking and online softmax, per query block
-      const bool full = (t0 + KT <= w.k_hi) && !p.causal;
-#pragma unroll
-      for (int qb = 0; qb < MB; ++qb) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float s = sacc[kb][qb][e];
-            if (!full) {
-              const int j = t0 + kb * 16 + l4 * 4 + e;
-              if (j >= w.k_hi || j > climit[qb]) s = -INFINITY;
-            }
-            sacc[kb][qb][e] = s;
-            mx = fmaxf(mx, s);
-          }
-        }
-        mx = fmaxf(mx, xor16(mx));
-        mx = fmaxf(mx, xor32(mx));
-        const float m_new = fmaxf(mrow[qb], mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2((mrow[qb] - m_use) * c2);
-        const float moff = -m_use * c2;
-        mrow[qb] = m_new;
-        float rs = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float pr = fast_exp2(fmaf(sacc[kb][qb][e], c2, moff));
-            sacc[kb][qb][e] = pr;
-            rs += pr;
-          }
-        }
-        lrow[qb] = fmaf(lrow[qb], alpha, rs);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[db][qb] *= alpha;
-      }
-
-      // ---- O^T += V^T P^T (V^T operand by transpose reads)
-#pragma unroll
-      for (int s2 = 0; s2 < NS2; ++s2) {
-        V8 pb[MB];
+      attend_tile(lds_kv[t % NST][0], lds_kv[t % NST][1], (t0 + KT <= w.k_hi) && !p.causal,
+                  [&](int) { return true; },
+                  [&](int qb, int kk) { return t0 + kk < w.k_hi && t0 + kk <= climit[qb]; });
+    }
+    if constexpr (MODE == 1) {
+      for (int t = ntp; t < nt; ++t) {
+        advance(t);
+        if (!wave_active) continue;
+        const int ub = (t - ntp) * KT;
+        const int u_hi = min(ub + KT, n_tail_keys);
+        bool act[MB];
 #pragma unroll
         for (int qb = 0; qb < MB; ++qb) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            pb[qb][e] = Traits<T>::from_f(sacc[2 * s2][qb][e]);
-            pb[qb][4 + e] = Traits<T>::from_f(sacc[2 * s2 + 1][qb][e]);
-          }
+          // rows of the slot table this query block reads: [lo, hi) (wave-uniform)
+          const int r_lo = row0 + qb * 16;
+          const int r_hi = min(r_lo + 16, M);
+          const int lo = r_lo < M ? (r_lo / p.group - kb_first) * n_tail : INT_MAX;
+          const int hi = r_lo < M ? ((r_hi - 1) / p.group - kb_first + 1) * n_tail : 0;
+          act[qb] = lo < u_hi && hi > ub;
         }
-        const int ra = 32 * s2 + 4 * l4 + (l16 >> 2);   // row read by this lane (+16 for the upper half)
-        const int swa = lds_swz<D>(ra);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int col = db * 16 + 4 * (l16 & 3);
-          const int off = (((col >> 3) ^ swa) << 3) + (col & 7);
-          // Assemble the operand from whole 32-bit words: building it from
-          // 16-bit elements gets miscompiled into duplicated halves.
-          const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr(&lv[ra * D + off]));
-          const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr(&lv[(ra + 16) * D + off]));
-          const V8 a = __builtin_bit_cast(V8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-#pragma unroll
-          for (int qb = 0; qb < MB; ++qb) oacc[db][qb] = Mfma<T>::mma(a, pb[qb], oacc[db][qb]);
-        }
+        attend_tile(lds_kv[t % NST][0], lds_kv[t % NST][1], false,
+                    [&](int qb) { return act[qb]; },
+                    [&](int qb, int kk) {
+                      const int u = ub + kk;
+                      return u >= tail_lo[qb] && u < tail_lo[qb] + n_tail && lds_tail[u] != -1;
+                    });
       }
     }
   }
 
-  // ---- fused step: each beam's tail joins the same online softmax
-  if constexpr (FUSED) {
-    const int n_tail = ri.tail;
-    __syncthreads();  // tail slot table written (the key loop may have had no tiles)
+  // ---- MODE 2: each beam's tail joins the same online softmax, key by key
+  if constexpr (MODE == 2) {
     if (n_tail > 0 && wave_active) {
       const int jcur = ri.seq - 1;
       constexpr int TC = 2;  // tail keys in flight together
@@ -442,8 +586,7 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
             const int t = t0 + c;
             int32_t e = -1;
             if (t < n_tail && row_ok)
-              e = tail_in_lds ? lds_tail[(kbeam - kb_first) * n_tail + t]
-                              : resolve_fused_slot(p, f, w.b, kbeam, w.g, ri.prefix + t, jcur);
+              e = resolve_fused_slot(p, f, w.b, kbeam, w.g, ri.prefix + t, jcur);
             ok[c] = e != -1;
             if (e >= 0) {
               kr[c] = kpool + (int64_t)e * D + 4 * l4;
@@ -474,8 +617,7 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
 #pragma unroll
                 for (int i = 0; i < 4; ++i) part = fmaf(Traits<T>::to_f(qe[i]), Traits<T>::to_f(ke[i]), part);
               }
-              part += xor16(part);
-              part += xor32(part);
+              part = sum4x16(part);
               sc[c] = ok[c] ? part : -INFINITY;
             }
             float mx = sc[0];
@@ -521,9 +663,7 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
   // ---- epilogue: normalise and write the partial state (or the final output)
 #pragma unroll
   for (int qb = 0; qb < MB; ++qb) {
-    float lt = lrow[qb];
-    lt += xor16(lt);
-    lt += xor32(lt);
+    const float lt = sum4x16(lrow[qb]);
     const int r = row0 + qb * 16 + l16;
     if (!wave_active || r >= M) continue;
     const int hh = r % p.group;
@@ -551,6 +691,52 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
       for (int db = 0; db < NDB; ++db)
         *reinterpret_cast<f32x4*>(op + db * 16) = oacc[db][qb] * inv;
       if (l4 == 0) p.lse_part[ohead] = lse;
+    }
+  }
+
+  // ---- fused step: write this tile's beams' current tokens into the pool
+  if constexpr (FUSED) {
+    const int jcur = ri.seq - 1;
+    if (n_tail <= 0) return;
+    // A beam's token is written by the tile holding its first row. It is
+    // written last: nothing in this launch reads it back from the pool (the
+    // tails take the current token from the new-token rows), and here its
+    // loads and stores delay no tile. Every thread issues the loads of
+    // several tasks before using any of them.
+    const int kw_lo = (w.qt * rt + p.group - 1) / p.group;
+    const int kw_hi = min(p.W, ((w.qt + 1) * rt + p.group - 1) / p.group);
+    const int n_tw = (kw_hi - kw_lo) * CPR;
+    constexpr int TW = 16;
+    for (int base = 0; base < n_tw; base += 256 * TW) {
+      int32_t page[TW];
+      u32x4 kd[TW], vd[TW];
+#pragma unroll
+      for (int i = 0; i < TW; ++i) {
+        const int task = base + i * 256 + tid;
+        page[i] = -1;
+        if (task < n_tw) {
+          const int kk = kw_lo + task / CPR;
+          const int64_t src = ((int64_t)w.b * p.W + kk) * f.new_stride + (int64_t)w.g * D + (task % CPR) * 8;
+          page[i] = f.block_tables[((int64_t)w.b * p.W + kk) * f.max_blocks + (jcur >> shift)];
+          kd[i] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(f.k_new) + src);
+          vd[i] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(f.v_new) + src);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < TW; ++i) {
+        const int task = base + i * 256 + tid;
+        if (task >= n_tw) continue;
+        if (page[i] < 0 || page[i] >= p.num_pages) {
+          if (task % CPR == 0)
+            record_fault(&p.hdr->error_bits, &p.hdr->fault_count, &p.hdr->first_value,
+                         kErrTailPage, page[i]);
+          continue;
+        }
+        const int64_t dst =
+            ((((int64_t)page[i] * p.hkv + w.g) << shift) + (jcur & pmask)) * D + (task % CPR) * 8;
+        *reinterpret_cast<u32x4*>(static_cast<T*>(f.k_pool_w) + dst) = kd[i];
+        *reinterpret_cast<u32x4*>(static_cast<T*>(f.v_pool_w) + dst) = vd[i];
+      }
     }
   }
 }
@@ -664,11 +850,11 @@ int prefix_rows_per_tile(int dtype, int head_dim, int rows_per_req) {
 }
 
 // Tile size and pipeline depth per head_dim: 64 KB of K/V stages per workgroup.
-template <typename T, bool FUSED>
+template <typename T, int MODE>
 static void launch_mfma(const PrefixParams& p, const FusedParams& f, int head_dim, int mb,
                         unsigned blocks, hipStream_t s) {
 #define BSP_PFX(DD, MBB, KTT, NS) \
-  prefix_mfma_kernel<T, DD, MBB, KTT, NS, FUSED><<<blocks, 256, 0, s>>>(p, f)
+  prefix_mfma_kernel<T, DD, MBB, KTT, NS, MODE><<<blocks, 256, 0, s>>>(p, f)
   if (head_dim == 64) {
     if (mb == 1) BSP_PFX(64, 1, 64, 4);
     else if (mb == 2) BSP_PFX(64, 2, 64, 4);
@@ -695,19 +881,26 @@ hipError_t launch_prefix(const PrefixParams& p, int dtype, int head_dim, int row
   } else {
     const int mb = pick_mb(head_dim, rows_per_req);
     const FusedParams none{};
-    if (dtype == BSP_F16) launch_mfma<_Float16, false>(p, none, head_dim, mb, blocks, s);
-    else launch_mfma<__bf16, false>(p, none, head_dim, mb, blocks, s);
+    if (dtype == BSP_F16) launch_mfma<_Float16, 0>(p, none, head_dim, mb, blocks, s);
+    else launch_mfma<__bf16, 0>(p, none, head_dim, mb, blocks, s);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_decode_step(const PrefixParams& p, const FusedParams& f, int dtype,
-                              int head_dim, int rows_per_req, hipStream_t s) {
+                              int head_dim, int rows_per_req, int tail_pad, hipStream_t s) {
   const unsigned blocks = (unsigned)(p.B * p.hkv * p.n_qtiles);
   if (blocks == 0) return hipSuccess;
   const int mb = pick_mb(head_dim, rows_per_req);
-  if (dtype == BSP_F16) launch_mfma<_Float16, true>(p, f, head_dim, mb, blocks, s);
-  else launch_mfma<__bf16, true>(p, f, head_dim, mb, blocks, s);
+  // beams with a row in one query tile, at most; their tail slots must fit the LDS table
+  const int nbt_max = min(p.W, (64 * mb - 1) / p.group + 2);
+  if ((int64_t)nbt_max * tail_pad <= kTailSlots) {
+    if (dtype == BSP_F16) launch_mfma<_Float16, 1>(p, f, head_dim, mb, blocks, s);
+    else launch_mfma<__bf16, 1>(p, f, head_dim, mb, blocks, s);
+  } else {
+    if (dtype == BSP_F16) launch_mfma<_Float16, 2>(p, f, head_dim, mb, blocks, s);
+    else launch_mfma<__bf16, 2>(p, f, head_dim, mb, blocks, s);
+  }
   return hipGetLastError();
 }
 

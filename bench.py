@@ -121,6 +121,9 @@ def main() -> None:
     ap.add_argument("--naive", action="store_true", help="also time the per-beam comparator")
     ap.add_argument("--skip-unfused", action="store_true",
                     help="do not time the four-launch (unfused) step beside the fused one")
+    ap.add_argument("--warm-seconds", type=float, default=0.5,
+                    help="untimed run of the step before the counted warmup steps, to reach "
+                         "steady GPU clocks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -174,7 +177,17 @@ def main() -> None:
     def unfused(i):
         S.run_beam_step(copies[i % layers])
 
-    def timed(fn, steps, warmup, events):
+    def timed(fn, steps, warmup, events, warm_seconds=0.0):
+        # Bring the GPU to its steady clocks first: a few dozen launches of a
+        # 50-500 us kernel are too short for that, and the first timed
+        # milliseconds after idle run about 15% slow.
+        t_end = time.perf_counter() + warm_seconds
+        i = 0
+        while time.perf_counter() < t_end:
+            for _ in range(16):
+                fn(i)
+                i += 1
+            torch.cuda.synchronize()
         for i in range(warmup):
             fn(i)
         B.bsp_check(base.plan)
@@ -200,7 +213,7 @@ def main() -> None:
         del src, dst
 
     # the timed step: bsp_decode_step, one launch per layer step
-    sec, fused_ms = timed(fused, args.steps, args.warmup, True)
+    sec, fused_ms = timed(fused, args.steps, args.warmup, True, args.warm_seconds)
     ms_per_step = sec / args.steps * 1e3
     achieved = step_bytes / (fused_ms * 1e-3) / 1e9
 
@@ -242,6 +255,7 @@ def main() -> None:
             "beam": inp.beam,
             "step": "bsp_decode_step (current-token write + shared prefix + tails, one launch)",
             "layers_rotated": layers,
+            "warm_seconds": args.warm_seconds,
             "step_alg_bytes": step_bytes,
             "step_alg_gbps": step_bytes / (ms_per_step * 1e-3) / 1e9,
             "plan_host_ms": t_plan * 1e3,
