@@ -42,6 +42,42 @@ WORKLOADS = {
 }
 
 
+KERNEL_SOURCES = ("beam_search_shared_amd/csrc/prefix_attn.hip",
+                  "beam_search_shared_amd/csrc/device_common.h",
+                  "beam_search_shared_amd/csrc/bsp_internal.h")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the sources of the fused kernel (ties counter records to a kernel version)."""
+    import hashlib
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(root, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(config: str):
+    """HBM bytes per launch of the fused kernel from the committed counter summaries
+    (profiles/*.md, lines ``traffic-record: {json}``), if they were taken on the
+    current kernel sources; otherwise None."""
+    root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
+    want = kernel_source_hash()
+    if not os.path.isdir(root):
+        return None
+    for name in sorted(os.listdir(root)):
+        if not name.endswith(".md"):
+            continue
+        with open(os.path.join(root, name)) as fh:
+            for line in fh:
+                if line.startswith("traffic-record:"):
+                    rec = json.loads(line.split(":", 1)[1])
+                    if rec.get("config") == config and rec.get("kernel_source_sha256") == want:
+                        return rec
+    return None
+
+
 def algorithmic_bytes(inp):
     """Bytes the method must move in one step, and those of the prefix kernel alone.
 
@@ -166,18 +202,28 @@ def main() -> None:
 
     stream = torch.cuda.current_stream()
 
-    def fused(i, ev=None):
-        c = copies[i % layers]
-        if ev is not None:
-            ev[0].record(stream)
-        S.run_decode_step(c)
-        if ev is not None:
-            ev[1].record(stream)
+    # The timed step calls the C entry point directly with its arguments
+    # marshalled once per layer copy, so that the loop measures the GPU rather
+    # than Python: bsp_decode_step, one launch per layer step.
+    lib = B.load_library()
+    decode = lib.bsp_decode_step
+    stream_h = stream.cuda_stream
+    row_stride = base.num_kv_heads * base.head_dim
+    fused_args = [(c.plan.handle, c.q.data_ptr(), c.k_new_beams.data_ptr(), c.v_new_beams.data_ptr(),
+                   row_stride, c.k_pool.data_ptr(), c.v_pool.data_ptr(), c.block_tables.data_ptr(),
+                   c.cache_indirection.data_ptr(), c.out.data_ptr(),
+                   c.lse_out.data_ptr() if c.lse_out is not None else None, stream_h)
+                  for c in copies]
+
+    def fused(i):
+        if decode(*fused_args[i % layers]) != 0:
+            B.bsp_check(base.plan)  # raises with the library's message
+            raise RuntimeError("bsp_decode_step failed")
 
     def unfused(i):
         S.run_beam_step(copies[i % layers])
 
-    def timed(fn, steps, warmup, events, warm_seconds=0.0):
+    def timed(fn, steps, warmup, warm_seconds=0.0):
         # Bring the GPU to its steady clocks first: a few dozen launches of a
         # 50-500 us kernel are too short for that, and the first timed
         # milliseconds after idle run about 15% slow.
@@ -192,16 +238,18 @@ def main() -> None:
             fn(i)
         B.bsp_check(base.plan)
         torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)] if events else None
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
+        e0.record(stream)
         for i in range(steps):
-            fn(i, ev[i]) if events else fn(i)
+            fn(i)
+        e1.record(stream)
         torch.cuda.synchronize()
         sec = time.perf_counter() - t0
         B.bsp_check(base.plan)
-        launch_ms = float(np.mean([a.elapsed_time(b) for a, b in ev])) if events else None
-        return sec, launch_ms
+        # GPU time per step on the launch stream (one kernel per fused step)
+        return sec, e0.elapsed_time(e1) / steps
 
     if args.calibrate_copy:
         n = args.calibrate_copy << 20
@@ -213,14 +261,15 @@ def main() -> None:
         del src, dst
 
     # the timed step: bsp_decode_step, one launch per layer step
-    sec, fused_ms = timed(fused, args.steps, args.warmup, True, args.warm_seconds)
+    sec, fused_ms = timed(fused, args.steps, args.warmup, args.warm_seconds)
     ms_per_step = sec / args.steps * 1e3
     achieved = step_bytes / (fused_ms * 1e-3) / 1e9
+    traffic = recorded_traffic(args.config)
 
     extra = {}
     if not args.skip_unfused:
         n_unf = max(10, args.steps // 4)
-        usec, _ = timed(unfused, n_unf, 5, False)
+        usec, _ = timed(unfused, n_unf, 5)
         extra["unfused_4_launch_ms_per_step"] = usec / n_unf * 1e3
     if args.naive:
         out = torch.empty_like(base.out)
@@ -231,7 +280,7 @@ def main() -> None:
             B.bsp_naive_beam_attn(c.plan, c.q, c.k_pool, c.v_pool, c.block_tables,
                                   c.cache_indirection, out)
         n_naive = max(3, min(20, args.steps // 10))
-        nsec, _ = timed(naive, n_naive, 2, False)
+        nsec, _ = timed(naive, n_naive, 2)
         extra["naive_per_beam_ms_per_step"] = nsec / n_naive * 1e3
         extra["cascade_speedup_vs_naive"] = extra["naive_per_beam_ms_per_step"] / ms_per_step
 
@@ -268,7 +317,8 @@ def main() -> None:
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": None,
+            "traffic": traffic["traffic_bytes_per_launch"] if traffic else None,
+            "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "alg_bytes_per_launch": step_bytes,
             "avg_launch_us": fused_ms * 1e3,
         },
