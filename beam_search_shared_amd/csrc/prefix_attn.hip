@@ -36,16 +36,29 @@
 namespace bsp {
 
 template <typename T> struct Mfma;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// mma: 16x16 output, 32-long contraction (8 elements per lane);
+// mma16: 16-long contraction (4 elements per lane), operands as raw 16-bit words.
 template <> struct Mfma<__bf16> {
   using V8 = bf16x8;
   static __device__ __forceinline__ f32x4 mma(V8 a, V8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mma16(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
   }
 };
 template <> struct Mfma<_Float16> {
   using V8 = f16x8;
   static __device__ __forceinline__ f32x4 mma(V8 a, V8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mma16(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
   }
 };
 
@@ -81,6 +94,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
+// Wait until this wave's LDS reads have completed (lgkmcnt 0, other counters free).
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
 
 // 16-byte direct global-to-LDS load (one per lane; a wave fills 1 KB at
 // `lds_dst` + 16 * lane). Issued through inline asm so that the compiler does
@@ -111,7 +128,6 @@ __device__ __forceinline__ void lds_dma16_s(const void* base, unsigned voff, voi
 }
 #pragma clang diagnostic pop
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // Four consecutive keys' values of one column, transposed across 16 lanes:
@@ -406,34 +422,17 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
     }
   };
 
-  // ---- fused step, tails from the slot table: after the shared keys, the
-  // tails of this tile's beams follow as more tiles of the same load
-  // pipeline, row u = (beam - kb_first) * n_tail + position. A tail key is
-  // visible only to its own beam's query rows.
   const int n_tail = FUSED ? ri.tail : 0;
-  const int n_tail_keys = MODE == 1 ? nbt * n_tail : 0;
-  const int ntt = (n_tail_keys + KT - 1) / KT;
-  int tail_lo[MB];  // this lane's rows of the slot table: [tail_lo, tail_lo + n_tail)
-#pragma unroll
-  for (int qb = 0; qb < MB; ++qb) {
-    const int r = row0 + qb * 16 + l16;
-    tail_lo[qb] = r < M ? (r / p.group - kb_first) * n_tail : -KT - n_tail;
-  }
-  // a finite row for tail rows that carry no key (padding, invalid slots)
-  const int64_t pad_row = ((int64_t)w.b * p.W + kb_first) * f.new_stride + (int64_t)w.g * D;
-
   const int win_first = w.k_lo / keys_per_win;
   const int n_win = w.k_hi > w.k_lo ? (w.k_hi - 1) / keys_per_win - win_first + 1 : 0;
-  const int n_win_iter = max(n_win, ntt > 0 ? 1 : 0);
 
-  for (int wi = 0; wi < n_win_iter; ++wi) {
-    const bool has_prompt = wi < n_win;
+  for (int wi = 0; wi < n_win; ++wi) {
     const int w0 = (win_first + wi) * keys_per_win;
-    const int seg_lo = has_prompt ? max(w.k_lo, w0) : 0;
-    const int seg_hi = has_prompt ? min(w.k_hi, w0 + keys_per_win) : 0;
+    const int seg_lo = max(w.k_lo, w0);
+    const int seg_hi = min(w.k_hi, w0 + keys_per_win);
     const int pg0 = w0 >> shift;
-    __syncthreads();  // every wave is done with the previous window; slot table visible
-    if (has_prompt) {
+    __syncthreads();  // every wave is done with the previous window
+    {
       const int npg = ((seg_hi - 1) >> shift) - pg0 + 1;
       for (int i = tid; i < npg; i += 256) {
         int32_t page = p.pages[ri.page_off + pg0 + i];
@@ -447,36 +446,11 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
       wait_vmcnt<0>();
       __syncthreads();
     }
-    const int ntp = has_prompt ? (seg_hi - seg_lo + KT - 1) / KT : 0;
-    const int nt = ntp + (wi == n_win_iter - 1 ? ntt : 0);
+    const int ntp = (seg_hi - seg_lo + KT - 1) / KT;
+    const int nt = ntp;
 
     // Issue the direct-to-LDS loads of one tile into one stage.
     auto issue = [&](int tile, int stage) {
-      if (MODE == 1 && tile >= ntp) {
-        const int ub = (tile - ntp) * KT;
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          const int chunk = (wave * NI + i) * 64 + lane;
-          const int r = chunk / CPR;
-          const int c = (chunk % CPR) ^ lds_swz<D>(r);
-          const int u = ub + r;
-          const int32_t e = u < n_tail_keys ? lds_tail[u] : -1;
-          const T* ksrc;
-          const T* vsrc;
-          if (e >= 0) {
-            ksrc = kpool + (int64_t)e * D + c * 8;
-            vsrc = vpool + (int64_t)e * D + c * 8;
-          } else {
-            const int64_t o = e <= -2 ? ((int64_t)w.b * p.W + (-2 - e)) * f.new_stride + (int64_t)w.g * D
-                                      : pad_row;
-            ksrc = static_cast<const T*>(f.k_new) + o + c * 8;
-            vsrc = static_cast<const T*>(f.v_new) + o + c * 8;
-          }
-          lds_dma16(ksrc, &lds_kv[stage][0][(wave * NI + i) * (1024 / (int)sizeof(T))]);
-          lds_dma16(vsrc, &lds_kv[stage][1][(wave * NI + i) * (1024 / (int)sizeof(T))]);
-        }
-        return;
-      }
       const int t0 = seg_lo + tile * KT;
       if ((t0 & pmask) + KT <= pmask + 1) {
         // The tile lies in one page: one scalar base per pool, and each lane
@@ -533,28 +507,137 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
                   [&](int) { return true; },
                   [&](int qb, int kk) { return t0 + kk < w.k_hi && t0 + kk <= climit[qb]; });
     }
-    if constexpr (MODE == 1) {
-      for (int t = ntp; t < nt; ++t) {
-        advance(t);
-        if (!wave_active) continue;
-        const int ub = (t - ntp) * KT;
-        const int u_hi = min(ub + KT, n_tail_keys);
+  }
+
+  // ---- MODE 1: each wave attends its own beams' tails (slot-table rows
+  // u = (beam - kb_first) * n_tail + t) in 16-key sub-tiles, double-buffered
+  // in its quarter of the now idle tile ring, with no workgroup barrier. A
+  // tail key is visible only to its own beam's query rows.
+  if constexpr (MODE == 1) {
+    __syncthreads();  // every wave is done with the ring; the slot table is visible
+    if (n_tail > 0 && wave_active) {
+      constexpr int KW = 16;                                       // keys per sub-tile
+      constexpr int SUB = KW * D;                                  // elements of K (or V)
+      constexpr int NIW = SUB * (int)sizeof(T) / 1024;             // 1 KB loads each
+      constexpr int REGION = (int)(sizeof(lds_kv) / sizeof(T)) / 4;  // elements per wave
+      constexpr int NBUF = REGION >= 4 * SUB ? 2 : 1;
+      static_assert(REGION >= 2 * SUB && NIW >= 1, "sub-tile must fit a wave's share of the ring");
+      T* region = &lds_kv[0][0][0] + wave * REGION;
+      const int r_last = min(row0 + 16 * MB, M) - 1;
+      const int u_lo = (row0 / p.group - kb_first) * n_tail;
+      const int u_hi = (r_last / p.group - kb_first + 1) * n_tail;
+      const int n_sub = (u_hi - u_lo + KW - 1) / KW;
+      int tail_lo[MB];  // this lane's rows of the slot table: [tail_lo, tail_lo + n_tail)
+#pragma unroll
+      for (int qb = 0; qb < MB; ++qb) {
+        const int r = row0 + qb * 16 + l16;
+        tail_lo[qb] = r < M ? (r / p.group - kb_first) * n_tail : INT_MIN / 2;
+      }
+      // a finite row for sub-tile rows that carry no key (padding, invalid slots)
+      const int64_t pad_row = ((int64_t)w.b * p.W + kb_first) * f.new_stride + (int64_t)w.g * D;
+      auto issue_sub = [&](int sidx, int buf) {
+        T* dk = region + buf * 2 * SUB;
+#pragma unroll
+        for (int i = 0; i < NIW; ++i) {
+          const int chunk = i * 64 + lane;
+          const int r = chunk / CPR;
+          const int c = (chunk % CPR) ^ lds_swz<D>(r);
+          const int u = u_lo + sidx * KW + r;
+          const int32_t e = u < u_hi ? lds_tail[u] : -1;
+          const T* ksrc;
+          const T* vsrc;
+          if (e >= 0) {
+            ksrc = kpool + (int64_t)e * D + c * 8;
+            vsrc = vpool + (int64_t)e * D + c * 8;
+          } else {
+            const int64_t o = e <= -2 ? ((int64_t)w.b * p.W + (-2 - e)) * f.new_stride + (int64_t)w.g * D
+                                      : pad_row;
+            ksrc = static_cast<const T*>(f.k_new) + o + c * 8;
+            vsrc = static_cast<const T*>(f.v_new) + o + c * 8;
+          }
+          lds_dma16(ksrc, dk + i * (1024 / (int)sizeof(T)));
+          lds_dma16(vsrc, dk + SUB + i * (1024 / (int)sizeof(T)));
+        }
+      };
+      issue_sub(0, 0);
+      if (NBUF == 2 && n_sub > 1) issue_sub(1, 1);
+      for (int sidx = 0; sidx < n_sub; ++sidx) {
+        const int buf = NBUF == 2 ? (sidx & 1) : 0;
+        if (NBUF == 2 && sidx + 1 < n_sub) wait_vmcnt<2 * NIW>();
+        else wait_vmcnt<0>();
+        const T* lk = region + buf * 2 * SUB;
+        const T* lv = lk + SUB;
+        const int u0 = u_lo + sidx * KW;
+        // ---- S^T = K Q^T for the query blocks whose beams own keys here
+        f32x4 sacc[MB];
         bool act[MB];
 #pragma unroll
         for (int qb = 0; qb < MB; ++qb) {
-          // rows of the slot table this query block reads: [lo, hi) (wave-uniform)
           const int r_lo = row0 + qb * 16;
-          const int r_hi = min(r_lo + 16, M);
-          const int lo = r_lo < M ? (r_lo / p.group - kb_first) * n_tail : INT_MAX;
-          const int hi = r_lo < M ? ((r_hi - 1) / p.group - kb_first + 1) * n_tail : 0;
-          act[qb] = lo < u_hi && hi > ub;
+          const int lo = (r_lo / p.group - kb_first) * n_tail;
+          const int hi = ((min(r_lo + 16, M) - 1) / p.group - kb_first + 1) * n_tail;
+          act[qb] = r_lo < M && lo < min(u0 + KW, u_hi) && hi > u0;
+          sacc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        attend_tile(lds_kv[t % NST][0], lds_kv[t % NST][1], false,
-                    [&](int qb) { return act[qb]; },
-                    [&](int qb, int kk) {
-                      const int u = ub + kk;
-                      return u >= tail_lo[qb] && u < tail_lo[qb] + n_tail && lds_tail[u] != -1;
-                    });
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) {
+          const V8 a = *reinterpret_cast<const V8*>(&lk[l16 * D + (((ds * 4 + l4) ^ lds_swz<D>(l16)) << 3)]);
+#pragma unroll
+          for (int qb = 0; qb < MB; ++qb)
+            if (act[qb]) sacc[qb] = Mfma<T>::mma(a, qv[qb][ds], sacc[qb]);
+        }
+        // ---- mask (own beam, valid slot) and online softmax
+        u32x2 pb[MB];
+#pragma unroll
+        for (int qb = 0; qb < MB; ++qb) {
+          if (!act[qb]) continue;
+          float mx = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int u = u0 + l4 * 4 + e;
+            const bool vis = u >= tail_lo[qb] && u < tail_lo[qb] + n_tail && lds_tail[u] != -1;
+            const float sv = vis ? sacc[qb][e] : -INFINITY;
+            sacc[qb][e] = sv;
+            mx = fmaxf(mx, sv);
+          }
+          mx = max4x16(mx);
+          const bool grow = (mx - mrow[qb]) * c2 > kLazyLog2;
+          if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            const float m_new = fmaxf(mrow[qb], mx);
+            const float m_use = m_new == -INFINITY ? 0.f : m_new;
+            const float alpha = fast_exp2((mrow[qb] - m_use) * c2);
+            mrow[qb] = m_new;
+            lrow[qb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) oacc[db][qb] *= alpha;
+          }
+          const float moff = mrow[qb] == -INFINITY ? 0.f : -mrow[qb] * c2;
+          T e4[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float pr = fast_exp2(fmaf(sacc[qb][e], c2, moff));
+            lrow[qb] += pr;
+            e4[e] = Traits<T>::from_f(pr);
+          }
+          pb[qb] = __builtin_bit_cast(u32x2, e4);
+        }
+        // ---- O^T += V^T P^T over the 16 keys (V^T operand by transpose reads)
+        const int ra = 4 * l4 + (l16 >> 2);
+        const int swa = lds_swz<D>(ra);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int col = db * 16 + 4 * (l16 & 3);
+          const int off = (((col >> 3) ^ swa) << 3) + (col & 7);
+          const u32x2 a = __builtin_bit_cast(u32x2, lds_read_tr(&lv[ra * D + off]));
+#pragma unroll
+          for (int qb = 0; qb < MB; ++qb)
+            if (act[qb]) oacc[db][qb] = Mfma<T>::mma16(a, pb[qb], oacc[db][qb]);
+        }
+        // refill this buffer once its LDS reads are done
+        if (NBUF == 2 ? sidx + 2 < n_sub : sidx + 1 < n_sub) {
+          wait_lgkmcnt0();
+          issue_sub(NBUF == 2 ? sidx + 2 : sidx + 1, buf);
+        }
       }
     }
   }
