@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
   constexpr int NI = TILE * (int)sizeof(T) / 4096;  // 1 KB loads per wave for K (and V)
   constexpr int LPT = 2 * NI;                       // vector-memory ops per thread per tile
   static_assert(NI >= 1 && TILE * sizeof(T) % 4096 == 0, "tile must split into 1 KB loads");
-  static_assert(NST >= 2 && NST <= 4 && (NST - 2) * LPT < 64, "pipeline depth");
+  static_assert(NST >= 2 && NST <= 4 && 2 * LPT < 64, "pipeline depth");
   __shared__ __attribute__((aligned(1024))) T lds_kv[NST][2][TILE];
   __shared__ int lds_pages[kPageWin];
   __shared__ int lds_tail[MODE == 1 ? kTailSlots : 1];
@@ -323,14 +323,12 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
   const float c2 = p.scale_log2e;
   const int keys_per_win = kPageWin << shift;
 
-  // One tile against the query blocks of this wave: S^T = K Q^T, masking,
-  // online softmax, O^T += V^T P^T. `act(qb)` (wave-uniform) skips query
-  // blocks the tile cannot touch; `visible(qb, kk)` is the mask of key kk of
-  // the tile for this lane's query row of block qb, consulted only when
-  // `full` is false.
-  auto attend_tile = [&](const T* lk, const T* lv, bool full, auto&& act, auto&& visible) {
-    // ---- S^T = K Q^T
-    f32x4 sacc[NKB][MB];
+  // One tile against the query blocks of this wave, in three parts:
+  // s_tile: S^T = K Q^T;
+  // softmax_tile: masking (`visible(qb, kk)`, consulted only when `full` is
+  //   false) and the online softmax; P^T leaves as the B operand of O^T;
+  // o_tile: O^T += V^T P^T.
+  auto s_tile = [&](const T* lk, f32x4 (&sacc)[NKB][MB]) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -342,35 +340,41 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
         const int r = kb * 16 + l16;
         const V8 a = *reinterpret_cast<const V8*>(&lk[r * D + (((ds * 4 + l4) ^ lds_swz<D>(r)) << 3)]);
 #pragma unroll
-        for (int qb = 0; qb < MB; ++qb)
-          if (act(qb)) sacc[kb][qb] = Mfma<T>::mma(a, qv[qb][ds], sacc[kb][qb]);
+        for (int qb = 0; qb < MB; ++qb) sacc[kb][qb] = Mfma<T>::mma(a, qv[qb][ds], sacc[kb][qb]);
       }
     }
+  };
 
-    // ---- masking and online softmax, per query block. A row's reference
-    // max m is raised only when the tile's max passes it by more than
-    // kLazyLog2 (base-2 units); otherwise O and l keep their scale and the
-    // tile's probabilities stay below 2^kLazyLog2, far inside the bf16/f16
-    // range. The log-sum-exp is taken against the same m, so the result is
-    // that of the exact running-max update.
+  // A row's reference max m is raised only when the tile's max passes it by
+  // more than kLazyLog2 (base-2 units); otherwise O and l keep their scale and
+  // the tile's probabilities stay below 2^kLazyLog2, far inside the bf16/f16
+  // range. The log-sum-exp is taken against the same m, so the result is that
+  // of the exact running-max update.
+  auto softmax_tile = [&](f32x4 (&sacc)[NKB][MB], bool full, auto&& visible, V8 (&pb)[NS2][MB]) {
+    if (__builtin_expect(!full, 0)) {  // wave-uniform: only a tile crossing the key bound
+      asm volatile("" ::: "memory");     // keep it a branch, not selects on every tile
+#pragma unroll
+      for (int qb = 0; qb < MB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sacc[kb][qb][e] = visible(qb, kb * 16 + l4 * 4 + e) ? sacc[kb][qb][e] : -INFINITY;
+    }
 #pragma unroll
     for (int qb = 0; qb < MB; ++qb) {
-      if (!act(qb)) continue;
       float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float sv = sacc[kb][qb][e];
-          if (!full && !visible(qb, kb * 16 + l4 * 4 + e)) sv = -INFINITY;
-          sacc[kb][qb][e] = sv;
-          mx = fmaxf(mx, sv);
-        }
-      }
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[kb][qb][e]);
       mx = max4x16(mx);
       // NaN (both -inf: nothing visible yet) compares false
       const bool grow = (mx - mrow[qb]) * c2 > kLazyLog2;
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(grow) != 0, 0)) {
+        // Keep this a branch: the compiler would otherwise scale O on every
+        // tile with alpha = 1.
+        asm volatile("" ::: "memory");
         const float m_new = fmaxf(mrow[qb], mx);
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
         const float alpha = fast_exp2((mrow[qb] - m_use) * c2);
@@ -391,20 +395,20 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
         }
       }
       lrow[qb] += rs;
-    }
-
-    // ---- O^T += V^T P^T (V^T operand by transpose reads)
 #pragma unroll
-    for (int s2 = 0; s2 < NS2; ++s2) {
-      V8 pb[MB];
-#pragma unroll
-      for (int qb = 0; qb < MB; ++qb) {
+      for (int s2 = 0; s2 < NS2; ++s2) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          pb[qb][e] = Traits<T>::from_f(sacc[2 * s2][qb][e]);
-          pb[qb][4 + e] = Traits<T>::from_f(sacc[2 * s2 + 1][qb][e]);
+          pb[s2][qb][e] = Traits<T>::from_f(sacc[2 * s2][qb][e]);
+          pb[s2][qb][4 + e] = Traits<T>::from_f(sacc[2 * s2 + 1][qb][e]);
         }
       }
+    }
+  };
+
+  auto o_tile = [&](const T* lv, const V8 (&pb)[NS2][MB]) {
+#pragma unroll
+    for (int s2 = 0; s2 < NS2; ++s2) {
       const int ra = 32 * s2 + 4 * l4 + (l16 >> 2);   // row read by this lane (+16 for the upper half)
       const int swa = lds_swz<D>(ra);
 #pragma unroll
@@ -416,11 +420,17 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
         const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr(&lv[(ra + 16) * D + off]));
         const V8 a = __builtin_bit_cast(V8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 #pragma unroll
-        for (int qb = 0; qb < MB; ++qb)
-          if (act(qb)) oacc[db][qb] = Mfma<T>::mma(a, pb[qb], oacc[db][qb]);
+        for (int qb = 0; qb < MB; ++qb) oacc[db][qb] = Mfma<T>::mma(a, pb[s2][qb], oacc[db][qb]);
       }
     }
   };
+
+  // With two or more query blocks per wave the prompt loop is rotated: tile
+  // t's S^T goes to the matrix cores, then tile t-1's O^T, and tile t's
+  // softmax runs on the vector ALU while they execute. Tile t-1 then holds
+  // its stage one iteration longer, so one tile fewer is loaded ahead.
+  constexpr bool ROT = MB >= 2 && NST >= 4;
+  constexpr int AHEAD = ROT ? NST - 2 : NST - 1;  // tiles in flight beyond the one computed
 
   const int n_tail = FUSED ? ri.tail : 0;
   const int win_first = w.k_lo / keys_per_win;
@@ -484,29 +494,35 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
       }
     };
 
-    // Wait for tile t, then reuse the stage of tile t-1 for tile t+NST-1.
+    // Wait for tile t, then reuse the stage freed by the previous iteration
+    // for tile t + AHEAD.
     auto advance = [&](int t) {
       // Tile t's loads are done once at most (tiles issued after it) * LPT are in flight.
-      const int ahead = min(NST - 2, nt - 1 - t);
-      if (ahead >= 2) wait_vmcnt<(NST >= 4 ? 2 : 0) * LPT>();
-      else if (ahead == 1) wait_vmcnt<LPT>();
+      const int after = min(AHEAD - 1, nt - 1 - t);
+      if (after >= 2) wait_vmcnt<2 * LPT>();
+      else if (after == 1) wait_vmcnt<LPT>();
       else wait_vmcnt<0>();
-      __syncthreads();  // all threads' loads of tile t landed; tile t-1's stage is free
-      if (t + NST - 1 < nt) issue(t + NST - 1, (t + NST - 1) % NST);
+      __syncthreads();  // all threads' loads of tile t landed; the freed stage is unused
+      if (t + AHEAD < nt) issue(t + AHEAD, (t + AHEAD) % NST);
     };
 
 #pragma unroll
-    for (int st = 0; st < NST - 1; ++st)
+    for (int st = 0; st < AHEAD; ++st)
       if (st < nt) issue(st, st);
 
+    V8 pb[NS2][MB];
     for (int t = 0; t < ntp; ++t) {
       advance(t);
       if (!wave_active) continue;
       const int t0 = seg_lo + t * KT;
-      attend_tile(lds_kv[t % NST][0], lds_kv[t % NST][1], (t0 + KT <= w.k_hi) && !p.causal,
-                  [&](int) { return true; },
-                  [&](int qb, int kk) { return t0 + kk < w.k_hi && t0 + kk <= climit[qb]; });
+      f32x4 sacc[NKB][MB];
+      s_tile(lds_kv[t % NST][0], sacc);
+      if (ROT && t > 0) o_tile(lds_kv[(t - 1) % NST][1], pb);
+      softmax_tile(sacc, (t0 + KT <= w.k_hi) && !p.causal,
+                   [&](int qb, int kk) { return (t0 + kk < w.k_hi) & (t0 + kk <= climit[qb]); }, pb);
+      if (!ROT) o_tile(lds_kv[t % NST][1], pb);
     }
+    if (ROT && wave_active && ntp > 0) o_tile(lds_kv[(ntp - 1) % NST][1], pb);
   }
 
   // ---- MODE 1: each wave attends its own beams' tails (slot-table rows
@@ -602,7 +618,8 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
           }
           mx = max4x16(mx);
           const bool grow = (mx - mrow[qb]) * c2 > kLazyLog2;
-          if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+          if (__builtin_expect(__builtin_amdgcn_ballot_w64(grow) != 0, 0)) {
+            asm volatile("" ::: "memory");
             const float m_new = fmaxf(mrow[qb], mx);
             const float m_use = m_new == -INFINITY ? 0.f : m_new;
             const float alpha = fast_exp2((mrow[qb] - m_use) * c2);

@@ -352,6 +352,34 @@ def test_decode_step_long_tails_resolved_on_the_fly():
     _run_fused_and_check(inp, "long tails")
 
 
+def _growing_scores(inp, tail_dominates=False):
+    """Queries along one unit vector and prompt keys growing along it with position,
+    so that every 32-key tile raises the row max by more than 2^8 (the online
+    softmax must rescale on every tile); optionally current tokens far above the
+    prompt, so the rescale also happens inside the tail."""
+    D, ps = inp.head_dim, inp.page_size
+    u = np.full(D, 1.0 / np.sqrt(D), np.float32)
+    inp.q[...] = u
+    for b in range(inp.batch):
+        for j in range(int(inp.prefix_len[b])):
+            page = inp.block_tables[b, 0, j // ps]
+            inp.k_pool[page, :, j % ps, :] = u * (0.5 + 2.5 * j)
+    if tail_dominates:
+        inp.k_new[...] = u * (2.5 * inp.prefix_len.max() + 400.0)
+    for a in (inp.q, inp.k_pool, inp.k_new):
+        synth.round_to_dtype(a, inp.dtype, inplace=True)
+    return inp
+
+
+@pytest.mark.parametrize("cfg,batch", [("qwen3_0p6b", 2), ("wide_beam", 1), ("qwen3_4b", 1)])
+@pytest.mark.parametrize("tail_dominates", [False, True])
+def test_decode_step_rescales_on_every_tile(cfg, batch, tail_dominates):
+    """The lazy running-max update taken on every prompt tile (and in the tail)."""
+    inp = _growing_scores(synth.make_beam_step(cfg, 5, batch=batch, tail_range=(2, 4)), tail_dominates)
+    say(f"fused growing scores {cfg} tail_dominates={tail_dominates} P={inp.prefix_len.tolist()}")
+    _run_fused_and_check(inp, f"growing scores {cfg}")
+
+
 def test_decode_step_rejects_unsupported():
     inp = synth.make_beam_step("tiny", 0)
     s = S.upload_beam_step(inp, DEV)
