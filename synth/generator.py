@@ -22,7 +22,8 @@ notes on prompt pages and tail gathering):
   own generated rows live;
 * ``cache_indirection[b, k, j]`` for a tail position ``P_b <= j < S_b`` names
   the beam whose pages hold that position for beam ``k``; it is drawn
-  uniformly from the request's beams;
+  uniformly from the request's beams (beam search), or is ``k`` itself for
+  n parallel samples of one prompt (``parents="self"``);
 * the last tail position (the current token, when the tail is not empty) holds
   large garbage in the pool until the step's KV write puts ``k_new``/``v_new``
   there through ``slots``;
@@ -100,6 +101,10 @@ class BeamConfig:
     tail_range: tuple
     shuffle_pages: bool
     max_tail: int = 0  # fixed padded tail length for graph-style plans (0: per step)
+    # tail parents: "uniform" (beam search: each tail position of each beam names a
+    # beam drawn uniformly) or "self" (n parallel samples of one prompt: every
+    # sample reads only its own generated rows)
+    parents: str = "uniform"
 
     @property
     def max_seq_len(self) -> int:
@@ -119,6 +124,10 @@ BEAM_CONFIGS = {
     # Qwen3-4B-like layer (head_dim 64/256 variants via make_beam_step(head_dim=...)).
     "qwen3_4b": BeamConfig("qwen3_4b", 64, 30, 32, 8, 128, "f16", 32,
                            (1600, 2400), (1, 4), False),
+    # n-sample prefix sharing (parallel sampling): 16 samples of each prompt,
+    # each attending the shared prompt and its own 8-32 generated tokens.
+    "nsample": BeamConfig("nsample", 64, 16, 16, 8, 128, "bf16", 32,
+                          (400, 600), (8, 32), False, parents="self"),
 }
 
 
@@ -181,7 +190,8 @@ def make_beam_step(config, seed: int = 0, *, batch: Optional[int] = None,
                    dtype: Optional[str] = None, prefix_range: Optional[tuple] = None,
                    tail_range: Optional[tuple] = None, garbage: str = "normal",
                    spare_frac: float = 0.05, shuffle_pages: Optional[bool] = None,
-                   page_stride: int = 1, keep_logical: bool = False) -> BeamStepInputs:
+                   page_stride: int = 1, keep_logical: bool = False,
+                   parents: Optional[str] = None) -> BeamStepInputs:
     """Draw one beam-decode step of ``config`` with ``numpy.random.default_rng(seed)``.
 
     ``config`` is a name in ``BEAM_CONFIGS`` or a ``BeamConfig``.
@@ -190,7 +200,8 @@ def make_beam_step(config, seed: int = 0, *, batch: Optional[int] = None,
     other page id unused (pages only at even ids). ``garbage`` fills
     unreferenced pool rows: "normal" N(0, 100), "unit" N(0, 1), "nan". With
     "unit" (and no ``keep_logical``) the pool draw itself supplies the
-    referenced rows, which is much faster for the large configs.
+    referenced rows, which is much faster for the large configs. ``parents``
+    overrides the config's tail-parent mode ("uniform" or "self").
     """
     spec = BEAM_CONFIGS[config] if isinstance(config, str) else config
     B = batch if batch is not None else spec.batch
@@ -200,6 +211,8 @@ def make_beam_step(config, seed: int = 0, *, batch: Optional[int] = None,
     p_lo, p_hi = prefix_range if prefix_range is not None else spec.prefix_range
     t_lo, t_hi = tail_range if tail_range is not None else spec.tail_range
     shuffle = spec.shuffle_pages if shuffle_pages is None else shuffle_pages
+    parent_mode = spec.parents if parents is None else parents
+    assert parent_mode in ("uniform", "self")
     Hq, Hkv, ps = spec.num_q_heads, spec.num_kv_heads, spec.page_size
     assert Hq % Hkv == 0 and dt in DTYPES
 
@@ -274,7 +287,10 @@ def make_beam_step(config, seed: int = 0, *, batch: Optional[int] = None,
     ci = np.full((B, W, max_seq_len), -1, dtype=np.int32)
     for b in range(B):
         if T[b] > 0:
-            ci[b, :, P[b]:S[b]] = rng.integers(0, W, size=(W, T[b]))
+            if parent_mode == "self":
+                ci[b, :, P[b]:S[b]] = np.arange(W, dtype=np.int32)[:, None]
+            else:
+                ci[b, :, P[b]:S[b]] = rng.integers(0, W, size=(W, T[b]))
 
     # Current token of each beam (last tail position), written during the step.
     k_new, v_new, slots = [], [], []

@@ -154,6 +154,8 @@ STEP_CASES = {
     "strided_pages_bf16": dict(cfg="qwen3_0p6b", batch=2, page_stride=2, shuffle_pages=True),
     "f32_d128": dict(cfg="qwen3_0p6b", batch=2, dtype="f32", prefix_range=(30, 90)),
     "f32_d256": dict(cfg="qwen3_4b", batch=1, dtype="f32", head_dim=256, prefix_range=(50, 90)),
+    "nsample_bf16": dict(cfg="nsample", batch=3),
+    "nsample_f16_d64": dict(cfg="nsample", batch=2, dtype="f16", head_dim=64, beam=40),
 }
 GROUP_CASES = {f"group{g}_{dt}": (g, dt) for g, dt in
                [(1, "bf16"), (2, "f16"), (3, "f16"), (4, "bf16"), (6, "bf16"), (8, "f16")]}
@@ -400,6 +402,28 @@ def test_decode_step_bad_parent_is_skipped_and_reported():
         B.bsp_check(s.plan)
     assert ei.value.name == "BSP_ERR_DEVICE_INDEX"
     assert not torch.isnan(s.out.float()).any()
+
+
+def test_full_size_nsample_fused_sampled():
+    """64 prompts x 16 parallel samples (own tails of 8-32 tokens), the fused step."""
+    inp = synth.make_beam_step("nsample", 0, garbage="unit")
+    s = S.upload_beam_step(inp, DEV)
+    S.plan_beam_step(s)
+    S.run_decode_step(s)
+    B.bsp_check(s.plan)
+    torch.cuda.synchronize()
+    ref = _applied(inp)
+    rng = np.random.default_rng(2)
+    W = inp.beam
+    picks = [(int(b), int(k)) for b, k in zip(rng.integers(0, inp.batch, 10), rng.integers(0, W, 10))]
+    picks += [(0, 0), (inp.batch - 1, W - 1)]
+    out = s.out.float().cpu().numpy().reshape(inp.batch, W, inp.num_q_heads, inp.head_dim)
+    lse = s.lse_out.cpu().numpy().reshape(inp.batch, W, inp.num_q_heads)
+    to, tl = TOL["bf16"]
+    for b, k in picks:
+        fo, fl = oracle.beam_attention_one(ref, b, k)
+        assert np.abs(out[b, k] - fo[0]).max() <= to, (b, k)
+        assert np.abs(lse[b, k] - fl[0]).max() <= tl, (b, k)
 
 
 def test_full_size_wide_beam_fused_sampled():

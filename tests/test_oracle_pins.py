@@ -160,6 +160,26 @@ def test_beam_decode_matches_50_digit_brute_force(seed):
     assert worst <= 1e-12
 
 
+def test_self_parents_read_only_own_rows():
+    """n parallel samples of one prompt (parents = self): each sample's sequence is
+    the shared prompt followed by its own rows, and the oracle matches brute force."""
+    inp = _applied(synth.make_beam_step(PIN_CFG, 4, keep_logical=True, parents="self",
+                                        tail_range=(2, 4)))
+    o, lse = oracle.beam_decode_attention(inp)
+    scale = 1.0 / math.sqrt(inp.head_dim)
+    G = inp.num_q_heads // inp.num_kv_heads
+    for b in range(inp.batch):
+        P, S = int(inp.prefix_len[b]), int(inp.seq_len[b])
+        assert (inp.cache_indirection[b, :, P:S] == np.arange(inp.beam)[:, None]).all()
+        for k in range(inp.beam):
+            K, V = _logical_sequence(inp, b, k)
+            assert np.array_equal(K[P:], inp.own_k[b][k].astype(np.float64))
+            for h in range(inp.num_q_heads):
+                mo, ml = _mp_attention(inp.q[b, k, 0, h], K[:, h // G], V[:, h // G], scale)
+                assert abs(float(ml) - lse[b, k, 0, h]) <= 1e-12
+                assert max(abs(float(x) - y) for x, y in zip(mo, o[b, k, 0, h])) <= 1e-12
+
+
 def test_cached_prefix_matches_50_digit_brute_force():
     inp = synth.make_cached_prefix(3, valid_rows=6, q_len=4, num_q_heads=4, num_kv_heads=2,
                                    head_dim=8, dtype="f32", max_cache_rows=16)
