@@ -82,6 +82,7 @@ _SIGS = {
     "bsp_decode_step": (_I32, [_P, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "bsp_check": (_I32, [_P, _P]),
     "bsp_debug_plan_tables": (_I32, [_P, _P, _P, _P, _P, _P]),
+    "bsp_debug_plan_pairs": (_I32, [_P, _P, _P]),
     "bsp_debug_tail_slots": (_I32, [_P, _P, _P, _P, _P]),
 }
 
@@ -267,6 +268,16 @@ def bsp_debug_plan_tables(plan: Plan, B: int):
     pages = np.zeros(max(int(indptr[B]), 1), np.int32)
     _check(lib.bsp_debug_plan_tables(plan.handle, None, _ptr(pages), None, None, None))
     return indptr, pages[:int(indptr[B])], n_keys, valid, tail
+
+
+def bsp_debug_plan_pairs(plan: Plan):
+    """The plan's balanced pairs as an int32 array [n_pairs][3] = (a, b, split)."""
+    lib = load_library()
+    n = np.zeros(1, np.int32)
+    _check(lib.bsp_debug_plan_pairs(plan.handle, _ptr(n), None))
+    pairs = np.zeros((max(int(n[0]), 1), 3), np.int32)
+    _check(lib.bsp_debug_plan_pairs(plan.handle, _ptr(n), _ptr(pairs)))
+    return pairs[:int(n[0])]
 
 
 def bsp_debug_tail_slots(plan: Plan, block_tables, cache_indirection, slots_out,

@@ -13,6 +13,7 @@
 // rounded up to the key bucket, capped at the allocation, one row for an empty
 // cache (Phi-4 cached-prefix PR, TensorRT-Model-Connect #2202: Exit Criteria,
 // Implementation).
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -67,6 +68,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 }  // namespace
 
+// automatic balanced pairs: longest prompt at least this many times the shortest
+constexpr int64_t kPairSpread = 3;
+
 struct bsp_plan_s {
   bsp_layer_desc_t desc;
   int32_t max_requests = 0, max_beam = 0, max_blocks = 0, max_seq_len = 0, max_q_len = 0;
@@ -75,6 +79,11 @@ struct bsp_plan_s {
   bool check_mode = false;
   int page_shift = 0;
   size_t ws_bytes = 0;
+  // balanced pairs of the fused step (reserved when the geometry allows them)
+  bool pair_capable = false;
+  int pair_mode = 2;  // 0 never, 1 always, 2 when the prompt lengths are spread wide
+  int32_t max_pairs = 0, pair_part_floats = 0;
+  size_t pairs_off = 0, pair_count_off = 0, pair_part_off = 0;
 
   // staging ring (pinned host memory, or malloc for host-only plans)
   void* staging[2] = {nullptr, nullptr};
@@ -84,10 +93,11 @@ struct bsp_plan_s {
 
   // current plan
   bool planned = false;
-  int32_t B = 0, W = 0, q_len = 0, tail_pad = 0, n_split = 1, rows_per_req = 0;
+  int32_t B = 0, W = 0, q_len = 0, tail_pad = 0, n_split = 1, rows_per_req = 0, n_pairs = 0;
   void* ws_d = nullptr;
   void* zeroed_ws = nullptr;  // workspace whose header this plan has cleared
   std::vector<ReqInfo> h_req;
+  std::vector<bsp::PairInfo> h_pairs;
   std::vector<int32_t> h_pages;
 };
 
@@ -187,6 +197,32 @@ bsp_status_t bsp_plan_create(const bsp_layer_desc_t* desc, int32_t max_requests,
   pl->ws_bytes = align_up(pages_offset(max_requests) +
                               sizeof(int32_t) * (size_t)max_requests * max_blocks_per_seq,
                           256);
+  // Balanced pairs need, after the tables, a pair list, a flag per pair and
+  // KV head, and a partial-state slot per pair and KV head. They apply to
+  // beam decode with bf16/f16, head_dim <= 128 and at most 64 * kPairMaxMB
+  // query rows per request and KV head.
+  {
+    // BSP_PAIRS=0: never; BSP_PAIRS=1: whenever the geometry allows; otherwise
+    // the planner decides per step.
+    const char* env = std::getenv("BSP_PAIRS");
+    pl->pair_mode = env == nullptr ? 2 : env[0] == '0' ? 0 : env[0] == '1' ? 1 : 2;
+    const int G = d.num_q_heads / d.num_kv_heads;
+    pl->pair_capable = d.key_bucket == 0 && d.dtype != BSP_F32 &&
+                       d.head_dim <= 128 && (int64_t)max_beam * G <= 64 * bsp::kPairMaxMB &&
+                       pl->pair_mode != 0;
+    if (pl->pair_capable) {
+      pl->max_pairs = (max_requests + 1) / 2;
+      pl->pair_part_floats = bsp::pair_part_floats(d.head_dim, bsp::kPairMaxMB);
+      pl->pairs_off = pl->ws_bytes;
+      pl->pair_count_off = align_up(pl->pairs_off + sizeof(bsp::PairInfo) * pl->max_pairs, 256);
+      pl->pair_part_off = align_up(
+          pl->pair_count_off + sizeof(int32_t) * (size_t)pl->max_pairs * d.num_kv_heads, 256);
+      pl->ws_bytes = align_up(pl->pair_part_off + sizeof(float) * (size_t)pl->max_pairs *
+                                                      d.num_kv_heads * 256 *
+                                                      pl->pair_part_floats,
+                              256);
+    }
+  }
   for (int i = 0; i < 2; ++i) {
     if (pl->host_only) {
       pl->staging[i] = std::calloc(1, pl->ws_bytes);
@@ -344,8 +380,56 @@ bsp_status_t bsp_plan(bsp_plan_t pl, int32_t B, int32_t W, int32_t q_len,
       pages[(size_t)req[b].page_off + i] = bt(b, 0, (int)i);
   if (!pages.empty()) std::memcpy(pg_out, pages.data(), sizeof(int32_t) * pages.size());
 
+  // Balanced pairs (beam decode): longest prompt with shortest, and so on. The
+  // long request's keys are split in half of the pair's total, so that X (its
+  // first keys, then completing it) and Y (its remaining keys, then the short
+  // request in full) stream about as many keys and complete one request each.
+  int32_t n_pairs = 0;
+  std::vector<bsp::PairInfo> pairs;
+  // Pairing pays only for a wide spread of prompt lengths: with the spread of
+  // a typical batch, the end phases of the shorter requests already overlap
+  // the longer ones' streaming, and the paired kernel costs about as much as
+  // the balance recovers. Automatic pairing needs the longest prompt to be at
+  // least three times the shortest.
+  bool want_pairs = pl->pair_capable && !cached && q_len == 1 && B >= 2;
+  if (want_pairs && pl->pair_mode == 2) {
+    int32_t p_min = req[0].prefix, p_max = req[0].prefix;
+    for (int b = 1; b < B; ++b) {
+      p_min = std::min(p_min, req[b].prefix);
+      p_max = std::max(p_max, req[b].prefix);
+    }
+    want_pairs = p_max >= kPairSpread * (int64_t)p_min && p_max > 0;
+  }
+  if (want_pairs) {
+    std::vector<int32_t> order(B);
+    for (int b = 0; b < B; ++b) order[b] = b;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int32_t x, int32_t y) { return req[x].prefix > req[y].prefix; });
+    n_pairs = (B + 1) / 2;
+    pairs.resize(n_pairs);
+    constexpr int32_t kAlign = 64;
+    for (int i = 0; i < n_pairs; ++i) {
+      bsp::PairInfo& q = pairs[i];
+      q.a = order[i];
+      q.b = (B - 1 - i) > i ? order[B - 1 - i] : -1;
+      const int32_t Pa = req[q.a].prefix;
+      const int32_t Pb = q.b >= 0 ? req[q.b].prefix : 0;
+      int32_t split = Pa;
+      if (q.b >= 0) {
+        const int64_t half = ((int64_t)Pa + Pb) / 2;
+        const int64_t s2 = (half + kAlign / 2) / kAlign * kAlign;  // nearest multiple
+        if (s2 >= kAlign && s2 < Pa) split = (int32_t)s2;
+      }
+      q.split = split;
+      q.pad = 0;
+    }
+    std::memcpy(st + pl->pairs_off, pairs.data(), sizeof(bsp::PairInfo) * n_pairs);
+    std::memset(st + pl->pair_count_off, 0, sizeof(int32_t) * (size_t)n_pairs * d.num_kv_heads);
+  }
+
   if (!pl->host_only) {
-    const size_t end = pages_offset(B) + sizeof(int32_t) * pages.size();
+    size_t end = pages_offset(B) + sizeof(int32_t) * pages.size();
+    if (n_pairs > 0) end = pl->pair_count_off + sizeof(int32_t) * (size_t)n_pairs * d.num_kv_heads;
     const size_t begin = workspace_d == pl->zeroed_ws ? req_offset() : 0;
     hipError_t e = hipMemcpyAsync(static_cast<char*>(workspace_d) + begin, st + begin,
                                   end - begin, hipMemcpyHostToDevice, stream);
@@ -363,6 +447,8 @@ bsp_status_t bsp_plan(bsp_plan_t pl, int32_t B, int32_t W, int32_t q_len,
   pl->tail_pad = d.max_tail > 0 ? d.max_tail : max_tail_seen;
   pl->n_split = n_split;
   pl->rows_per_req = W * q_len * (d.num_q_heads / d.num_kv_heads);
+  pl->n_pairs = n_pairs;
+  pl->h_pairs = std::move(pairs);
   pl->ws_d = workspace_d;
   pl->h_req = std::move(req);
   pl->h_pages = std::move(pages);
@@ -499,6 +585,18 @@ bsp_status_t bsp_decode_step(bsp_plan_t pl, const void* q, const void* k_new, co
   f.max_seq_len = pl->max_seq_len;
   f.o_out = o_out;
   f.lse_out = lse_out;
+  f.pairs = nullptr;
+  f.pair_count = nullptr;
+  f.pair_part = nullptr;
+  f.n_pairs = 0;
+  f.part_floats = pl->pair_part_floats;
+  if (pl->n_pairs > 0 && pl->rows_per_req <= 64 * bsp::kPairMaxMB) {
+    char* ws = static_cast<char*>(pl->ws_d);
+    f.pairs = reinterpret_cast<const bsp::PairInfo*>(ws + pl->pairs_off);
+    f.pair_count = reinterpret_cast<int32_t*>(ws + pl->pair_count_off);
+    f.pair_part = reinterpret_cast<float*>(ws + pl->pair_part_off);
+    f.n_pairs = pl->n_pairs;
+  }
   return after_launch(
       pl, bsp::launch_decode_step(p, f, d.dtype, d.head_dim, pl->rows_per_req, pl->tail_pad, stream),
       "decode step launch", stream);
@@ -610,8 +708,9 @@ bsp_status_t bsp_check(bsp_plan_t pl, hipStream_t stream) {
   e = hipMemcpy(pl->ws_d, &zero, sizeof(zero), hipMemcpyHostToDevice);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpy (clear error word)");
   return fail(BSP_ERR_DEVICE_INDEX,
-              "kernels skipped %d out-of-range index reads/writes (bits 0x%x: 1 prompt page, 2 "
-              "cache_indirection parent, 4 tail page, 8 write slot); first value %d",
+              "kernels skipped %d out-of-range index reads/writes or waits (bits 0x%x: 1 prompt "
+              "page, 2 cache_indirection parent, 4 tail page, 8 write slot, 16 pair wait); "
+              "first value %d",
               h.fault_count, h.error_bits, h.first_value);
 }
 
@@ -629,6 +728,19 @@ bsp_status_t bsp_debug_plan_tables(bsp_plan_t pl, int32_t* indptr_h, int32_t* pa
   if (indptr_h) indptr_h[pl->B] = (int32_t)pl->h_pages.size();
   if (pages_h && !pl->h_pages.empty())
     std::memcpy(pages_h, pl->h_pages.data(), sizeof(int32_t) * pl->h_pages.size());
+  return ok();
+}
+
+bsp_status_t bsp_debug_plan_pairs(bsp_plan_t pl, int32_t* n_pairs_h, int32_t* pairs_h) {
+  if (pl == nullptr || n_pairs_h == nullptr) return fail(BSP_ERR_ARG, "null pointer");
+  if (!pl->planned) return fail(BSP_ERR_STALE_PLAN, "plan has no valid step");
+  *n_pairs_h = pl->n_pairs;
+  if (pairs_h != nullptr)
+    for (int i = 0; i < pl->n_pairs; ++i) {
+      pairs_h[3 * i] = pl->h_pairs[i].a;
+      pairs_h[3 * i + 1] = pl->h_pairs[i].b;
+      pairs_h[3 * i + 2] = pl->h_pairs[i].split;
+    }
   return ok();
 }
 

@@ -24,6 +24,7 @@ enum ErrorBits : int32_t {
   kErrTailParent = 2,   // a cache_indirection entry outside [0, W)
   kErrTailPage = 4,     // a tail block-table entry outside [0, num_pages)
   kErrWriteSlot = 8,    // a KV-write slot outside [0, num_pages * page_size)
+  kErrPairWait = 16,    // a balanced pair's partial state did not arrive within the wait
 };
 
 struct DevHeader {
@@ -33,6 +34,28 @@ struct DevHeader {
   int32_t pad[61];
 };
 static_assert(sizeof(DevHeader) == kHeaderBytes, "header size");
+
+// Balanced pairs of the fused step: the request with the longest prompt is
+// paired with the shortest, the second longest with the second shortest, and
+// so on. For each KV head, workgroup Y first attends the long request `a` over
+// keys [split, P_a) and leaves that partial state (O, running max and sum) in
+// the pair's slot, raising the pair's flag; then it attends the short request
+// `b` in full. Workgroup X attends `a` over [0, split), waits for the flag,
+// merges Y's partial state into its own and completes `a` (tail, output,
+// token write). b < 0: `a` alone (odd count). split == P_a: no split.
+struct PairInfo {
+  int32_t a, b, split, pad;
+};
+static_assert(sizeof(PairInfo) == 16, "PairInfo size");
+
+// Bounded wait for a pair's flag, in sleeps of ~128 clocks (~0.1 s in all).
+constexpr int kPairSpin = 1 << 20;
+// Per-thread floats of one partial state in a pair slot: O accumulators
+// (D/16 blocks x MB query blocks x 4) then the running max and sum per query
+// block; stored element-major over the 256 threads of a workgroup.
+constexpr int pair_part_floats(int head_dim, int mb) { return (head_dim / 16) * mb * 4 + 2 * mb; }
+// Pairing applies to query tiles of at most this many 16-row blocks per wave.
+constexpr int kPairMaxMB = 2;
 
 struct ReqInfo {
   int32_t page_off;  // first entry of this request in the page table
@@ -94,6 +117,11 @@ struct FusedParams {
   int32_t max_blocks, max_seq_len;
   void* o_out;                  // dtype [B*W][Hq][D]
   float* lse_out;               // [B*W][Hq] or null
+  // balanced pairs (null: one workgroup per request and KV head)
+  const PairInfo* pairs;
+  int32_t* pair_count;          // flags [n_pairs][Hkv], zero between launches
+  float* pair_part;             // [n_pairs][Hkv][part_floats][256]
+  int32_t n_pairs, part_floats;
 };
 
 struct TailParams {

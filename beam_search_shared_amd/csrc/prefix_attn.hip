@@ -170,10 +170,11 @@ __device__ __forceinline__ int32_t resolve_fused_slot(const PrefixParams& p, con
 // storage dtype. MODE 1 resolves the tail slots into an LDS table and streams
 // the tail rows through the tile pipeline after the shared keys; MODE 2, for
 // tails too long for that table, gathers them key by key afterwards.
-template <typename T, int D, int MB, int KT, int NST, int MODE>
+template <typename T, int D, int MB, int KT, int NST, int MODE, bool PAIR>
 __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma_kernel(PrefixParams p,
                                                                                           FusedParams f) {
   constexpr bool FUSED = MODE != 0;
+  static_assert(!PAIR || (MODE == 1 && MB <= kPairMaxMB), "pairs run in the fused step, MB <= 2");
   using V8 = typename Mfma<T>::V8;
   constexpr int NDS = D / 32;                       // contraction steps of S^T
   constexpr int NDB = D / 16;                       // 16-row blocks of O^T
@@ -189,26 +190,71 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
   __shared__ int lds_pages[kPageWin];
   __shared__ int lds_tail[MODE == 1 ? kTailSlots : 1];
 
-  const int tid = threadIdx.x;
+
+  // ---- work: one (request, KV head, key split, query tile) item; with
+  // balanced pairs (PairInfo), one or two segments of a pair for one KV head.
+  int nseg = 1;
+  int sg_b0 = 0, sg_lo0 = 0, sg_hi0 = 0, sg_b1 = 0, sg_lo1 = 0, sg_hi1 = 0;
+  bool sg_share0 = false, sg_share1 = false;
+  int pair_idx = 0, pair_role = 0;
+  WorkItem w;
+  {
+    int bid = blockIdx.x;
+    if constexpr (PAIR) {
+      // Every Y workgroup comes before every X workgroup in the grid, so an X
+      // never waits for a Y that could not be dispatched yet.
+      const int npk = f.n_pairs * p.hkv;
+      pair_role = bid < npk ? 1 : 0;
+      if (bid >= npk) bid -= npk;
+      pair_idx = bid / p.hkv;
+      w.g = bid % p.hkv;
+      w.split = 0;
+      w.qt = 0;
+      const PairInfo pr = f.pairs[pair_idx];
+      const int Pa = p.req[pr.a].valid;
+      if (pair_role == 0) {  // X: the long request's first keys, then finishes it
+        sg_b0 = pr.a; sg_lo0 = 0; sg_hi0 = pr.split; sg_share0 = pr.split < Pa;
+        nseg = 1;
+      } else if (pr.b < 0) {
+        nseg = 0;  // a request without partner: X has all of it
+      } else if (pr.split < Pa) {  // Y: the long request's last keys, then the short one
+        sg_b0 = pr.a; sg_lo0 = pr.split; sg_hi0 = Pa; sg_share0 = true;
+        sg_b1 = pr.b; sg_lo1 = 0; sg_hi1 = p.req[pr.b].valid;
+        nseg = 2;
+      } else {
+        sg_b0 = pr.b; sg_lo0 = 0; sg_hi0 = p.req[pr.b].valid;
+        nseg = 1;
+      }
+    } else {
+      w.qt = bid % p.n_qtiles;
+      bid /= p.n_qtiles;
+      w.split = bid % p.n_split;
+      bid /= p.n_split;
+      w.g = bid % p.hkv;
+      sg_b0 = bid / p.hkv;
+      const int valid = p.req[sg_b0].valid;
+      sg_lo0 = p.split_keys > 0 ? w.split * p.split_keys : 0;
+      sg_hi0 = p.split_keys > 0 ? min(valid, sg_lo0 + p.split_keys) : valid;
+      if (sg_hi0 < sg_lo0) sg_hi0 = sg_lo0;
+    }
+  }
+
+#pragma nounroll
+  for (int si = 0; si < nseg; ++si) {
+  if (si > 0) __syncthreads();  // the previous segment is done with LDS
+  w.b = si == 0 ? sg_b0 : sg_b1;
+  w.k_lo = si == 0 ? sg_lo0 : sg_lo1;
+  w.k_hi = si == 0 ? sg_hi0 : sg_hi1;
+  const bool share = PAIR && (si == 0 ? sg_share0 : sg_share1);
+  // Lane indices are derived again in every segment: hoisted out of the
+  // segment loop, everything computed from them would stay live across it.
+  int tid = threadIdx.x;
+  if constexpr (PAIR) asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform by construction
   const int l16 = lane & 15;
   const int l4 = lane >> 4;
-
-  WorkItem w;
-  {
-    int bid = blockIdx.x;
-    w.qt = bid % p.n_qtiles;
-    bid /= p.n_qtiles;
-    w.split = bid % p.n_split;
-    bid /= p.n_split;
-    w.g = bid % p.hkv;
-    w.b = bid / p.hkv;
-  }
   const ReqInfo ri = p.req[w.b];
-  w.k_lo = p.split_keys > 0 ? w.split * p.split_keys : 0;
-  w.k_hi = p.split_keys > 0 ? min(ri.valid, w.k_lo + p.split_keys) : ri.valid;
-  if (w.k_hi < w.k_lo) w.k_hi = w.k_lo;
 
   const int M = p.W * p.q_len * p.group;
   const int row0 = w.qt * (64 * MB) + wave * (16 * MB);
@@ -221,10 +267,12 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
   const int kb_first = (w.qt * rt) / p.group;   // beams with a row in this tile
   const int kb_last = min(p.W - 1, ((w.qt + 1) * rt - 1) / p.group);
   const int nbt = kb_last - kb_first + 1;
+  // Y's share of a pair ends with its partial state: no tail, output or token
+  const bool finishes = !(PAIR && share && pair_role == 1);
   if constexpr (FUSED) {
     const int n_tail = ri.tail;
     const int jcur = ri.seq - 1;
-    if (n_tail > 0) {
+    if (n_tail > 0 && finishes) {
       // MODE 1: resolve the tail slots of this tile's beams into the LDS table
       // (the host checked that it holds them), several per thread at a time:
       // all parent lookups, then all page lookups.
@@ -525,6 +573,81 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
     if (ROT && wave_active && ntp > 0) o_tile(lds_kv[(ntp - 1) % NST][1], pb);
   }
 
+  // ---- balanced pairs: Y leaves its partial state of the long request in
+  // the pair's slot and raises the flag; X waits for the flag (Y streamed
+  // fewer keys and started no later), merges, and completes the request.
+  // The slot and the flag are accessed only with agent-coherent loads and
+  // stores, and the flag is raised once those stores have completed, so no
+  // cache-wide write-back or invalidation is needed on either side.
+  if constexpr (PAIR) {
+    if (share) {
+      const int64_t slot = (int64_t)pair_idx * p.hkv + w.g;
+      float* part = f.pair_part + slot * f.part_floats * 256;
+      int32_t* flag = f.pair_count + slot;
+      auto put = [](float* q, float v) {
+        __hip_atomic_store(q, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      };
+      auto get = [](const float* q) {
+        return __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      };
+      if (pair_role == 1) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int qb = 0; qb < MB; ++qb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) put(part + ((db * MB + qb) * 4 + e) * 256 + tid, oacc[db][qb][e]);
+#pragma unroll
+        for (int qb = 0; qb < MB; ++qb) {
+          put(part + (NDB * MB * 4 + qb) * 256 + tid, mrow[qb]);
+          put(part + (NDB * MB * 4 + MB + qb) * 256 + tid, lrow[qb]);
+        }
+        // this thread's stores are complete (the clobber keeps them above)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();  // and so are every other thread's
+        if (tid == 0) __hip_atomic_store(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        continue;  // on to the short request
+      }
+      // The page table of the last window is no longer read: its first entry
+      // carries whether the partial state arrived within the bounded wait.
+      if (tid == 0) {
+        int got = 0;
+        for (int it = 0; it < kPairSpin; ++it) {
+          if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+            got = 1;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+        if (!got)
+          record_fault(&p.hdr->error_bits, &p.hdr->fault_count, &p.hdr->first_value,
+                       kErrPairWait, (int32_t)slot);
+        else  // ready for the next launch
+          __hip_atomic_store(flag, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lds_pages[0] = got;
+      }
+      __syncthreads();  // the slot loads below are issued after the flag was seen
+      if (lds_pages[0] != 0) {
+#pragma unroll
+        for (int qb = 0; qb < MB; ++qb) {
+          const float m2 = get(part + (NDB * MB * 4 + qb) * 256 + tid);
+          const float l2 = get(part + (NDB * MB * 4 + MB + qb) * 256 + tid);
+          const float m_new = fmaxf(mrow[qb], m2);
+          const float m_use = m_new == -INFINITY ? 0.f : m_new;
+          const float a1 = fast_exp2((mrow[qb] - m_use) * c2);
+          const float a2 = fast_exp2((m2 - m_use) * c2);
+          mrow[qb] = m_new;
+          lrow[qb] = lrow[qb] * a1 + l2 * a2;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              oacc[db][qb][e] = oacc[db][qb][e] * a1 + get(part + ((db * MB + qb) * 4 + e) * 256 + tid) * a2;
+        }
+      }
+    }
+  }
+
   // ---- MODE 1: each wave attends its own beams' tails (slot-table rows
   // u = (beam - kb_first) * n_tail + t) in 16-key sub-tiles, double-buffered
   // in its quarter of the now idle tile ring, with no workgroup barrier. A
@@ -795,9 +918,8 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
   }
 
   // ---- fused step: write this tile's beams' current tokens into the pool
-  if constexpr (FUSED) {
+  if (FUSED && n_tail > 0) {
     const int jcur = ri.seq - 1;
-    if (n_tail <= 0) return;
     // A beam's token is written by the tile holding its first row. It is
     // written last: nothing in this launch reads it back from the pool (the
     // tails take the current token from the new-token rows), and here its
@@ -806,7 +928,9 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
     const int kw_lo = (w.qt * rt + p.group - 1) / p.group;
     const int kw_hi = min(p.W, ((w.qt + 1) * rt + p.group - 1) / p.group);
     const int n_tw = (kw_hi - kw_lo) * CPR;
-    constexpr int TW = 16;
+    // tasks per thread: all of a wide beam's tokens in one round; fewer in the
+    // paired kernel, where the next segment's state is live across the loads
+    constexpr int TW = PAIR ? 4 : 16;
     for (int base = 0; base < n_tw; base += 256 * TW) {
       int32_t page[TW];
       u32x4 kd[TW], vd[TW];
@@ -839,6 +963,8 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
       }
     }
   }
+  }  // segments
+
 }
 
 // f32: one wave per query row, lanes split head_dim, keys in chunks of 8.
@@ -950,22 +1076,32 @@ int prefix_rows_per_tile(int dtype, int head_dim, int rows_per_req) {
 }
 
 // Tile size and pipeline depth per head_dim: 64 KB of K/V stages per workgroup.
-template <typename T, int MODE>
+template <typename T, int MODE, bool PAIR>
 static void launch_mfma(const PrefixParams& p, const FusedParams& f, int head_dim, int mb,
                         unsigned blocks, hipStream_t s) {
 #define BSP_PFX(DD, MBB, KTT, NS) \
-  prefix_mfma_kernel<T, DD, MBB, KTT, NS, MODE><<<blocks, 256, 0, s>>>(p, f)
-  if (head_dim == 64) {
-    if (mb == 1) BSP_PFX(64, 1, 64, 4);
-    else if (mb == 2) BSP_PFX(64, 2, 64, 4);
-    else BSP_PFX(64, 3, 64, 4);
-  } else if (head_dim == 128) {
-    if (mb == 1) BSP_PFX(128, 1, 32, 4);
-    else if (mb == 2) BSP_PFX(128, 2, 32, 4);
-    else BSP_PFX(128, 3, 32, 4);
+  prefix_mfma_kernel<T, DD, MBB, KTT, NS, MODE, PAIR><<<blocks, 256, 0, s>>>(p, f)
+  if constexpr (PAIR) {  // MB <= 2, head_dim <= 128
+    if (head_dim == 64) {
+      if (mb == 1) BSP_PFX(64, 1, 64, 4);
+      else BSP_PFX(64, 2, 64, 4);
+    } else {
+      if (mb == 1) BSP_PFX(128, 1, 32, 4);
+      else BSP_PFX(128, 2, 32, 4);
+    }
   } else {
-    if (mb == 1) BSP_PFX(256, 1, 32, 2);
-    else BSP_PFX(256, 2, 32, 4);
+    if (head_dim == 64) {
+      if (mb == 1) BSP_PFX(64, 1, 64, 4);
+      else if (mb == 2) BSP_PFX(64, 2, 64, 4);
+      else BSP_PFX(64, 3, 64, 4);
+    } else if (head_dim == 128) {
+      if (mb == 1) BSP_PFX(128, 1, 32, 4);
+      else if (mb == 2) BSP_PFX(128, 2, 32, 4);
+      else BSP_PFX(128, 3, 32, 4);
+    } else {
+      if (mb == 1) BSP_PFX(256, 1, 32, 2);
+      else BSP_PFX(256, 2, 32, 4);
+    }
   }
 #undef BSP_PFX
 }
@@ -981,8 +1117,8 @@ hipError_t launch_prefix(const PrefixParams& p, int dtype, int head_dim, int row
   } else {
     const int mb = pick_mb(head_dim, rows_per_req);
     const FusedParams none{};
-    if (dtype == BSP_F16) launch_mfma<_Float16, 0>(p, none, head_dim, mb, blocks, s);
-    else launch_mfma<__bf16, 0>(p, none, head_dim, mb, blocks, s);
+    if (dtype == BSP_F16) launch_mfma<_Float16, 0, false>(p, none, head_dim, mb, blocks, s);
+    else launch_mfma<__bf16, 0, false>(p, none, head_dim, mb, blocks, s);
   }
   return hipGetLastError();
 }
@@ -995,11 +1131,19 @@ hipError_t launch_decode_step(const PrefixParams& p, const FusedParams& f, int d
   // beams with a row in one query tile, at most; their tail slots must fit the LDS table
   const int nbt_max = min(p.W, (64 * mb - 1) / p.group + 2);
   if ((int64_t)nbt_max * tail_pad <= kTailSlots) {
-    if (dtype == BSP_F16) launch_mfma<_Float16, 1>(p, f, head_dim, mb, blocks, s);
-    else launch_mfma<__bf16, 1>(p, f, head_dim, mb, blocks, s);
+    // balanced pairs when the plan built them and the tile shape allows them
+    if (f.pairs != nullptr && f.n_pairs > 0 && mb <= kPairMaxMB && head_dim <= 128 &&
+        p.n_qtiles == 1 && f.part_floats >= pair_part_floats(head_dim, mb)) {
+      const unsigned pblocks = (unsigned)(f.n_pairs * p.hkv * 2);
+      if (dtype == BSP_F16) launch_mfma<_Float16, 1, true>(p, f, head_dim, mb, pblocks, s);
+      else launch_mfma<__bf16, 1, true>(p, f, head_dim, mb, pblocks, s);
+    } else {
+      if (dtype == BSP_F16) launch_mfma<_Float16, 1, false>(p, f, head_dim, mb, blocks, s);
+      else launch_mfma<__bf16, 1, false>(p, f, head_dim, mb, blocks, s);
+    }
   } else {
-    if (dtype == BSP_F16) launch_mfma<_Float16, 2>(p, f, head_dim, mb, blocks, s);
-    else launch_mfma<__bf16, 2>(p, f, head_dim, mb, blocks, s);
+    if (dtype == BSP_F16) launch_mfma<_Float16, 2, false>(p, f, head_dim, mb, blocks, s);
+    else launch_mfma<__bf16, 2, false>(p, f, head_dim, mb, blocks, s);
   }
   return hipGetLastError();
 }

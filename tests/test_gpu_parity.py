@@ -446,3 +446,89 @@ def test_full_size_wide_beam_fused_sampled():
         fo, fl = oracle.beam_attention_one(ref, b, k)
         assert np.abs(out[b, k] - fo[0]).max() <= to
         assert np.abs(lse[b, k] - fl[0]).max() <= tl
+
+
+# ------------------------------------ balanced pairs in the fused step
+
+PAIR_CASES = {
+    "odd_spread_bf16": dict(cfg="qwen3_0p6b", batch=7, prefix_range=(0, 1200)),
+    "two_bf16": dict(cfg="qwen3_0p6b", batch=2, prefix_range=(32, 1500)),
+    "equal_bf16": dict(cfg="qwen3_0p6b", batch=4, prefix_range=(512, 512)),
+    "no_tails_bf16": dict(cfg="qwen3_0p6b", batch=4, prefix_range=(0, 900), tail_range=(0, 0)),
+    "mb2_d128_f16": dict(cfg="qwen3_4b", batch=5, prefix_range=(64, 3000)),
+    "mb2_d64_f16": dict(cfg="qwen3_4b", batch=4, head_dim=64, prefix_range=(100, 2400)),
+    "nsample_bf16": dict(cfg="nsample", batch=5, prefix_range=(30, 1000)),
+}
+
+
+@pytest.mark.parametrize("case", list(PAIR_CASES))
+def test_decode_step_balanced_pairs(case, monkeypatch):
+    """The step with balanced pairs (the long request of a pair split between two
+    workgroups, its partial states merged) matches the oracle on two launches
+    in a row (each launch leaves the pair flags cleared for the next), and so
+    does the same step with pairing switched off."""
+    kw = dict(PAIR_CASES[case])
+    cfg = kw.pop("cfg")
+    monkeypatch.setenv("BSP_PAIRS", "1")
+    inp = synth.make_beam_step(cfg, 5, **kw)
+    P = inp.prefix_len
+    say(f"pairs {case} P={P.tolist()} T={inp.tail_len.tolist()}")
+    s = S.upload_beam_step(inp, DEV)
+    S.plan_beam_step(s)
+    pairs = B.bsp_debug_plan_pairs(s.plan)
+    assert len(pairs) == (inp.batch + 1) // 2
+    lo, hi = kw.get("prefix_range", (0, 0))
+    if hi - lo >= 500:
+        assert any(split < P[a] for a, b, split in pairs), pairs
+    ref = _applied(synth.make_beam_step(cfg, 5, **kw))
+    fo, fl = oracle.beam_decode_attention(ref)
+    for rep in range(2):
+        S.run_decode_step(s)
+        B.bsp_check(s.plan)
+        torch.cuda.synchronize()
+        err = assert_close(s.out, s.lse_out, fo, fl, inp.dtype, f"{case} launch {rep}")
+        say(f"  launch {rep}: max |dO| = {err:.3g}")
+    assert torch.equal(s.k_pool.cpu(), S.to_device(ref.k_pool, inp.dtype, "cpu")), case
+    assert torch.equal(s.v_pool.cpu(), S.to_device(ref.v_pool, inp.dtype, "cpu")), case
+
+    monkeypatch.setenv("BSP_PAIRS", "0")
+    s2 = S.upload_beam_step(synth.make_beam_step(cfg, 5, **kw), DEV)
+    S.plan_beam_step(s2)
+    assert len(B.bsp_debug_plan_pairs(s2.plan)) == 0
+    S.run_decode_step(s2)
+    B.bsp_check(s2.plan)
+    torch.cuda.synchronize()
+    assert_close(s2.out, s2.lse_out, fo, fl, inp.dtype, f"{case} unpaired")
+
+
+@pytest.mark.parametrize("cfg,pairs_env", [("qwen3_0p6b", None), ("qwen3_0p6b", "1"),
+                                           ("qwen3_4b", None), ("qwen3_4b", "1")])
+def test_full_size_fused_sampled(cfg, pairs_env, monkeypatch):
+    """The bench's full shapes (64 requests x 30 beams) through the fused step,
+    as planned (no pairs for these prompt spreads) and with balanced pairs
+    forced; sampled beams against the oracle."""
+    if pairs_env is not None:
+        monkeypatch.setenv("BSP_PAIRS", pairs_env)
+    inp = synth.make_beam_step(cfg, 0, garbage="unit")
+    s = S.upload_beam_step(inp, DEV)
+    S.plan_beam_step(s)
+    pairs = B.bsp_debug_plan_pairs(s.plan)
+    say(f"full-size fused {cfg}: pairs={len(pairs)}")
+    assert len(pairs) == (32 if pairs_env == "1" else 0)
+    S.run_decode_step(s)
+    B.bsp_check(s.plan)
+    torch.cuda.synchronize()
+    ref = _applied(inp)
+    rng = np.random.default_rng(3)
+    W, Hq, D = inp.beam, inp.num_q_heads, inp.head_dim
+    # the longest and the shortest prompt (the first pair), plus random ones
+    a, b = int(np.argmax(inp.prefix_len)), int(np.argmin(inp.prefix_len))
+    picks = [(a, 0), (a, W - 1), (b, 1)]
+    picks += [(int(x), int(k)) for x, k in zip(rng.integers(0, inp.batch, 10), rng.integers(0, W, 10))]
+    out = s.out.float().cpu().numpy().reshape(inp.batch, W, Hq, D)
+    lse = s.lse_out.cpu().numpy().reshape(inp.batch, W, Hq)
+    to, tl = TOL[inp.dtype]
+    for x, k in picks:
+        fo, fl = oracle.beam_attention_one(ref, x, k)
+        assert np.abs(out[x, k] - fo[0]).max() <= to, (x, k)
+        assert np.abs(lse[x, k] - fl[0]).max() <= tl, (x, k)

@@ -214,3 +214,85 @@ def test_check_mode_requires_shared_prompt_blocks(monkeypatch):
     name, msg = _status(lambda: B.bsp_plan(plan, inp.batch, inp.beam, 1, inp.prefix_len,
                                            inp.seq_len, bt))
     assert name == "BSP_ERR_ARG" and "share prompt block" in msg
+
+
+# ------------------------------------------------ balanced pairs (host plan)
+
+def _pair_plan(B_, W, G, D, dtype, prefix, key_bucket=0):
+    ps = 32
+    nb = -(-(max(prefix) + 8) // ps)
+    desc = B.make_desc(2 * G, 2, D, ps, 4096, dtype, key_bucket=key_bucket,
+                       max_cache_rows=nb * ps if key_bucket else 0)
+    plan = B.Plan(desc, B_, W, nb, nb * ps, 1, host_only=True)
+    P = np.asarray(prefix, np.int32)
+    bt = np.arange(B_ * W * nb, dtype=np.int32).reshape(B_, W, nb) % 4096
+    bt[:, :, :] = bt[:, :1, :]  # every beam shares its request's blocks
+    S = P if key_bucket else P + 3
+    B.bsp_plan(plan, B_, W, 1, P, S.astype(np.int32), bt)
+    return B.bsp_debug_plan_pairs(plan)
+
+
+def test_pairs_cover_every_request_once_and_balance_keys(monkeypatch):
+    """Longest prompt with shortest: each request in exactly one pair, the long
+    one split at a multiple of 64 so that both workgroups stream about as many
+    keys (X: a's first keys; Y: a's last keys and all of b)."""
+    monkeypatch.setenv("BSP_PAIRS", "1")
+    rng = np.random.default_rng(7)
+    for trial in range(300):
+        Bn = int(rng.integers(2, 12))
+        P = rng.integers(0, 2500, size=Bn)
+        pairs = _pair_plan(Bn, 30, 2, 128, "bf16", P)
+        assert len(pairs) == (Bn + 1) // 2
+        seen = [int(r) for r in pairs[:, 0]] + [int(r) for r in pairs[:, 1] if r >= 0]
+        assert sorted(seen) == list(range(Bn))
+        assert (pairs[:, 1] < 0).sum() == Bn % 2
+        a_len = P[pairs[:, 0]]
+        assert np.all(np.diff(a_len) <= 0)  # pairs in order of the long prompt
+        for a, b, split in pairs:
+            Pa, Pb = int(P[a]), int(P[b]) if b >= 0 else 0
+            assert b < 0 or Pa >= Pb
+            if b < 0:
+                assert split == Pa
+            elif split < Pa:
+                assert split % 64 == 0 and split >= 64
+                assert abs(split - (Pa - split + Pb)) <= 64
+            else:
+                assert split == Pa and Pa - Pb <= 128
+
+
+@pytest.mark.parametrize("what", ["f32", "d256", "rows", "cached", "one", "env"])
+def test_pairs_only_where_the_step_supports_them(what, monkeypatch):
+    P = [2000, 100, 900, 1500]
+    kw = dict(B_=4, W=30, G=2, D=128, dtype="bf16", prefix=P)
+    assert len(_pair_plan(**kw)) == 2
+    if what == "f32":
+        kw["dtype"] = "f32"
+    elif what == "d256":
+        kw["D"] = 256
+    elif what == "rows":
+        kw["W"] = 65  # 130 query rows per request and KV head
+    elif what == "cached":
+        kw.update(key_bucket=64, W=1)
+    elif what == "one":
+        kw.update(B_=1, prefix=[2000])
+    else:
+        monkeypatch.setenv("BSP_PAIRS", "0")
+    assert len(_pair_plan(**kw)) == 0
+
+
+@pytest.mark.parametrize("prefix,paired", [([500, 450, 600, 420], False),
+                                           ([1600, 2400, 2000, 1900], False),
+                                           ([200, 800, 500, 700], True),
+                                           ([300, 899, 600, 500, 700], False),
+                                           ([300, 900, 600, 500, 700], True),
+                                           ([150, 800, 500, 700], True),
+                                           ([0, 100, 50], True),
+                                           ([0, 0, 0], False)])
+def test_pairs_chosen_for_wide_prompt_spread(prefix, paired, monkeypatch):
+    """Without BSP_PAIRS the planner pairs only when the longest prompt is at
+    least three times the shortest (and some prompt is non-empty)."""
+    monkeypatch.delenv("BSP_PAIRS", raising=False)
+    pairs = _pair_plan(len(prefix), 30, 2, 128, "bf16", prefix)
+    assert (len(pairs) > 0) == paired
+    monkeypatch.setenv("BSP_PAIRS", "1")
+    assert len(_pair_plan(len(prefix), 30, 2, 128, "bf16", prefix)) == (len(prefix) + 1) // 2
