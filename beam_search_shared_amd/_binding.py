@@ -80,6 +80,8 @@ _SIGS = {
     "bsp_merge": (_I32, [_I32, _I32, _I32, _I32, _P, _P, _I64, _I64, _P, _I32, _P, _P]),
     "bsp_naive_beam_attn": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "bsp_decode_step": (_I32, [_P, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P]),
+    "bsp_plan_prefill": (_I32, [_P, _I32, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "bsp_prefill_attn": (_I32, [_P, _P, _P, _P, _P, _P, _P]),
     "bsp_check": (_I32, [_P, _P]),
     "bsp_debug_plan_tables": (_I32, [_P, _P, _P, _P, _P, _P]),
     "bsp_debug_plan_pairs": (_I32, [_P, _P, _P]),
@@ -250,6 +252,23 @@ def bsp_decode_step(plan: Plan, q, k_new, v_new, new_row_stride: int, k_pool, v_
                                           new_row_stride, _ptr(k_pool), _ptr(v_pool),
                                           _ptr(block_tables), _ptr(cache_indirection),
                                           _ptr(o_out), _ptr(lse_out), _stream(stream)))
+
+
+def bsp_plan_prefill(plan: Plan, C: int, q_len, cached_len, block_tables, workspace=None,
+                     stream=None) -> None:
+    ql = _host_i32(q_len)
+    cl = _host_i32(cached_len)
+    bt = _host_i32(block_tables)
+    plan._keep = [ql, cl, bt]
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = None if plan.host_only else _stream(stream)
+    _check(load_library().bsp_plan_prefill(plan.handle, C, _ptr(ql), _ptr(cl), _ptr(bt),
+                                           _ptr(workspace), nbytes, st))
+
+
+def bsp_prefill_attn(plan: Plan, q, k_pool, v_pool, o_out, lse_out=None, stream=None) -> None:
+    _check(load_library().bsp_prefill_attn(plan.handle, _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                           _ptr(o_out), _ptr(lse_out), _stream(stream)))
 
 
 def bsp_check(plan: Plan, stream=None) -> None:

@@ -14,6 +14,7 @@
 // cache (Phi-4 cached-prefix PR, TensorRT-Model-Connect #2202: Exit Criteria,
 // Implementation).
 #include <algorithm>
+#include <array>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -84,6 +85,9 @@ struct bsp_plan_s {
   int pair_mode = 2;  // 0 never, 1 always, 2 when the prompt lengths are spread wide
   int32_t max_pairs = 0, pair_part_floats = 0;
   size_t pairs_off = 0, pair_count_off = 0, pair_part_off = 0;
+  // prefill work list (bsp_plan_prefill): (request, query tile) int32 pairs
+  int32_t max_items = 0;
+  size_t items_off = 0;
 
   // staging ring (pinned host memory, or malloc for host-only plans)
   void* staging[2] = {nullptr, nullptr};
@@ -99,6 +103,9 @@ struct bsp_plan_s {
   std::vector<ReqInfo> h_req;
   std::vector<bsp::PairInfo> h_pairs;
   std::vector<int32_t> h_pages;
+  // prefill plans (bsp_plan_prefill): ragged query rows, work list
+  bool prefill = false;
+  int32_t rows_total = 0, n_items = 0, prefill_mb = 1;
 };
 
 namespace {
@@ -125,6 +132,15 @@ bsp_status_t check_device_ready(const bsp_plan_s* pl) {
   if (!pl->planned)
     return fail(BSP_ERR_STALE_PLAN, "plan has no valid step: call bsp_plan first");
   if (pl->host_only) return fail(BSP_ERR_ARG, "host-only plan cannot launch kernels");
+  return BSP_OK;
+}
+
+// Entry points of the beam step need a bsp_plan step; bsp_prefill_attn needs a
+// bsp_plan_prefill step.
+bsp_status_t check_beam_ready(const bsp_plan_s* pl) {
+  const bsp_status_t st = check_device_ready(pl);
+  if (st != BSP_OK) return st;
+  if (pl->prefill) return fail(BSP_ERR_ARG, "plan holds a prefill step (bsp_plan_prefill)");
   return BSP_OK;
 }
 
@@ -222,6 +238,14 @@ bsp_status_t bsp_plan_create(const bsp_layer_desc_t* desc, int32_t max_requests,
                                                       pl->pair_part_floats,
                               256);
     }
+  }
+  // Prefill work list: at most one item per 64 query rows of each request.
+  {
+    const int G = d.num_q_heads / d.num_kv_heads;
+    pl->max_items = (int32_t)std::min<int64_t>(
+        INT32_MAX / 2, (int64_t)max_requests * ceil_div((int64_t)max_q_len * G, 64));
+    pl->items_off = pl->ws_bytes;
+    pl->ws_bytes = align_up(pl->items_off + 2 * sizeof(int32_t) * (size_t)pl->max_items, 256);
   }
   for (int i = 0; i < 2; ++i) {
     if (pl->host_only) {
@@ -449,6 +473,9 @@ bsp_status_t bsp_plan(bsp_plan_t pl, int32_t B, int32_t W, int32_t q_len,
   pl->rows_per_req = W * q_len * (d.num_q_heads / d.num_kv_heads);
   pl->n_pairs = n_pairs;
   pl->h_pairs = std::move(pairs);
+  pl->prefill = false;
+  pl->rows_total = B * W * q_len;
+  pl->n_items = 0;
   pl->ws_d = workspace_d;
   pl->h_req = std::move(req);
   pl->h_pages = std::move(pages);
@@ -458,6 +485,173 @@ bsp_status_t bsp_plan(bsp_plan_t pl, int32_t B, int32_t W, int32_t q_len,
 
 int32_t bsp_plan_num_splits(bsp_plan_t pl) { return pl && pl->planned ? pl->n_split : -1; }
 int32_t bsp_plan_tail_len(bsp_plan_t pl) { return pl && pl->planned ? pl->tail_pad : -1; }
+
+bsp_status_t bsp_plan_prefill(bsp_plan_t pl, int32_t C, const int32_t* q_len_h,
+                              const int32_t* cached_len_h, const int32_t* block_tables_h,
+                              void* workspace_d, size_t workspace_bytes, hipStream_t stream) {
+  if (pl == nullptr) return fail(BSP_ERR_ARG, "null plan");
+  pl->planned = false;
+  const bsp_layer_desc_t& d = pl->desc;
+  if (d.key_bucket > 0) return fail(BSP_ERR_ARG, "prefill steps need a plan without key_bucket");
+  if (C < 1 || C > pl->max_requests)
+    return fail(BSP_ERR_ARG, "C = %d outside [1, %d]", C, pl->max_requests);
+  if (q_len_h == nullptr || cached_len_h == nullptr || block_tables_h == nullptr)
+    return fail(BSP_ERR_ARG, "null host table");
+  if (pl->host_only) {
+    if (workspace_d != nullptr) return fail(BSP_ERR_ARG, "host-only plan takes no workspace");
+  } else {
+    if (workspace_d == nullptr) return fail(BSP_ERR_WORKSPACE, "null workspace");
+    if (workspace_bytes < pl->ws_bytes)
+      return fail(BSP_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
+                  pl->ws_bytes);
+    if ((reinterpret_cast<uintptr_t>(workspace_d) & 255u) != 0)
+      return fail(BSP_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
+  const int ps = d.page_size;
+  const int MBLK = pl->max_blocks;
+  const int G = d.num_q_heads / d.num_kv_heads;
+  // Query rows per work item: the tallest tile (most reuse of each key tile)
+  // that still gives every CU two workgroups, else the shortest.
+  int mb = bsp::prefill_max_mb(d.head_dim);
+  for (; mb > 1; --mb) {
+    int64_t n = 0;
+    for (int b = 0; b < C; ++b) n += ceil_div((int64_t)std::max(q_len_h[b], 0) * G, 64 * mb);
+    if (n * d.num_kv_heads >= bsp::kPrefillMinBlocks) break;
+  }
+  const int rpt = 64 * mb;
+  std::vector<ReqInfo> req(C);
+  std::vector<int32_t> pages;
+  std::vector<std::array<int32_t, 3>> items;  // (keys, request, tile)
+  int64_t rows = 0;
+  for (int b = 0; b < C; ++b) {
+    const int32_t Sq = q_len_h[b], L = cached_len_h[b];
+    if (Sq < 1 || Sq > pl->max_q_len)
+      return fail(BSP_ERR_ARG, "request %d: chunk of %d rows outside [1, %d]", b, Sq,
+                  pl->max_q_len);
+    if (L < 0 || (int64_t)L + Sq > pl->max_seq_len)
+      return fail(BSP_ERR_ARG, "request %d: need 0 <= cached (%d) and cached + chunk (%lld) <= %d",
+                  b, L, (long long)L + Sq, pl->max_seq_len);
+    ReqInfo& r = req[b];
+    std::memset(&r, 0, sizeof(r));
+    r.n_keys = r.valid = r.seq = L + Sq;
+    r.prefix = L;
+    r.tail = Sq;
+    r.n_split = 1;
+    r.q_off = (int32_t)rows;
+    r.page_off = (int32_t)pages.size();
+    const int64_t nblk = ceil_div(r.n_keys, ps);
+    if (nblk > MBLK)
+      return fail(BSP_ERR_ARG, "request %d: %lld blocks > max_blocks %d", b, (long long)nblk, MBLK);
+    for (int64_t i = 0; i < nblk; ++i) {
+      const int32_t pg = block_tables_h[(int64_t)b * MBLK + i];
+      if (pg < 0 || pg >= d.num_pages)
+        return fail(BSP_ERR_PAGE_INDEX, "request %d block %lld: page id %d outside [0, %d)", b,
+                    (long long)i, pg, d.num_pages);
+      pages.push_back(pg);
+    }
+    const int32_t nqt = (int32_t)ceil_div((int64_t)Sq * G, rpt);
+    for (int32_t qt = 0; qt < nqt; ++qt) {
+      const int64_t last = std::min<int64_t>((int64_t)(qt + 1) * rpt, (int64_t)Sq * G) - 1;
+      items.push_back({(int32_t)(L + last / G + 1), b, qt});
+    }
+    rows += Sq;
+  }
+  if (rows > INT32_MAX / 2) return fail(BSP_ERR_ARG, "too many query rows (%lld)", (long long)rows);
+  if ((int64_t)items.size() > pl->max_items)
+    return fail(BSP_ERR_ARG, "%zu work items > %d", items.size(), pl->max_items);
+  // Longest key range first: the items that stream the most keys start in the
+  // first round of workgroups, the short ones fill in behind them.
+  std::stable_sort(items.begin(), items.end(),
+                   [](const std::array<int32_t, 3>& x, const std::array<int32_t, 3>& y) {
+                     return x[0] > y[0];
+                   });
+
+  const int slot = pl->ring;
+  if (pl->staged_pending[slot]) {
+    const hipError_t e = hipEventSynchronize(pl->staged[slot]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize (plan staging)");
+    pl->staged_pending[slot] = false;
+  }
+  char* st = static_cast<char*>(pl->staging[slot]);
+  std::memset(st, 0, bsp::kHeaderBytes);
+  std::memcpy(st + req_offset(), req.data(), sizeof(ReqInfo) * C);
+  if (!pages.empty())
+    std::memcpy(st + pages_offset(C), pages.data(), sizeof(int32_t) * pages.size());
+  int32_t* it = reinterpret_cast<int32_t*>(st + pl->items_off);
+  for (size_t i = 0; i < items.size(); ++i) {
+    it[2 * i] = items[i][1];
+    it[2 * i + 1] = items[i][2];
+  }
+  if (!pl->host_only) {
+    const size_t begin = workspace_d == pl->zeroed_ws ? req_offset() : 0;
+    const size_t end = pl->items_off + 2 * sizeof(int32_t) * items.size();
+    hipError_t e = hipMemcpyAsync(static_cast<char*>(workspace_d) + begin, st + begin,
+                                  end - begin, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (prefill tables)");
+    e = hipEventRecord(pl->staged[slot], stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord (plan staging)");
+    pl->staged_pending[slot] = true;
+    pl->ring = 1 - slot;
+    pl->zeroed_ws = workspace_d;
+  }
+  pl->B = C;
+  pl->W = 1;
+  pl->q_len = 0;
+  pl->tail_pad = 0;
+  pl->n_split = 1;
+  pl->rows_per_req = 0;
+  pl->n_pairs = 0;
+  pl->h_pairs.clear();
+  pl->prefill = true;
+  pl->rows_total = (int32_t)rows;
+  pl->n_items = (int32_t)items.size();
+  pl->prefill_mb = mb;
+  pl->ws_d = workspace_d;
+  pl->h_req = std::move(req);
+  pl->h_pages = std::move(pages);
+  pl->planned = true;
+  return ok();
+}
+
+bsp_status_t bsp_prefill_attn(bsp_plan_t pl, const void* q, const void* k_pool, const void* v_pool,
+                              void* o_out, float* lse_out, hipStream_t stream) {
+  bsp_status_t st = check_device_ready(pl);
+  if (st != BSP_OK) return st;
+  if (!pl->prefill) return fail(BSP_ERR_STALE_PLAN, "plan holds no prefill step: call bsp_plan_prefill");
+  const bsp_layer_desc_t& d = pl->desc;
+  if (d.dtype == BSP_F32) return fail(BSP_ERR_UNSUPPORTED, "bsp_prefill_attn is bf16/f16 only");
+  if (!q || !k_pool || !v_pool || !o_out) return fail(BSP_ERR_ARG, "null pointer");
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o_out))
+    return fail(BSP_ERR_ARG, "q, the pools and o_out must be 16-byte aligned");
+  bsp::PrefixParams p{};
+  p.q = q;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.req = dev_req(pl);
+  p.pages = dev_pages(pl);
+  p.hdr = dev_header(pl);
+  p.items = reinterpret_cast<const int32_t*>(static_cast<char*>(pl->ws_d) + pl->items_off);
+  p.B = pl->B;
+  p.W = 1;
+  p.q_len = 1;
+  p.hq = d.num_q_heads;
+  p.hkv = d.num_kv_heads;
+  p.group = d.num_q_heads / d.num_kv_heads;
+  p.page_shift = pl->page_shift;
+  p.num_pages = d.num_pages;
+  p.n_split = 1;
+  p.split_keys = 0;
+  p.n_qtiles = 1;
+  p.causal = 1;
+  p.rows_total = pl->rows_total;
+  p.scale = d.sm_scale;
+  p.scale_log2e = d.sm_scale * 1.4426950408889634f;
+  bsp::FusedParams f{};
+  f.o_out = o_out;
+  f.lse_out = lse_out;
+  return after_launch(pl, bsp::launch_prefill(p, f, d.dtype, d.head_dim, pl->prefill_mb, pl->n_items, stream),
+                      "prefill launch", stream);
+}
 
 bsp_status_t bsp_write_kv(bsp_plan_t pl, const void* k_new, const void* v_new,
                           int64_t src_row_stride, const int32_t* slots_d, int32_t n, void* k_pool,
@@ -492,13 +686,13 @@ bsp_status_t bsp_write_kv(bsp_plan_t pl, const void* k_new, const void* v_new,
 
 bsp_status_t bsp_prefix_attn(bsp_plan_t pl, const void* q, const void* k_pool, const void* v_pool,
                              float* o_part, float* lse_part, hipStream_t stream) {
-  bsp_status_t st = check_device_ready(pl);
+  bsp_status_t st = check_beam_ready(pl);
   if (st != BSP_OK) return st;
   if (!q || !k_pool || !v_pool || !o_part || !lse_part) return fail(BSP_ERR_ARG, "null pointer");
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o_part))
     return fail(BSP_ERR_ARG, "q, the pools and o_part must be 16-byte aligned");
   const bsp_layer_desc_t& d = pl->desc;
-  bsp::PrefixParams p;
+  bsp::PrefixParams p{};
   p.q = q;
   p.k_pool = k_pool;
   p.v_pool = v_pool;
@@ -531,7 +725,7 @@ bsp_status_t bsp_decode_step(bsp_plan_t pl, const void* q, const void* k_new, co
                              int64_t new_row_stride, void* k_pool, void* v_pool,
                              const int32_t* block_tables_d, const int32_t* cache_indirection_d,
                              void* o_out, float* lse_out, hipStream_t stream) {
-  bsp_status_t st = check_device_ready(pl);
+  bsp_status_t st = check_beam_ready(pl);
   if (st != BSP_OK) return st;
   const bsp_layer_desc_t& d = pl->desc;
   if (d.dtype == BSP_F32)
@@ -549,7 +743,7 @@ bsp_status_t bsp_decode_step(bsp_plan_t pl, const void* q, const void* k_new, co
   if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) ||
       !aligned16(v_pool) || (reinterpret_cast<uintptr_t>(o_out) & 7u) != 0)
     return fail(BSP_ERR_ARG, "q, k_new, v_new and the pools must be 16-byte aligned, o_out 8-byte");
-  bsp::PrefixParams p;
+  bsp::PrefixParams p{};
   std::memset(&p, 0, sizeof(p));
   p.q = q;
   p.k_pool = k_pool;
@@ -632,7 +826,7 @@ static bsp::TailParams tail_params(const bsp_plan_s* pl, const void* q, const vo
 bsp_status_t bsp_tail_attn(bsp_plan_t pl, const void* q, const void* k_pool, const void* v_pool,
                            const int32_t* block_tables_d, const int32_t* cache_indirection_d,
                            float* o_tail, float* lse_tail, hipStream_t stream) {
-  bsp_status_t st = check_device_ready(pl);
+  bsp_status_t st = check_beam_ready(pl);
   if (st != BSP_OK) return st;
   if (pl->q_len != 1) return fail(BSP_ERR_UNSUPPORTED, "tail attention needs q_len == 1");
   if (!q || !k_pool || !v_pool || !block_tables_d || !cache_indirection_d || !o_tail || !lse_tail)
@@ -648,7 +842,7 @@ bsp_status_t bsp_naive_beam_attn(bsp_plan_t pl, const void* q, const void* k_poo
                                  const void* v_pool, const int32_t* block_tables_d,
                                  const int32_t* cache_indirection_d, void* o_out, float* lse_out,
                                  hipStream_t stream) {
-  bsp_status_t st = check_device_ready(pl);
+  bsp_status_t st = check_beam_ready(pl);
   if (st != BSP_OK) return st;
   if (pl->q_len != 1) return fail(BSP_ERR_UNSUPPORTED, "naive attention needs q_len == 1");
   if (pl->desc.key_bucket > 0) return fail(BSP_ERR_UNSUPPORTED, "naive attention is beam mode only");
@@ -747,7 +941,7 @@ bsp_status_t bsp_debug_plan_pairs(bsp_plan_t pl, int32_t* n_pairs_h, int32_t* pa
 bsp_status_t bsp_debug_tail_slots(bsp_plan_t pl, const int32_t* block_tables_d,
                                   const int32_t* cache_indirection_d, int32_t* slots_d,
                                   hipStream_t stream) {
-  bsp_status_t st = check_device_ready(pl);
+  bsp_status_t st = check_beam_ready(pl);
   if (st != BSP_OK) return st;
   if (!block_tables_d || !cache_indirection_d || !slots_d) return fail(BSP_ERR_ARG, "null pointer");
   bsp::TailParams p = tail_params(pl, nullptr, nullptr, nullptr, block_tables_d, cache_indirection_d);

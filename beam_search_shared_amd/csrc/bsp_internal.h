@@ -65,8 +65,11 @@ struct ReqInfo {
   int32_t seq;       // S_b
   int32_t tail;      // S_b - P_b
   int32_t n_split;   // splits holding keys
-  int32_t pad;
+  int32_t q_off;     // prefill plans: first packed query row of this request (else 0)
 };
+// In prefill plans (bsp_plan_prefill) prefix = L_b cached rows before the
+// chunk, tail = the chunk's rows (the query rows), seq = n_keys = valid = L_b +
+// chunk rows: the page table covers the cached rows and the chunk's own rows.
 static_assert(sizeof(ReqInfo) == 32, "ReqInfo size");
 
 // ---------------------------------------------------------------------------
@@ -99,7 +102,8 @@ struct PrefixParams {
   int32_t num_pages;
   int32_t n_split, split_keys, n_qtiles;
   int32_t causal;
-  int32_t rows_total;   // B * W * q_len
+  int32_t rows_total;   // B * W * q_len (prefill: packed rows)
+  const int32_t* items; // prefill: work list, (request, query tile) int32 pairs
   float scale;          // softmax scale
   float scale_log2e;    // scale * log2(e)
 };
@@ -162,6 +166,13 @@ hipError_t launch_decode_step(const PrefixParams& p, const FusedParams& f, int d
 // Rows per workgroup the prefix kernel picks for this shape (so the host can
 // size the grid before launching).
 int prefix_rows_per_tile(int dtype, int head_dim, int rows_per_req);
+// Prefill (bsp_prefill_attn): at most this many 16-row query blocks per wave
+// (64 * mb query rows per work item); the plan takes fewer when the batch is
+// too small to give every CU two workgroups.
+constexpr int prefill_max_mb(int head_dim) { return head_dim == 256 ? 2 : 3; }
+constexpr int kPrefillMinBlocks = 512;
+hipError_t launch_prefill(const PrefixParams& p, const FusedParams& f, int dtype, int head_dim,
+                          int mb, int n_items, hipStream_t s);
 hipError_t launch_tail(const TailParams& p, int dtype, int head_dim, hipStream_t s);
 hipError_t launch_tail_slots(const TailParams& p, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, int out_dtype, hipStream_t s);

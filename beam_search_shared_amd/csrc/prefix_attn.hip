@@ -170,10 +170,16 @@ __device__ __forceinline__ int32_t resolve_fused_slot(const PrefixParams& p, con
 // storage dtype. MODE 1 resolves the tail slots into an LDS table and streams
 // the tail rows through the tile pipeline after the shared keys; MODE 2, for
 // tails too long for that table, gathers them key by key afterwards.
+// MODE 3: bsp_prefill_attn, the context requests of a mixed step: ragged query
+// rows packed per request, each row attending the request's cached rows and,
+// causally, the chunk's rows up to its own; work items (request, query tile)
+// come from the plan's list and key tiles past a tile's last visible key are
+// never loaded; the output is written in the storage dtype.
 template <typename T, int D, int MB, int KT, int NST, int MODE, bool PAIR>
 __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma_kernel(PrefixParams p,
                                                                                           FusedParams f) {
-  constexpr bool FUSED = MODE != 0;
+  constexpr bool FUSED = MODE == 1 || MODE == 2;
+  constexpr bool PREFILL = MODE == 3;
   static_assert(!PAIR || (MODE == 1 && MB <= kPairMaxMB), "pairs run in the fused step, MB <= 2");
   using V8 = typename Mfma<T>::V8;
   constexpr int NDS = D / 32;                       // contraction steps of S^T
@@ -225,6 +231,17 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
         sg_b0 = pr.b; sg_lo0 = 0; sg_hi0 = p.req[pr.b].valid;
         nseg = 1;
       }
+    } else if constexpr (PREFILL) {
+      w.g = bid % p.hkv;
+      const int item = bid / p.hkv;
+      sg_b0 = p.items[2 * item];
+      w.qt = p.items[2 * item + 1];
+      w.split = 0;
+      // keys up to the tile's last row (row r holds chunk position r / group)
+      const ReqInfo rb = p.req[sg_b0];
+      const int last = min((w.qt + 1) * 64 * MB, rb.tail * p.group) - 1;
+      sg_lo0 = 0;
+      sg_hi0 = min(rb.valid, rb.valid - rb.tail + last / p.group + 1);
     } else {
       w.qt = bid % p.n_qtiles;
       bid /= p.n_qtiles;
@@ -256,7 +273,7 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
   const int l4 = lane >> 4;
   const ReqInfo ri = p.req[w.b];
 
-  const int M = p.W * p.q_len * p.group;
+  const int M = PREFILL ? ri.tail * p.group : p.W * p.q_len * p.group;
   const int row0 = w.qt * (64 * MB) + wave * (16 * MB);
   const bool wave_active = row0 < M;
   const int shift = p.page_shift;
@@ -334,14 +351,19 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
     if (r < M) {
       const int hh = r % p.group;
       const int t = r / p.group;
-      const int i = t % p.q_len;
-      const int kbeam = t / p.q_len;
-      const int64_t qrow =
-          (((int64_t)w.b * p.W + kbeam) * p.q_len + i) * p.hq + w.g * p.group + hh;
+      int64_t qrow;
+      if constexpr (PREFILL) {  // packed rows; chunk position t sees keys up to valid - rows + t
+        qrow = ((int64_t)ri.q_off + t) * p.hq + w.g * p.group + hh;
+        climit[qb] = ri.valid - ri.tail + t;
+      } else {
+        const int i = t % p.q_len;
+        const int kbeam = t / p.q_len;
+        qrow = (((int64_t)w.b * p.W + kbeam) * p.q_len + i) * p.hq + w.g * p.group + hh;
+        if (p.causal) climit[qb] = ri.n_keys - p.q_len + i;
+      }
       const T* qp = static_cast<const T*>(p.q) + qrow * D + l4 * 8;
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) qv[qb][ds] = *reinterpret_cast<const V8*>(qp + ds * 32);
-      if (p.causal) climit[qb] = ri.n_keys - p.q_len + i;
     } else {
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) {
@@ -481,6 +503,9 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
   constexpr int AHEAD = ROT ? NST - 2 : NST - 1;  // tiles in flight beyond the one computed
 
   const int n_tail = FUSED ? ri.tail : 0;
+  // prefill: the smallest causal limit among this wave's rows (its first row);
+  // a key tile at or below it needs no mask
+  const int c_first = PREFILL ? ri.valid - ri.tail + row0 / p.group : 0;
   const int win_first = w.k_lo / keys_per_win;
   const int n_win = w.k_hi > w.k_lo ? (w.k_hi - 1) / keys_per_win - win_first + 1 : 0;
 
@@ -566,7 +591,7 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
       f32x4 sacc[NKB][MB];
       s_tile(lds_kv[t % NST][0], sacc);
       if (ROT && t > 0) o_tile(lds_kv[(t - 1) % NST][1], pb);
-      softmax_tile(sacc, (t0 + KT <= w.k_hi) && !p.causal,
+      softmax_tile(sacc, (t0 + KT <= w.k_hi) && (PREFILL ? t0 + KT - 1 <= c_first : !p.causal),
                    [&](int qb, int kk) { return (t0 + kk < w.k_hi) & (t0 + kk <= climit[qb]); }, pb);
       if (!ROT) o_tile(lds_kv[t % NST][1], pb);
     }
@@ -891,12 +916,11 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
     if (!wave_active || r >= M) continue;
     const int hh = r % p.group;
     const int t = r / p.group;
-    const int i = t % p.q_len;
-    const int kbeam = t / p.q_len;
-    const int64_t grow = ((int64_t)w.b * p.W + kbeam) * p.q_len + i;
+    const int64_t grow = PREFILL ? (int64_t)ri.q_off + t
+                                 : ((int64_t)w.b * p.W + t / p.q_len) * p.q_len + t % p.q_len;
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const float lse = lt > 0.f ? mrow[qb] * p.scale + __logf(lt) : -INFINITY;
-    if constexpr (FUSED) {
+    if constexpr (FUSED || PREFILL) {
       const int64_t ohead = grow * p.hq + w.g * p.group + hh;
       T* op = static_cast<T*>(f.o_out) + ohead * D + l4 * 4;
 #pragma unroll
@@ -1120,6 +1144,37 @@ hipError_t launch_prefix(const PrefixParams& p, int dtype, int head_dim, int row
     if (dtype == BSP_F16) launch_mfma<_Float16, 0, false>(p, none, head_dim, mb, blocks, s);
     else launch_mfma<__bf16, 0, false>(p, none, head_dim, mb, blocks, s);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(const PrefixParams& p, const FusedParams& f, int dtype, int head_dim,
+                          int mb, int n_items, hipStream_t s) {
+  const unsigned blocks = (unsigned)(n_items * p.hkv);
+  if (blocks == 0) return hipSuccess;
+#define BSP_PRE(TT, DD, MBB, KTT) \
+  prefix_mfma_kernel<TT, DD, MBB, KTT, 4, 3, false><<<blocks, 256, 0, s>>>(p, f)
+#define BSP_PRE_T(TT)                                      \
+  if (head_dim == 64) {                                    \
+    if (mb == 1) BSP_PRE(TT, 64, 1, 64);                   \
+    else if (mb == 2) BSP_PRE(TT, 64, 2, 64);              \
+    else BSP_PRE(TT, 64, 3, 64);                           \
+  } else if (head_dim == 128) {                            \
+    if (mb == 1) BSP_PRE(TT, 128, 1, 32);                  \
+    else if (mb == 2) BSP_PRE(TT, 128, 2, 32);             \
+    else BSP_PRE(TT, 128, 3, 32);                          \
+  } else {                                                 \
+    if (mb == 1) BSP_PRE(TT, 256, 1, 32);                  \
+    else BSP_PRE(TT, 256, 2, 32);                          \
+  }
+  static_assert(prefill_max_mb(64) == 3 && prefill_max_mb(128) == 3 && prefill_max_mb(256) == 2,
+                "instantiated tiles");
+  if (dtype == BSP_F16) {
+    BSP_PRE_T(_Float16)
+  } else {
+    BSP_PRE_T(__bf16)
+  }
+#undef BSP_PRE_T
+#undef BSP_PRE
   return hipGetLastError();
 }
 

@@ -15,6 +15,14 @@ and a cached-prefix call (beam 1) is
     bsp_prefix_attn  the bound cache rows (valid rows only), split into chunks
     bsp_prefix_attn  this call's rows, causal
     bsp_merge        n-way merge of all the partial states
+
+and a mixed step (context requests beside generation requests) is
+
+    bsp_write_kv     the context chunks' rows -> their requests' pages
+    bsp_prefill_attn causal attention of every context row (ragged, one launch)
+    bsp_decode_step  the generation requests' beam step
+
+with the context part on a second stream when one is given.
 """
 
 from __future__ import annotations
@@ -245,3 +253,88 @@ def run_cached_prefix(c: CachedPrefixDevice, stream=None) -> None:
     rows = c.q_len
     B.bsp_merge(rows, c.num_q_heads, D, ns + 1, c.o_part, c.lse_part, rows * c.num_q_heads * D,
                 rows * c.num_q_heads, c.out, c.dtype, c.lse_out, stream)
+
+
+@dataclass
+class PrefillDevice:
+    """The context requests of a mixed step on the device, with their plan."""
+
+    dtype: str
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    plan: B.Plan
+    q_len: np.ndarray
+    cached_len: np.ndarray
+    block_tables_h: np.ndarray
+    q: torch.Tensor          # dtype [R, Hq, D], packed by request
+    k_pool: torch.Tensor
+    v_pool: torch.Tensor
+    new_k: torch.Tensor      # dtype [R, Hkv, D]
+    new_v: torch.Tensor
+    slots: torch.Tensor      # int32 [R]
+    workspace: torch.Tensor
+    out: torch.Tensor        # dtype [R, Hq, D]
+    lse_out: torch.Tensor    # float [R, Hq]
+
+    @property
+    def rows(self) -> int:
+        return int(self.q_len.sum())
+
+
+def upload_prefill(inp, device="cuda", plan_desc_kw: Optional[dict] = None) -> PrefillDevice:
+    """Copy a ``synth.PrefillInputs`` to the GPU and create its plan."""
+    desc = B.make_desc(inp.num_q_heads, inp.num_kv_heads, inp.head_dim, inp.page_size,
+                       inp.num_pages, inp.dtype, **(plan_desc_kw or {}))
+    plan = B.Plan(desc, max_requests=inp.batch, max_beam=1, max_blocks_per_seq=inp.max_blocks,
+                  max_seq_len=inp.max_seq_len, max_q_len=inp.max_q_len)
+    R, Hq, D = inp.q.shape
+    return PrefillDevice(
+        dtype=inp.dtype, batch=inp.batch, num_q_heads=Hq, num_kv_heads=inp.num_kv_heads,
+        head_dim=D, plan=plan, q_len=inp.q_len.astype(np.int32),
+        cached_len=inp.cached_len.astype(np.int32), block_tables_h=inp.block_tables.copy(),
+        q=to_device(inp.q, inp.dtype, device),
+        k_pool=to_device(inp.k_pool, inp.dtype, device),
+        v_pool=to_device(inp.v_pool, inp.dtype, device),
+        new_k=to_device(inp.new_k, inp.dtype, device),
+        new_v=to_device(inp.new_v, inp.dtype, device),
+        slots=_i32(inp.slots, device),
+        workspace=torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device=device),
+        out=torch.zeros((R, Hq, D), device=device, dtype=TORCH_DTYPE[inp.dtype]),
+        lse_out=torch.zeros((R, Hq), device=device, dtype=torch.float32),
+    )
+
+
+def plan_prefill(c: PrefillDevice, stream=None) -> None:
+    B.bsp_plan_prefill(c.plan, c.batch, c.q_len, c.cached_len, c.block_tables_h, c.workspace,
+                       stream)
+
+
+def run_prefill(c: PrefillDevice, stream=None, write: bool = True) -> None:
+    """The context phase: write the chunks' rows, then causal attention of every row."""
+    if write:
+        B.bsp_write_kv(c.plan, c.new_k, c.new_v, c.num_kv_heads * c.head_dim, c.slots, c.rows,
+                       c.k_pool, c.v_pool, stream)
+    B.bsp_prefill_attn(c.plan, c.q, c.k_pool, c.v_pool, c.out, c.lse_out, stream)
+
+
+def run_mixed_step(ctx: PrefillDevice, gen: BeamStepDevice, stream=None,
+                   ctx_stream=None) -> None:
+    """One mixed step: the context requests' prefill and the generation requests'
+    fused beam step. The two touch disjoint pages; with ``ctx_stream`` the
+    prefill (matrix-core heavy) runs beside the beam step (HBM heavy) and
+    ``stream`` waits for it at the end."""
+    if ctx_stream is None:
+        run_prefill(ctx, stream)
+        run_decode_step(gen, stream)
+        return
+    main = torch.cuda.current_stream() if stream is None else stream
+    ready = torch.cuda.Event()
+    ready.record(main)
+    ctx_stream.wait_event(ready)
+    run_prefill(ctx, ctx_stream)
+    run_decode_step(gen, main)
+    done = torch.cuda.Event()
+    done.record(ctx_stream)
+    main.wait_event(done)

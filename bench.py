@@ -42,7 +42,16 @@ WORKLOADS = {
     "nsample": "n-sample prefix sharing (parallel sampling): 16 Q / 8 KV heads, head_dim 128, bf16, "
                "32-token pages, 64 prompts x 16 samples, prompts U{400..600}, each sample's own "
                "tail U{8..32}",
+    "prefill": "context phase of a mixed step alone: Qwen3-0.6B-like layer (16 Q / 8 KV heads, "
+               "head_dim 128, bf16, 32-token pages shuffled), 8 fresh prompts U{1500..2500} "
+               "as whole-prompt chunks, causal",
+    "mixed": "mixed step: the qwen3_0p6b beam step (64 requests x beam 30, prompts U{400..600}, "
+             "tails U{0..4}) plus 4 newly arrived requests whose prompts U{400..600} run as "
+             "whole-prompt chunks (write + causal prefill) beside it on a second stream",
 }
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+PREFILL_SHAPE = dict(batch=8, chunk_range=(1500, 2500), cached_range=(0, 0))
+MIXED_CTX_SHAPE = dict(batch=4, chunk_range=(400, 600), cached_range=(0, 0))
 
 
 KERNEL_SOURCES = ("beam_search_shared_amd/csrc/prefix_attn.hip",
@@ -110,6 +119,44 @@ def algorithmic_bytes(inp):
     return step, prefix_kernel
 
 
+def prefill_work(inp):
+    """FLOPs of causal attention (2 products of 2 FLOPs per visible key, query
+    head and dimension) and algorithmic bytes (K+V of every request read once
+    per KV head, chunk K+V written, Q read, O written) of one context phase."""
+    e = EBYTES[inp.dtype]
+    Hq, Hkv, D = inp.num_q_heads, inp.num_kv_heads, inp.head_dim
+    keys = 0
+    for b in range(inp.batch):
+        L, n = int(inp.cached_len[b]), int(inp.q_len[b])
+        keys += n * L + n * (n + 1) // 2
+    R = int(inp.q_len.sum())
+    flops = 4 * keys * Hq * D
+    kv_read = int((inp.cached_len + inp.q_len).sum()) * Hkv * D * e * 2
+    nbytes = kv_read + R * Hkv * D * e * 2 + 2 * R * Hq * D * e
+    return flops, nbytes, keys
+
+
+def cpu_baseline_prefill(inp, budget_s: float):
+    """The fp64 oracle on a bounded sample of rows of the same context phase,
+    scaled to the whole phase by visible keys."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    rng = np.random.default_rng(0)
+    _, _, keys_total = prefill_work(inp)
+    done_keys, total, n = 0, 0.0, 0
+    while total < budget_s / 2:
+        b = int(rng.integers(0, inp.batch))
+        i = int(rng.integers(0, int(inp.q_len[b])))
+        t0 = time.perf_counter()
+        oracle.prefill_attention_one(inp, b, i)
+        total += time.perf_counter() - t0
+        done_keys += int(inp.cached_len[b]) + i + 1
+        n += 1
+    threads = max([int(x.get("num_threads", 1)) for x in threadpool_info()] or [1])
+    return total * keys_total / done_keys, threads, n
+
+
 def cpu_baseline(config: str, seed: int, budget_s: float):
     """Time the fp64 oracle, as it stands, on a bounded sample of the same workload.
 
@@ -148,6 +195,156 @@ def cpu_baseline(config: str, seed: int, budget_s: float):
                       f"scaled to whole steps"}
 
 
+def _timed_loop(torch, fn, steps, warmup, warm_seconds, stream, sync):
+    t_end = time.perf_counter() + warm_seconds
+    i = 0
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+    for i in range(warmup):
+        fn(i)
+    sync()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sec = time.perf_counter() - t0
+    sync()
+    return sec, e0.elapsed_time(e1) / steps
+
+
+def _prefill_copies(S, inp, dev, layers):
+    base = S.upload_prefill(inp, dev)
+    copies = [base]
+    for _ in range(layers - 1):
+        c = S.PrefillDevice(**{**base.__dict__})
+        c.k_pool = base.k_pool.clone()
+        c.v_pool = base.v_pool.clone()
+        c.q = base.q.clone()
+        c.out = base.out.clone()
+        copies.append(c)
+    S.plan_prefill(base)
+    return base, copies
+
+
+def bench_prefill(args, torch, synth, B, S) -> dict:
+    """Context phase alone: bsp_write_kv + bsp_prefill_attn per layer step."""
+    dev = "cuda"
+    inp = synth.make_prefill("qwen3_0p6b", args.seed, garbage="unit", **PREFILL_SHAPE)
+    flops, nbytes, _ = prefill_work(inp)
+    pool = inp.k_pool.size * 2 * EBYTES[inp.dtype]
+    layers = args.layers or max(2, int(np.ceil(1.0e9 / pool)))
+    base, copies = _prefill_copies(S, inp, dev, layers)
+    stream = torch.cuda.current_stream()
+    sync = lambda: B.bsp_check(base.plan)  # noqa: E731
+    sec, _ = _timed_loop(torch, lambda i: S.run_prefill(copies[i % layers], stream), args.steps,
+                         args.warmup, args.warm_seconds, stream, sync)
+    _, attn_ms = _timed_loop(torch, lambda i: S.run_prefill(copies[i % layers], stream,
+                                                            write=False),
+                             args.steps, args.warmup, 0.0, stream, sync)
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    res = {
+        "metric": "context-phase (causal prefill) steps/s per layer + achieved TFLOP/s vs roofline",
+        "value": args.steps / sec, "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": sec / args.steps * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": inp.dtype, "data": "synthetic",
+        "config": {"workload": WORKLOADS["prefill"], "name": "prefill",
+                   "prompts": inp.q_len.tolist(), "layers_rotated": layers,
+                   "step": "bsp_write_kv + bsp_prefill_attn", "flops": flops,
+                   "alg_bytes": nbytes},
+        "roofline": {"kernel": "prefix_mfma_kernel<MODE 3> (bsp_prefill_attn)", "bound": "mfma",
+                     "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "avg_launch_us": attn_ms * 1e3,
+                     "hbm_gbps_alg": nbytes / (attn_ms * 1e-3) / 1e9},
+    }
+    if not args.no_cpu_baseline:
+        t, threads, n = cpu_baseline_prefill(inp, args.cpu_budget)
+        res["cpu_baseline"] = {"value": 1.0 / t, "unit": "steps/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": f"{n} random rows of the same phase (seed {args.seed}) "
+                                         f"in fp64 numpy, scaled to the whole phase by visible "
+                                         f"keys"}
+    return res
+
+
+def bench_mixed(args, torch, synth, B, S) -> dict:
+    """Mixed step: context phase on a second stream beside the fused beam step."""
+    dev = "cuda"
+    gen = synth.make_beam_step("qwen3_0p6b", args.seed, garbage="unit")
+    ctx = synth.make_prefill("qwen3_0p6b", args.seed + 1, garbage="unit", **MIXED_CTX_SHAPE)
+    step_bytes, _ = algorithmic_bytes(gen)
+    flops, ctx_bytes, _ = prefill_work(ctx)
+    gbase = S.upload_beam_step(gen, dev)
+    pool = gbase.k_pool.numel() * gbase.k_pool.element_size() * 2
+    layers = args.layers or max(2, int(np.ceil(1.0e9 / pool)))
+    gcopies = [gbase]
+    for _ in range(layers - 1):
+        c = S.BeamStepDevice(**{**gbase.__dict__})
+        c.q = gbase.q.clone()
+        c.k_pool = gbase.k_pool.clone()
+        c.v_pool = gbase.v_pool.clone()
+        c.k_new_beams = gbase.k_new_beams.clone()
+        c.v_new_beams = gbase.v_new_beams.clone()
+        gcopies.append(c)
+    S.plan_beam_step(gbase)
+    cbase, ccopies = _prefill_copies(S, ctx, dev, layers)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+
+    def sync():
+        B.bsp_check(gbase.plan)
+        B.bsp_check(cbase.plan)
+
+    res_t = {}
+    for name, cs in (("one_stream", None), ("two_streams", side)):
+        sec, _ = _timed_loop(torch, lambda i: S.run_mixed_step(ccopies[i % layers],
+                                                               gcopies[i % layers], main, cs),
+                             args.steps, args.warmup, args.warm_seconds, main, sync)
+        res_t[name] = sec / args.steps * 1e3
+    sec_g, gen_ms = _timed_loop(torch, lambda i: S.run_decode_step(gcopies[i % layers], main),
+                                args.steps, args.warmup, 0.0, main, sync)
+    sec_c, _ = _timed_loop(torch, lambda i: S.run_prefill(ccopies[i % layers], main),
+                           args.steps, args.warmup, 0.0, main, sync)
+    ms = res_t["two_streams"]
+    achieved = step_bytes / (gen_ms * 1e-3) / 1e9
+    res = {
+        "metric": "mixed steps/s per layer (context prefill + beam decode step)",
+        "value": 1e3 / ms, "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": gen.dtype, "data": "synthetic",
+        "config": {"workload": WORKLOADS["mixed"], "name": "mixed",
+                   "context_prompts": ctx.q_len.tolist(), "layers_rotated": layers,
+                   "step": "bsp_write_kv + bsp_prefill_attn (second stream) || bsp_decode_step",
+                   "one_stream_ms_per_step": res_t["one_stream"],
+                   "two_streams_ms_per_step": ms,
+                   "decode_step_alone_ms": sec_g / args.steps * 1e3,
+                   "context_phase_alone_ms": sec_c / args.steps * 1e3,
+                   "context_flops": flops, "context_alg_bytes": ctx_bytes,
+                   "decode_alg_bytes": step_bytes},
+        "roofline": {"kernel": "prefix_mfma_kernel<FUSED> (bsp_decode_step)", "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "avg_launch_us": gen_ms * 1e3},
+    }
+    if not args.no_cpu_baseline:
+        t_ctx, threads, n = cpu_baseline_prefill(ctx, args.cpu_budget / 2)
+        gen_rate = cpu_baseline("qwen3_0p6b", args.seed, args.cpu_budget / 2)["value"]
+        res["cpu_baseline"] = {"value": 1.0 / (t_ctx + 1.0 / gen_rate), "unit": "steps/s",
+                               "cores": threads, "kind": "oracle",
+                               "sample": f"{n} random context rows scaled by visible keys plus "
+                                         f"the beam-step oracle on its first requests scaled "
+                                         f"to the batch, fp64 numpy"}
+    return res
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -181,6 +378,10 @@ def main() -> None:
     from beam_search_shared_amd import step as S
 
     B.load_library()
+    if args.config in ("prefill", "mixed"):
+        fn = bench_prefill if args.config == "prefill" else bench_mixed
+        print(json.dumps(fn(args, torch, synth, B, S)), flush=True)
+        return
     dev = "cuda"
     inp = synth.make_beam_step(args.config, args.seed, garbage="unit")
     step_bytes, _ = algorithmic_bytes(inp)

@@ -250,6 +250,42 @@ bsp_status_t bsp_decode_step(bsp_plan_t plan, const void* q, const void* k_new,
                              hipStream_t stream);
 
 /*
+ * Context phase of a mixed step (PR #21738, mixed-batches commit: a step may
+ * carry context requests ahead of the generation requests; the library serves
+ * the generation rows and the context rows go through a regular paged causal
+ * prefill). Plans C context requests of one chunk each: request b has
+ * cached_len_h[b] = L_b rows already in its pages and q_len_h[b] = Sq_b new
+ * rows (1 <= Sq_b <= max_q_len, L_b + Sq_b <= max_seq_len), whose K/V the
+ * caller writes at positions L_b .. L_b + Sq_b - 1 of the request's pages
+ * (bsp_write_kv) before bsp_prefill_attn runs. block_tables_h: host int32
+ * [C][max_blocks_per_seq], the first ceil((L_b + Sq_b) / page_size) entries of
+ * each row read (BSP_ERR_PAGE_INDEX outside [0, num_pages)). Replaces the
+ * plan's current step: the beam entry points reject a plan holding a prefill
+ * step (BSP_ERR_ARG) until the next bsp_plan. Plans without key_bucket only.
+ * Workspace, staging and stream rules as for bsp_plan.
+ */
+bsp_status_t bsp_plan_prefill(bsp_plan_t plan, int32_t C, const int32_t* q_len_h,
+                              const int32_t* cached_len_h, const int32_t* block_tables_h,
+                              void* workspace_d, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Causal paged attention of the planned context requests: query row i of
+ * request b (packed row q_off_b + i, q_off_b = Sq_0 + ... + Sq_{b-1}) attends
+ * the request's keys 0 .. L_b + i (its cached rows and the chunk's rows up to
+ * its own), query head h reading KV head h / G. One launch for the whole
+ * ragged batch.
+ *   q        dtype [sum Sq_b][Hq][D], 16-byte aligned
+ *   k_pool, v_pool  as for bsp_prefix_attn, holding the chunk's rows already
+ *   o_out    dtype [sum Sq_b][Hq][D]; lse_out float [sum Sq_b][Hq] or null
+ * bf16/f16 only (BSP_ERR_UNSUPPORTED for f32). BSP_ERR_STALE_PLAN without a
+ * prefill step. Out-of-range page ids met on the device are skipped and
+ * recorded for bsp_check.
+ */
+bsp_status_t bsp_prefill_attn(bsp_plan_t plan, const void* q, const void* k_pool,
+                              const void* v_pool, void* o_out, float* lse_out,
+                              hipStream_t stream);
+
+/*
  * Comparator, not part of the cascade: per-beam attention over each beam's
  * whole sequence, reading the shared prompt once per (beam, KV head) through
  * the beam's own block table, as the decode kernel that the cascade replaces

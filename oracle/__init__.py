@@ -18,6 +18,8 @@ from .attention import (  # noqa: F401
     cached_prefix_attention,
     cached_prefix_partial,
     merge_states,
+    prefill_attention,
+    prefill_attention_one,
     sequence_slots,
     write_kv,
 )

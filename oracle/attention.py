@@ -274,3 +274,40 @@ def cached_prefix_partial(inp, segment: str, causal: bool = True,
             o[i, heads] = oo
             lse[i, heads] = ll
     return o, lse
+
+
+def prefill_attention_one(inp, b: int, i: int, scale: Optional[float] = None):
+    """Causal attention of chunk row ``i`` of context request ``b``: ``o [Hq, D]``, ``lse [Hq]``.
+
+    The context requests of a mixed step go through an ordinary causal prefill
+    (TensorRT-LLM PR #21738, mixed-batches commit: the generation rows of a
+    step that also carries context requests use the cascade, the context rows
+    the regular attention). The row at sequence position ``L_b + i`` sees the
+    request's cached rows ``0 .. L_b - 1`` and the chunk's rows ``0 .. i``,
+    and nothing after itself.
+    """
+    Hq, D = inp.q.shape[1], inp.q.shape[2]
+    Hkv = inp.new_k.shape[1]
+    G = Hq // Hkv
+    sc = default_scale(D) if scale is None else scale
+    r0 = int(inp.q_off[b])
+    o = np.zeros((Hq, D))
+    lse = np.full(Hq, NEG_INF)
+    for g in range(Hkv):
+        K = np.concatenate([inp.cache_k[b][:, g, :], inp.new_k[r0:r0 + i + 1, g, :]])
+        V = np.concatenate([inp.cache_v[b][:, g, :], inp.new_v[r0:r0 + i + 1, g, :]])
+        heads = slice(g * G, (g + 1) * G)
+        o[heads], lse[heads] = attend(inp.q[r0 + i, heads], K, V, sc)
+    return o, lse
+
+
+def prefill_attention(inp, scale: Optional[float] = None):
+    """``prefill_attention_one`` for every packed row: ``o [R, Hq, D]``, ``lse [R, Hq]``."""
+    R, Hq, D = inp.q.shape
+    o = np.zeros((R, Hq, D))
+    lse = np.full((R, Hq), NEG_INF)
+    for b in range(inp.batch):
+        r0 = int(inp.q_off[b])
+        for i in range(int(inp.q_len[b])):
+            o[r0 + i], lse[r0 + i] = prefill_attention_one(inp, b, i, scale)
+    return o, lse

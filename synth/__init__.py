@@ -10,8 +10,10 @@ from .generator import (  # noqa: F401
     BeamConfig,
     BeamStepInputs,
     CachedPrefixInputs,
+    PrefillInputs,
     make_beam_step,
     make_cached_prefix,
+    make_prefill,
     round_to_dtype,
     paged_from_rows,
 )

@@ -391,6 +391,105 @@ def make_cached_prefix(seed: int = 0, *, valid_rows: Optional[int] = None,
                               cache_k=rd(ck), cache_v=rd(cv), new_k=rd(nk), new_v=rd(nv))
 
 
+@dataclass
+class PrefillInputs:
+    """The context requests of a mixed step: one chunk of new rows per request.
+
+    Request ``b`` has ``cached_len[b] = L_b`` rows already in its pages and
+    ``q_len[b] = Sq_b`` new rows at positions ``L_b .. L_b + Sq_b - 1``. Query,
+    new-K and new-V rows are packed request after request (``q_off``). The pool
+    holds the cached rows at their pages; the chunk's positions hold garbage
+    until the step's KV write puts ``new_k``/``new_v`` there through ``slots``.
+    """
+
+    dtype: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    num_pages: int
+    max_blocks: int
+    max_seq_len: int
+    max_q_len: int
+    q_len: np.ndarray         # int64 [C]
+    cached_len: np.ndarray    # int64 [C]
+    q: np.ndarray             # float32 [R, Hq, D], R = sum q_len
+    new_k: np.ndarray         # float32 [R, Hkv, D]
+    new_v: np.ndarray
+    cache_k: list             # per request float32 [L_b, Hkv, D]
+    cache_v: list
+    k_pool: np.ndarray        # float32 [num_pages, Hkv, page_size, D]
+    v_pool: np.ndarray
+    block_tables: np.ndarray  # int32 [C, max_blocks], -1 past each request's blocks
+    slots: np.ndarray         # int32 [R]: page * page_size + row of each new row
+
+    @property
+    def batch(self) -> int:
+        return int(self.q_len.shape[0])
+
+    @property
+    def q_off(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.q_len)[:-1]]).astype(np.int64)
+
+
+def make_prefill(config, seed: int = 0, *, batch: int = 4, chunk_range: tuple = (1, 600),
+                 cached_range: tuple = (0, 0), head_dim: Optional[int] = None,
+                 dtype: Optional[str] = None, garbage: str = "normal",
+                 spare_frac: float = 0.05, max_q_len: Optional[int] = None) -> PrefillInputs:
+    """Draw the context requests of a mixed step with the heads, dtype and page
+    size of beam config ``config``: per request a chunk length in
+    ``chunk_range`` and a cached length in ``cached_range`` (inclusive), pages
+    drawn without replacement from a shuffled pool."""
+    spec = BEAM_CONFIGS[config] if isinstance(config, str) else config
+    D = head_dim if head_dim is not None else spec.head_dim
+    dt = dtype if dtype is not None else spec.dtype
+    Hq, Hkv, ps = spec.num_q_heads, spec.num_kv_heads, spec.page_size
+    rng = np.random.default_rng(seed)
+    C = batch
+    Sq = rng.integers(chunk_range[0], chunk_range[1] + 1, size=C).astype(np.int64)
+    L = rng.integers(cached_range[0], cached_range[1] + 1, size=C).astype(np.int64)
+    max_seq_len = int(cached_range[1] + chunk_range[1])
+    max_blocks = -(-max_seq_len // ps)
+    nblk = -(-(L + Sq) // ps)
+    used = int(nblk.sum())
+    num_pages = used + max(1, int(used * spare_frac))
+    perm = rng.permutation(num_pages).astype(np.int32)
+    bt = np.full((C, max_blocks), -1, np.int32)
+    off = 0
+    for b in range(C):
+        bt[b, :nblk[b]] = perm[off:off + nblk[b]]
+        off += int(nblk[b])
+    shape = (num_pages, Hkv, ps, D)
+    kp = _pool_fill(rng, shape, garbage)
+    vp = _pool_fill(rng, shape, garbage)
+    rd = lambda a: round_to_dtype(a, dt)  # noqa: E731
+    ck, cv = [], []
+    for b in range(C):
+        k = rd(rng.standard_normal((int(L[b]), Hkv, D), dtype=np.float32))
+        v = rd(rng.standard_normal((int(L[b]), Hkv, D), dtype=np.float32))
+        ck.append(k)
+        cv.append(v)
+        for j in range(int(L[b])):
+            kp[bt[b, j // ps], :, j % ps, :] = k[j]
+            vp[bt[b, j // ps], :, j % ps, :] = v[j]
+    R = int(Sq.sum())
+    q = rd(rng.standard_normal((R, Hq, D), dtype=np.float32))
+    nk = rd(rng.standard_normal((R, Hkv, D), dtype=np.float32))
+    nv = rd(rng.standard_normal((R, Hkv, D), dtype=np.float32))
+    slots = np.empty(R, np.int32)
+    r = 0
+    for b in range(C):
+        for i in range(int(Sq[b])):
+            j = int(L[b]) + i
+            slots[r] = bt[b, j // ps] * ps + j % ps
+            r += 1
+    return PrefillInputs(dtype=dt, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=ps,
+                         num_pages=num_pages, max_blocks=max_blocks, max_seq_len=max_seq_len,
+                         max_q_len=int(max_q_len if max_q_len is not None else chunk_range[1]),
+                         q_len=Sq, cached_len=L, q=q, new_k=nk, new_v=nv, cache_k=ck, cache_v=cv,
+                         k_pool=kp, v_pool=vp, block_tables=bt, slots=slots)
+
+
 def paged_from_rows(rows: np.ndarray, page_size: int, num_pages: Optional[int] = None,
                     fill: float = np.nan) -> np.ndarray:
     """Lay a row array ``[n, Hkv, D]`` out as identity pages ``[pages, Hkv, ps, D]``.

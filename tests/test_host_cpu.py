@@ -296,3 +296,63 @@ def test_pairs_chosen_for_wide_prompt_spread(prefix, paired, monkeypatch):
     assert (len(pairs) > 0) == paired
     monkeypatch.setenv("BSP_PAIRS", "1")
     assert len(_pair_plan(len(prefix), 30, 2, 128, "bf16", prefix)) == (len(prefix) + 1) // 2
+
+
+# ------------------------------------------------ prefill plans (mixed steps)
+
+def _prefill_host_plan(inp, max_q_len=None):
+    desc = B.make_desc(inp.num_q_heads, inp.num_kv_heads, inp.head_dim, inp.page_size,
+                       inp.num_pages, inp.dtype)
+    return B.Plan(desc, inp.batch, 1, inp.max_blocks, inp.max_seq_len,
+                  max_q_len or inp.max_q_len, host_only=True)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_prefill_plan_tables(seed):
+    """Page CSR from each request's block table over cached + chunk rows, keys
+    and query rows per request (bit-exact against the generator's layout)."""
+    inp = synth.make_prefill("qwen3_0p6b", seed, batch=5, chunk_range=(1, 300),
+                             cached_range=(0, 400), garbage="unit")
+    plan = _prefill_host_plan(inp)
+    B.bsp_plan_prefill(plan, inp.batch, inp.q_len, inp.cached_len, inp.block_tables)
+    indptr, pages, n_keys, valid, tail = B.bsp_debug_plan_tables(plan, inp.batch)
+    ps = inp.page_size
+    nblk = -(-(inp.cached_len + inp.q_len) // ps)
+    assert np.array_equal(np.diff(indptr), nblk)
+    want = np.concatenate([inp.block_tables[b, :nblk[b]] for b in range(inp.batch)])
+    assert np.array_equal(pages, want)
+    assert np.array_equal(n_keys, inp.cached_len + inp.q_len)
+    assert np.array_equal(valid, inp.cached_len + inp.q_len)
+    assert np.array_equal(tail, inp.q_len)
+
+
+def test_prefill_plan_rejects_bad_input():
+    inp = synth.make_prefill("qwen3_0p6b", 1, batch=3, chunk_range=(1, 50), cached_range=(0, 60),
+                             garbage="unit")
+    plan = _prefill_host_plan(inp)
+
+    def status(fn):
+        try:
+            fn()
+        except B.BspError as e:
+            return e.name
+        return "BSP_OK"
+
+    ql = inp.q_len.copy()
+    ql[1] = 51  # above max_q_len
+    assert status(lambda: B.bsp_plan_prefill(plan, 3, ql, inp.cached_len, inp.block_tables)) == \
+        "BSP_ERR_ARG"
+    ql[1] = 0
+    assert status(lambda: B.bsp_plan_prefill(plan, 3, ql, inp.cached_len, inp.block_tables)) == \
+        "BSP_ERR_ARG"
+    bt = inp.block_tables.copy()
+    bt[2, 0] = inp.num_pages
+    assert status(lambda: B.bsp_plan_prefill(plan, 3, inp.q_len, inp.cached_len, bt)) == \
+        "BSP_ERR_PAGE_INDEX"
+    cl = inp.cached_len.copy()
+    cl[0] = inp.max_seq_len
+    assert status(lambda: B.bsp_plan_prefill(plan, 3, inp.q_len, cl, inp.block_tables)) == \
+        "BSP_ERR_ARG"
+    assert status(lambda: B.bsp_plan_prefill(plan, 4, inp.q_len, inp.cached_len,
+                                             inp.block_tables)) == "BSP_ERR_ARG"
+    B.bsp_plan_prefill(plan, 3, inp.q_len, inp.cached_len, inp.block_tables)

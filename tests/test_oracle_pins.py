@@ -416,3 +416,86 @@ def test_input_slips_change_the_result():
     raw = synth.make_beam_step(PIN_CFG, 0)
     o3, _ = oracle.beam_decode_attention(raw)
     assert np.abs(o3 - o).max() > 1e-3
+
+
+# ------------------------------------------- context requests of a mixed step
+
+PREFILL_CFG = BeamConfig("pf", batch=1, beam=1, num_q_heads=6, num_kv_heads=2, head_dim=16,
+                         dtype="f32", page_size=4, prefix_range=(0, 0), tail_range=(0, 0),
+                         shuffle_pages=True)
+
+
+def test_prefill_without_cache_is_torch_causal_attention():
+    """No cached rows: each request is plain causal GQA attention (torch's is_causal)."""
+    inp = synth.make_prefill(PREFILL_CFG, 3, batch=3, chunk_range=(1, 23))
+    o, lse = oracle.prefill_attention(inp)
+    G = 3
+    for b in range(inp.batch):
+        r0, n = int(inp.q_off[b]), int(inp.q_len[b])
+        q = inp.q[r0:r0 + n].astype(np.float64).transpose(1, 0, 2)            # [Hq, n, D]
+        K = np.repeat(inp.new_k[r0:r0 + n].astype(np.float64).transpose(1, 0, 2), G, axis=0)
+        V = np.repeat(inp.new_v[r0:r0 + n].astype(np.float64).transpose(1, 0, 2), G, axis=0)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q), torch.from_numpy(K), torch.from_numpy(V), is_causal=True).numpy()
+        assert np.abs(ref.transpose(1, 0, 2) - o[r0:r0 + n]).max() <= 1e-12
+
+
+def test_prefill_with_cache_matches_torch_sdpa_with_explicit_mask():
+    """Cached rows then the chunk: key j is visible to chunk row i iff j <= L + i."""
+    inp = synth.make_prefill(PREFILL_CFG, 4, batch=3, chunk_range=(1, 9), cached_range=(0, 30))
+    o, _ = oracle.prefill_attention(inp)
+    G = 3
+    for b in range(inp.batch):
+        r0, n, L = int(inp.q_off[b]), int(inp.q_len[b]), int(inp.cached_len[b])
+        K = np.concatenate([inp.cache_k[b], inp.new_k[r0:r0 + n]]).astype(np.float64)
+        V = np.concatenate([inp.cache_v[b], inp.new_v[r0:r0 + n]]).astype(np.float64)
+        mask = np.arange(L + n)[None, :] <= (L + np.arange(n))[:, None]       # [n, L + n]
+        Kh = np.repeat(K.transpose(1, 0, 2), G, axis=0)
+        Vh = np.repeat(V.transpose(1, 0, 2), G, axis=0)
+        ref = _sdpa(inp.q[r0:r0 + n].astype(np.float64).transpose(1, 0, 2), Kh, Vh, mask[None])
+        assert np.abs(ref.transpose(1, 0, 2) - o[r0:r0 + n]).max() <= 1e-12
+
+
+def test_prefill_row_matches_50_digit_brute_force():
+    inp = synth.make_prefill(PREFILL_CFG, 5, batch=2, chunk_range=(3, 5), cached_range=(2, 6))
+    b, i, h = 1, 2, 4
+    o, lse = oracle.prefill_attention_one(inp, b, i)
+    r0, L = int(inp.q_off[b]), int(inp.cached_len[b])
+    g = h // 3
+    K = np.concatenate([inp.cache_k[b][:, g], inp.new_k[r0:r0 + i + 1, g]]).astype(np.float64)
+    V = np.concatenate([inp.cache_v[b][:, g], inp.new_v[r0:r0 + i + 1, g]]).astype(np.float64)
+    assert K.shape[0] == L + i + 1
+    mo, ml = _mp_attention(inp.q[r0 + i, h], K, V, 1 / math.sqrt(16))
+    assert abs(float(ml) - lse[h]) <= 1e-12
+    assert max(abs(float(x) - y) for x, y in zip(mo, o[h])) <= 1e-12
+
+
+def test_prefill_in_two_chunks_equals_one_chunk():
+    """Chunked prefill: the second chunk, with the first one cached, gives the
+    same rows as the whole chunk at once."""
+    inp = synth.make_prefill(PREFILL_CFG, 6, batch=1, chunk_range=(12, 12), cached_range=(5, 5))
+    o, lse = oracle.prefill_attention(inp)
+    cut = 7
+    second = synth.PrefillInputs(**{**inp.__dict__,
+                                    "q_len": np.array([12 - cut]),
+                                    "cached_len": np.array([5 + cut]),
+                                    "q": inp.q[cut:], "new_k": inp.new_k[cut:],
+                                    "new_v": inp.new_v[cut:],
+                                    "cache_k": [np.concatenate([inp.cache_k[0], inp.new_k[:cut]])],
+                                    "cache_v": [np.concatenate([inp.cache_v[0], inp.new_v[:cut]])]})
+    o2, lse2 = oracle.prefill_attention(second)
+    assert np.abs(o2 - o[cut:]).max() <= 1e-13 and np.abs(lse2 - lse[cut:]).max() <= 1e-13
+
+
+def test_prefill_pool_and_slots_hold_the_logical_rows():
+    """After the KV write through ``slots``, the request's pages read in block
+    order give its cached rows followed by the chunk's rows."""
+    inp = synth.make_prefill(PREFILL_CFG, 7, batch=3, chunk_range=(1, 9), cached_range=(0, 13))
+    kp, vp = oracle.write_kv(inp.k_pool, inp.v_pool, inp.slots, inp.new_k, inp.new_v,
+                             inp.page_size)
+    ps = inp.page_size
+    for b in range(inp.batch):
+        r0, n, L = int(inp.q_off[b]), int(inp.q_len[b]), int(inp.cached_len[b])
+        want = np.concatenate([inp.cache_k[b], inp.new_k[r0:r0 + n]])
+        got = np.stack([kp[inp.block_tables[b, j // ps], :, j % ps] for j in range(L + n)])
+        assert np.array_equal(got, want)
