@@ -286,58 +286,67 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
   const int nbt = kb_last - kb_first + 1;
   // Y's share of a pair ends with its partial state: no tail, output or token
   const bool finishes = !(PAIR && share && pair_role == 1);
-  if constexpr (FUSED) {
-    const int n_tail = ri.tail;
-    const int jcur = ri.seq - 1;
-    if (n_tail > 0 && finishes) {
-      // MODE 1: resolve the tail slots of this tile's beams into the LDS table
-      // (the host checked that it holds them), several per thread at a time:
-      // all parent lookups, then all page lookups.
-      if constexpr (MODE == 1) {
-        const int n_sl = nbt * n_tail;
-        constexpr int TR = 4;
-        for (int base = 0; base < n_sl; base += 256 * TR) {
-          int32_t src[TR], page[TR];
+  // MODE 1 tail slots of this tile's beams (slot-table rows u = (beam -
+  // kb_first) * n_tail + t), TR per thread at a time: all parent lookups, then
+  // all page lookups, then the table entries (the host checked that the table
+  // holds them).
+  constexpr int TR = 4;
+  const int n_sl = MODE == 1 && finishes ? nbt * ri.tail : 0;
+  auto sl_parents = [&](int base, int32_t (&src)[TR]) {
 #pragma unroll
-          for (int i = 0; i < TR; ++i) {
-            const int task = base + i * 256 + tid;
-            src[i] = -1;
-            if (task < n_sl) {
-              const int kk = kb_first + task / n_tail;
-              src[i] = f.ci[((int64_t)w.b * p.W + kk) * f.max_seq_len + ri.prefix + task % n_tail];
-            }
-          }
-#pragma unroll
-          for (int i = 0; i < TR; ++i) {
-            const int task = base + i * 256 + tid;
-            const int j = ri.prefix + task % n_tail;
-            page[i] = -1;
-            if (task < n_sl && src[i] >= 0 && src[i] < p.W && j != jcur)
-              page[i] = f.block_tables[((int64_t)w.b * p.W + src[i]) * f.max_blocks + (j >> shift)];
-          }
-#pragma unroll
-          for (int i = 0; i < TR; ++i) {
-            const int task = base + i * 256 + tid;
-            if (task >= n_sl) continue;
-            const int j = ri.prefix + task % n_tail;
-            int32_t e;
-            if (src[i] < 0 || src[i] >= p.W) {
-              record_fault(&p.hdr->error_bits, &p.hdr->fault_count, &p.hdr->first_value,
-                           kErrTailParent, src[i]);
-              e = -1;
-            } else if (j == jcur) {
-              e = -2 - src[i];
-            } else if (page[i] < 0 || page[i] >= p.num_pages) {
-              record_fault(&p.hdr->error_bits, &p.hdr->fault_count, &p.hdr->first_value,
-                           kErrTailPage, page[i]);
-              e = -1;
-            } else {
-              e = ((page[i] * p.hkv + w.g) << shift) + (j & pmask);
-            }
-            lds_tail[task] = e;
-          }
-        }
+    for (int i = 0; i < TR; ++i) {
+      const int task = base + i * 256 + tid;
+      src[i] = -1;
+      if (task < n_sl) {
+        const int kk = kb_first + task / ri.tail;
+        src[i] = f.ci[((int64_t)w.b * p.W + kk) * f.max_seq_len + ri.prefix + task % ri.tail];
       }
+    }
+  };
+  auto sl_pages = [&](int base, const int32_t (&src)[TR], int32_t (&page)[TR]) {
+#pragma unroll
+    for (int i = 0; i < TR; ++i) {
+      const int task = base + i * 256 + tid;
+      const int j = ri.prefix + task % max(ri.tail, 1);
+      page[i] = -1;
+      if (task < n_sl && src[i] >= 0 && src[i] < p.W && j != ri.seq - 1)
+        page[i] = f.block_tables[((int64_t)w.b * p.W + src[i]) * f.max_blocks + (j >> shift)];
+    }
+  };
+  auto sl_commit = [&](int base, const int32_t (&src)[TR], const int32_t (&page)[TR]) {
+#pragma unroll
+    for (int i = 0; i < TR; ++i) {
+      const int task = base + i * 256 + tid;
+      if (task >= n_sl) continue;
+      const int j = ri.prefix + task % ri.tail;
+      int32_t e;
+      if (src[i] < 0 || src[i] >= p.W) {
+        record_fault(&p.hdr->error_bits, &p.hdr->fault_count, &p.hdr->first_value,
+                     kErrTailParent, src[i]);
+        e = -1;
+      } else if (j == ri.seq - 1) {
+        e = -2 - src[i];
+      } else if (page[i] < 0 || page[i] >= p.num_pages) {
+        record_fault(&p.hdr->error_bits, &p.hdr->fault_count, &p.hdr->first_value,
+                     kErrTailPage, page[i]);
+        e = -1;
+      } else {
+        e = ((page[i] * p.hkv + w.g) << shift) + (j & pmask);
+      }
+      lds_tail[task] = e;
+    }
+  };
+  // With MB <= 2 the first batch's lookups overlap the start of the prompt
+  // stream: parents go out with the queries and the first page ids, pages
+  // right after, and the table is written once the prompt is done. (At MB = 3
+  // the eight registers they hold are not free.)
+  constexpr bool DEFER = MODE == 1 && MB <= 2;
+  int32_t t_src[TR], t_page[TR];
+  if constexpr (MODE == 1 && !DEFER) {
+    for (int base = 0; base < n_sl; base += 256 * TR) {
+      sl_parents(base, t_src);
+      sl_pages(base, t_src, t_page);
+      sl_commit(base, t_src, t_page);
     }
   }
 
@@ -373,10 +382,7 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
     }
   }
 
-  // The query loads must be complete before the tile loads start: the
-  // compiler does not count the inline-asm tile loads, so a wait it placed
-  // later for a query register would also wait for every tile in flight.
-  wait_vmcnt<0>();
+  if constexpr (DEFER) sl_parents(0, t_src);
 
   f32x4 oacc[NDB][MB];
   float mrow[MB], lrow[MB];
@@ -509,26 +515,45 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
   const int win_first = w.k_lo / keys_per_win;
   const int n_win = w.k_hi > w.k_lo ? (w.k_hi - 1) / keys_per_win - win_first + 1 : 0;
 
+  // Page ids of one window of the request's keys into LDS.
+  auto fill_pages = [&](int wi) {
+    const int w0 = (win_first + wi) * keys_per_win;
+    const int pg0 = w0 >> shift;
+    const int npg = ((min(w.k_hi, w0 + keys_per_win) - 1) >> shift) - pg0 + 1;
+    for (int i = tid; i < npg; i += 256) {
+      int32_t page = p.pages[ri.page_off + pg0 + i];
+      if (page < 0 || page >= p.num_pages) {  // the plan validated these; flag corruption
+        record_fault(&p.hdr->error_bits, &p.hdr->fault_count, &p.hdr->first_value,
+                     kErrPrefixPage, page);
+        page = 0;
+      }
+      lds_pages[i] = page;
+    }
+  };
+  if constexpr (DEFER) {
+    if (n_win > 0) fill_pages(0);
+    // The queries, the tail parents and the first page ids are complete
+    // before any tile load is issued (the compiler does not count the
+    // inline-asm tile loads, so a wait it placed later for one of these
+    // registers would also wait for every tile in flight). The tail page
+    // lookups then stay in flight beside the tiles; they are used after the
+    // prompt, when everything has landed.
+    wait_vmcnt<0>();
+    sl_pages(0, t_src, t_page);
+  }
+
   for (int wi = 0; wi < n_win; ++wi) {
     const int w0 = (win_first + wi) * keys_per_win;
     const int seg_lo = max(w.k_lo, w0);
     const int seg_hi = min(w.k_hi, w0 + keys_per_win);
     const int pg0 = w0 >> shift;
-    __syncthreads();  // every wave is done with the previous window
-    {
-      const int npg = ((seg_hi - 1) >> shift) - pg0 + 1;
-      for (int i = tid; i < npg; i += 256) {
-        int32_t page = p.pages[ri.page_off + pg0 + i];
-        if (page < 0 || page >= p.num_pages) {  // the plan validated these; flag corruption
-          record_fault(&p.hdr->error_bits, &p.hdr->fault_count, &p.hdr->first_value,
-                       kErrPrefixPage, page);
-          page = 0;
-        }
-        lds_pages[i] = page;
-      }
+    if (!DEFER || wi > 0) {
+      __syncthreads();  // every wave is done with the previous window
+      fill_pages(wi);
+      // also the queries (first window): see above
       wait_vmcnt<0>();
-      __syncthreads();
     }
+    __syncthreads();
     const int ntp = (seg_hi - seg_lo + KT - 1) / KT;
     const int nt = ntp;
 
@@ -672,6 +697,58 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
       }
     }
   }
+
+  if constexpr (DEFER) {  // the slot table, now that the prompt is done
+    sl_commit(0, t_src, t_page);
+    for (int base = 256 * TR; base < n_sl; base += 256 * TR) {
+      sl_parents(base, t_src);
+      sl_pages(base, t_src, t_page);
+      sl_commit(base, t_src, t_page);
+    }
+  }
+
+  // ---- current tokens of this tile's beams: a beam's token is written by the
+  // tile holding its first row, 16 bytes per task. Nothing in this launch
+  // reads it back from the pool (the tails take the current token from the
+  // new-token rows), so it is written last, where its loads and stores delay
+  // no tile. (Loading the first tasks before the tails, to overlap the two
+  // round trips, measured slower.)
+  const int kw_lo = (w.qt * rt + p.group - 1) / p.group;
+  const int kw_hi = min(p.W, ((w.qt + 1) * rt + p.group - 1) / p.group);
+  const int n_tw = FUSED && n_tail > 0 && finishes ? (kw_hi - kw_lo) * CPR : 0;
+  auto tw_load = [&](int base, auto& page, auto& kd, auto& vd) {
+    constexpr int N = (int)(sizeof(page) / sizeof(int32_t));
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int task = base + i * 256 + tid;
+      page[i] = -1;
+      if (task < n_tw) {
+        const int kk = kw_lo + task / CPR;
+        const int64_t src = ((int64_t)w.b * p.W + kk) * f.new_stride + (int64_t)w.g * D + (task % CPR) * 8;
+        page[i] = f.block_tables[((int64_t)w.b * p.W + kk) * f.max_blocks + ((ri.seq - 1) >> shift)];
+        kd[i] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(f.k_new) + src);
+        vd[i] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(f.v_new) + src);
+      }
+    }
+  };
+  auto tw_store = [&](int base, const auto& page, const auto& kd, const auto& vd) {
+    constexpr int N = (int)(sizeof(page) / sizeof(int32_t));
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int task = base + i * 256 + tid;
+      if (task >= n_tw) continue;
+      if (page[i] < 0 || page[i] >= p.num_pages) {
+        if (task % CPR == 0)
+          record_fault(&p.hdr->error_bits, &p.hdr->fault_count, &p.hdr->first_value,
+                       kErrTailPage, page[i]);
+        continue;
+      }
+      const int64_t dst =
+          ((((int64_t)page[i] * p.hkv + w.g) << shift) + ((ri.seq - 1) & pmask)) * D + (task % CPR) * 8;
+      *reinterpret_cast<u32x4*>(static_cast<T*>(f.k_pool_w) + dst) = kd[i];
+      *reinterpret_cast<u32x4*>(static_cast<T*>(f.v_pool_w) + dst) = vd[i];
+    }
+  };
 
   // ---- MODE 1: each wave attends its own beams' tails (slot-table rows
   // u = (beam - kb_first) * n_tail + t) in 16-key sub-tiles, double-buffered
@@ -941,50 +1018,16 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
     }
   }
 
-  // ---- fused step: write this tile's beams' current tokens into the pool
-  if (FUSED && n_tail > 0) {
-    const int jcur = ri.seq - 1;
-    // A beam's token is written by the tile holding its first row. It is
-    // written last: nothing in this launch reads it back from the pool (the
-    // tails take the current token from the new-token rows), and here its
-    // loads and stores delay no tile. Every thread issues the loads of
-    // several tasks before using any of them.
-    const int kw_lo = (w.qt * rt + p.group - 1) / p.group;
-    const int kw_hi = min(p.W, ((w.qt + 1) * rt + p.group - 1) / p.group);
-    const int n_tw = (kw_hi - kw_lo) * CPR;
-    // tasks per thread: all of a wide beam's tokens in one round; fewer in the
-    // paired kernel, where the next segment's state is live across the loads
+  // ---- the current tokens (see above); the unrolled batch holds all of a
+  // wide beam's tasks, fewer in the paired kernel, where the next segment's
+  // state is live across the loads
+  if (n_tw > 0) {
     constexpr int TW = PAIR ? 4 : 16;
     for (int base = 0; base < n_tw; base += 256 * TW) {
       int32_t page[TW];
       u32x4 kd[TW], vd[TW];
-#pragma unroll
-      for (int i = 0; i < TW; ++i) {
-        const int task = base + i * 256 + tid;
-        page[i] = -1;
-        if (task < n_tw) {
-          const int kk = kw_lo + task / CPR;
-          const int64_t src = ((int64_t)w.b * p.W + kk) * f.new_stride + (int64_t)w.g * D + (task % CPR) * 8;
-          page[i] = f.block_tables[((int64_t)w.b * p.W + kk) * f.max_blocks + (jcur >> shift)];
-          kd[i] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(f.k_new) + src);
-          vd[i] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(f.v_new) + src);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < TW; ++i) {
-        const int task = base + i * 256 + tid;
-        if (task >= n_tw) continue;
-        if (page[i] < 0 || page[i] >= p.num_pages) {
-          if (task % CPR == 0)
-            record_fault(&p.hdr->error_bits, &p.hdr->fault_count, &p.hdr->first_value,
-                         kErrTailPage, page[i]);
-          continue;
-        }
-        const int64_t dst =
-            ((((int64_t)page[i] * p.hkv + w.g) << shift) + (jcur & pmask)) * D + (task % CPR) * 8;
-        *reinterpret_cast<u32x4*>(static_cast<T*>(f.k_pool_w) + dst) = kd[i];
-        *reinterpret_cast<u32x4*>(static_cast<T*>(f.v_pool_w) + dst) = vd[i];
-      }
+      tw_load(base, page, kd, vd);
+      tw_store(base, page, kd, vd);
     }
   }
   }  // segments

@@ -140,3 +140,15 @@ def test_full_size_prefill_sampled():
             r = int(off[b]) + i
             assert np.abs(out[r] - fo).max() <= to, (b, i)
             assert np.abs(lse[r] - fl).max() <= tl, (b, i)
+
+
+@pytest.mark.parametrize("name,page_size,kw", [
+    ("single_key", 16, dict(batch=1, chunk_range=(1, 1), cached_range=(0, 0))),
+    ("page_size_1", 1, dict(batch=3, chunk_range=(1, 120), cached_range=(0, 90))),
+    ("page_size_1024", 1024, dict(batch=3, chunk_range=(100, 700), cached_range=(0, 900))),
+])
+def test_prefill_degenerate_shapes(name, page_size, kw):
+    cfg = BeamConfig(name, 1, 1, 8, 2, 128, "bf16", page_size, (0, 0), (0, 0), True)
+    inp = synth.make_prefill(cfg, 13, **kw)
+    say(f"prefill {name} Sq={inp.q_len.tolist()} L={inp.cached_len.tolist()}")
+    _check_prefill(inp, name)

@@ -532,3 +532,21 @@ def test_full_size_fused_sampled(cfg, pairs_env, monkeypatch):
         fo, fl = oracle.beam_attention_one(ref, x, k)
         assert np.abs(out[x, k] - fo[0]).max() <= to, (x, k)
         assert np.abs(lse[x, k] - fl[0]).max() <= tl, (x, k)
+
+
+# ------------------------------------------------- degenerate shapes, fused
+
+@pytest.mark.parametrize("name,cfg", [
+    # every prompt empty: only the tails are attended
+    ("empty_prompts", BeamConfig("e0", 3, 5, 4, 2, 128, "bf16", 16, (0, 0), (1, 6), True)),
+    # one request, one beam, MHA (group 1), prompt inside one page
+    ("single_mha", BeamConfig("s1", 1, 1, 2, 2, 64, "f16", 32, (1, 20), (1, 1), False)),
+    # one-row pages: every key tile spans 32 pages
+    ("page_size_1", BeamConfig("p1", 2, 6, 4, 2, 128, "bf16", 1, (40, 200), (1, 5), True)),
+    # 1024-row pages: a prompt in one page
+    ("page_size_1024", BeamConfig("p1k", 2, 6, 8, 2, 128, "f16", 1024, (300, 900), (1, 5), True)),
+])
+def test_decode_step_degenerate_shapes(name, cfg):
+    inp = synth.make_beam_step(cfg, 21)
+    say(f"fused {name} P={inp.prefix_len.tolist()} T={inp.tail_len.tolist()}")
+    _run_fused_and_check(inp, name)
