@@ -274,8 +274,14 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
   const ReqInfo ri = p.req[w.b];
 
   const int M = PREFILL ? ri.tail * p.group : p.W * p.q_len * p.group;
-  const int row0 = w.qt * (64 * MB) + wave * (16 * MB);
+  // Rows per wave: 16 per query block; in the fused step with one block per
+  // wave and at most 32 (16) query rows per request, 8 (4) per wave, so that
+  // all four waves share the beams' tails instead of two (one) of them. Lanes
+  // past a wave's rows are treated like rows past M.
+  const int rpw = MODE == 1 && MB == 1 && p.n_qtiles == 1 ? (M <= 16 ? 4 : M <= 32 ? 8 : 16) : 16;
+  const int row0 = w.qt * (64 * MB) + wave * (rpw * MB);
   const bool wave_active = row0 < M;
+  const int row_end = min(M, row0 + rpw * MB);  // this wave's rows: [row0, row_end)
   const int shift = p.page_shift;
   const int pmask = (1 << shift) - 1;
 
@@ -357,7 +363,7 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
   for (int qb = 0; qb < MB; ++qb) {
     const int r = row0 + qb * 16 + l16;
     climit[qb] = INT_MAX;
-    if (r < M) {
+    if (r < row_end) {
       const int hh = r % p.group;
       const int t = r / p.group;
       int64_t qrow;
@@ -764,7 +770,7 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
       constexpr int NBUF = REGION >= 4 * SUB ? 2 : 1;
       static_assert(REGION >= 2 * SUB && NIW >= 1, "sub-tile must fit a wave's share of the ring");
       T* region = &lds_kv[0][0][0] + wave * REGION;
-      const int r_last = min(row0 + 16 * MB, M) - 1;
+      const int r_last = row_end - 1;
       const int u_lo = (row0 / p.group - kb_first) * n_tail;
       const int u_hi = (r_last / p.group - kb_first + 1) * n_tail;
       const int n_sub = (u_hi - u_lo + KW - 1) / KW;
@@ -772,7 +778,7 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
 #pragma unroll
       for (int qb = 0; qb < MB; ++qb) {
         const int r = row0 + qb * 16 + l16;
-        tail_lo[qb] = r < M ? (r / p.group - kb_first) * n_tail : INT_MIN / 2;
+        tail_lo[qb] = r < row_end ? (r / p.group - kb_first) * n_tail : INT_MIN / 2;
       }
       // a finite row for sub-tile rows that carry no key (padding, invalid slots)
       const int64_t pad_row = ((int64_t)w.b * p.W + kb_first) * f.new_stride + (int64_t)w.g * D;
@@ -816,8 +822,8 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
         for (int qb = 0; qb < MB; ++qb) {
           const int r_lo = row0 + qb * 16;
           const int lo = (r_lo / p.group - kb_first) * n_tail;
-          const int hi = ((min(r_lo + 16, M) - 1) / p.group - kb_first + 1) * n_tail;
-          act[qb] = r_lo < M && lo < min(u0 + KW, u_hi) && hi > u0;
+          const int hi = ((min(r_lo + 16, row_end) - 1) / p.group - kb_first + 1) * n_tail;
+          act[qb] = r_lo < row_end && lo < min(u0 + KW, u_hi) && hi > u0;
           sacc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
@@ -892,7 +898,7 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
 #pragma unroll
       for (int qb = 0; qb < MB; ++qb) {
         const int r = row0 + qb * 16 + l16;
-        const bool row_ok = r < M;
+        const bool row_ok = r < row_end;
         const int kbeam = row_ok ? r / p.group : kb_first;
         const int h = w.g * p.group + (row_ok ? r % p.group : 0);
         // this lane's columns of O^T: d = db * 16 + 4 * l4 + i (query kept packed)
@@ -990,7 +996,7 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
   for (int qb = 0; qb < MB; ++qb) {
     const float lt = sum4x16(lrow[qb]);
     const int r = row0 + qb * 16 + l16;
-    if (!wave_active || r >= M) continue;
+    if (!wave_active || r >= row_end) continue;
     const int hh = r % p.group;
     const int t = r / p.group;
     const int64_t grow = PREFILL ? (int64_t)ri.q_off + t
