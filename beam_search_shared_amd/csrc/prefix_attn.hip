@@ -167,9 +167,10 @@ __device__ __forceinline__ int32_t resolve_fused_slot(const PrefixParams& p, con
 // (request, KV head, query tile) also writes its beams' current tokens and
 // attends each beam's tail (gathered through cache_indirection) in the same
 // online softmax as the shared keys, then writes the final output in the
-// storage dtype. MODE 1 resolves the tail slots into an LDS table and streams
-// the tail rows through the tile pipeline after the shared keys; MODE 2, for
-// tails too long for that table, gathers them key by key afterwards.
+// storage dtype. MODE 1 resolves the tail slots into an LDS table and, after
+// the shared keys, each wave streams its own beams' tail rows through its
+// quarter of the then idle tile ring; MODE 2, for tails too long for that
+// table, gathers them key by key afterwards.
 // MODE 3: bsp_prefill_attn, the context requests of a mixed step: ragged query
 // rows packed per request, each row attending the request's cached rows and,
 // causally, the chunk's rows up to its own; work items (request, query tile)
@@ -195,7 +196,6 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
   __shared__ __attribute__((aligned(1024))) T lds_kv[NST][2][TILE];
   __shared__ int lds_pages[kPageWin];
   __shared__ int lds_tail[MODE == 1 ? kTailSlots : 1];
-
 
   // ---- work: one (request, KV head, key split, query tile) item; with
   // balanced pairs (PairInfo), one or two segments of a pair for one KV head.
@@ -256,6 +256,9 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
     }
   }
 
+  // Everything from here to the end of the kernel runs once per segment (one
+  // segment except in the second workgroup of a balanced pair); the body is
+  // not indented for the loop.
 #pragma nounroll
   for (int si = 0; si < nseg; ++si) {
   if (si > 0) __syncthreads();  // the previous segment is done with LDS
@@ -285,7 +288,7 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
   const int shift = p.page_shift;
   const int pmask = (1 << shift) - 1;
 
-  // ---- fused step: write this tile's beams' current tokens, resolve tail slots
+  // ---- fused step: the beams with a row in this query tile, their tail slots
   const int rt = 64 * MB;                       // query rows per workgroup
   const int kb_first = (w.qt * rt) / p.group;   // beams with a row in this tile
   const int kb_last = min(p.W - 1, ((w.qt + 1) * rt - 1) / p.group);
@@ -342,11 +345,12 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
       lds_tail[task] = e;
     }
   };
-  // With MB <= 2 the first batch's lookups overlap the start of the prompt
-  // stream: parents go out with the queries and the first page ids, pages
-  // right after, and the table is written once the prompt is done. (At MB = 3
-  // the eight registers they hold are not free.)
-  constexpr bool DEFER = MODE == 1 && MB <= 2;
+  // With one query block per wave the first batch's lookups overlap the start
+  // of the prompt stream: parents go out with the queries and the first page
+  // ids, pages right after, and the table is written once the prompt is done.
+  // (With more blocks the eight registers they hold cost more than the
+  // overlap gains: measured at MB = 2, not free at MB = 3.)
+  constexpr bool DEFER = MODE == 1 && MB == 1;
   int32_t t_src[TR], t_page[TR];
   if constexpr (MODE == 1 && !DEFER) {
     for (int base = 0; base < n_sl; base += 256 * TR) {

@@ -10,6 +10,9 @@
  * are merged exactly through their log-sum-exp. A beam-1 variant bounds the
  * key range to the valid cached prefix rounded up to 256 rows (Phi-4 cached-
  * prefix PR, TensorRT-Model-Connect #2202: Exit Criteria, Implementation).
+ * Steps that also carry context requests (PR #21738, mixed-batches commit)
+ * run those through a ragged causal prefill (bsp_plan_prefill,
+ * bsp_prefill_attn) beside the beam step of the generation requests.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -34,6 +37,7 @@
  *     cache_indirection int32 [B, W, max_seq_len]
  *     partial o       float [n_parts][B * W * q_len][num_q_heads][head_dim]
  *     partial lse     float [n_parts][B * W * q_len][num_q_heads]
+ *     prefill q / o   [sum of chunk rows][num_q_heads][head_dim], request-major
  *   Query head h reads KV head h / (num_q_heads / num_kv_heads).
  * - LSE is the natural log of the softmax denominator, scale included; an
  *   empty key set gives o = 0 and lse = -inf.
