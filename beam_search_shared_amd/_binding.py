@@ -73,6 +73,7 @@ _SIGS = {
     "bsp_plan_destroy": (None, [_P]),
     "bsp_plan": (_I32, [_P, _I32, _I32, _I32, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "bsp_plan_num_splits": (_I32, [_P]),
+    "bsp_plan_split_keys": (_I32, [_P]),
     "bsp_plan_tail_len": (_I32, [_P]),
     "bsp_write_kv": (_I32, [_P, _P, _P, _I64, _P, _I32, _P, _P, _P]),
     "bsp_prefix_attn": (_I32, [_P, _P, _P, _P, _P, _P, _P]),
@@ -173,6 +174,10 @@ class Plan:
     @property
     def num_splits(self) -> int:
         return int(load_library().bsp_plan_num_splits(self.handle))
+
+    @property
+    def split_keys(self) -> int:
+        return int(load_library().bsp_plan_split_keys(self.handle))
 
     @property
     def tail_len(self) -> int:

@@ -98,6 +98,7 @@ struct bsp_plan_s {
   // current plan
   bool planned = false;
   int32_t B = 0, W = 0, q_len = 0, tail_pad = 0, n_split = 1, rows_per_req = 0, n_pairs = 0;
+  int32_t split_keys = 0;  // keys per split of the current step (0: one pass)
   void* ws_d = nullptr;
   void* zeroed_ws = nullptr;  // workspace whose header this plan has cleared
   std::vector<ReqInfo> h_req;
@@ -186,8 +187,9 @@ bsp_status_t bsp_plan_create(const bsp_layer_desc_t* desc, int32_t max_requests,
     return fail(BSP_ERR_ARG, "cached-prefix mode needs max_cache_rows > 0");
   if (d.mask != BSP_MASK_NONE && d.mask != BSP_MASK_CAUSAL)
     return fail(BSP_ERR_ARG, "mask %d is not NONE or CAUSAL", d.mask);
-  if (d.kv_split < 0 || d.kv_split % 64 != 0)
-    return fail(BSP_ERR_ARG, "kv_split (%d) must be 0 or a positive multiple of 64", d.kv_split);
+  if (d.kv_split < -1 || (d.kv_split > 0 && d.kv_split % 64 != 0))
+    return fail(BSP_ERR_ARG, "kv_split (%d) must be -1, 0 or a positive multiple of 64",
+                d.kv_split);
   if (max_requests <= 0 || max_beam <= 0 || max_blocks_per_seq <= 0 || max_seq_len <= 0 ||
       max_q_len <= 0)
     return fail(BSP_ERR_ARG, "capacities must be positive");
@@ -383,7 +385,30 @@ bsp_status_t bsp_plan(bsp_plan_t pl, int32_t B, int32_t W, int32_t q_len,
     }
     r.page_off = (int32_t)total_pages;
     total_pages += nblk;
-    r.n_split = d.kv_split > 0 ? (int32_t)(r.valid > 0 ? ceil_div(r.valid, d.kv_split) : 1) : 1;
+  }
+
+  // Key split: fixed, none, or (kv_split = -1) the smallest multiple of 64
+  // keys whose work items (request, KV head, split, query tile) still fit one
+  // round of two workgroups per CU; a split above the longest key range is no
+  // split.
+  int32_t split_keys = d.kv_split > 0 ? d.kv_split : 0;
+  if (d.kv_split < 0) {
+    const int rows = W * q_len * (d.num_q_heads / d.num_kv_heads);
+    const int64_t n_qt = ceil_div(rows, bsp::prefix_rows_per_tile(d.dtype, d.head_dim, rows));
+    int32_t v_max = 0;
+    for (int b = 0; b < B; ++b) v_max = std::max(v_max, req[b].valid);
+    auto items = [&](int64_t s) {
+      int64_t n = 0;
+      for (int b = 0; b < B; ++b) n += std::max<int64_t>(1, ceil_div(req[b].valid, s));
+      return n * d.num_kv_heads * n_qt;
+    };
+    int64_t s = 64;
+    while (s < v_max && items(s) > bsp::kFillBlocks) s += 64;
+    split_keys = s < v_max ? (int32_t)s : 0;
+  }
+  for (int b = 0; b < B; ++b) {
+    ReqInfo& r = req[b];
+    r.n_split = split_keys > 0 ? (int32_t)(r.valid > 0 ? ceil_div(r.valid, split_keys) : 1) : 1;
     if (r.n_split > n_split) n_split = r.n_split;
   }
 
@@ -470,6 +495,7 @@ bsp_status_t bsp_plan(bsp_plan_t pl, int32_t B, int32_t W, int32_t q_len,
   pl->q_len = q_len;
   pl->tail_pad = d.max_tail > 0 ? d.max_tail : max_tail_seen;
   pl->n_split = n_split;
+  pl->split_keys = split_keys;
   pl->rows_per_req = W * q_len * (d.num_q_heads / d.num_kv_heads);
   pl->n_pairs = n_pairs;
   pl->h_pairs = std::move(pairs);
@@ -484,6 +510,7 @@ bsp_status_t bsp_plan(bsp_plan_t pl, int32_t B, int32_t W, int32_t q_len,
 }
 
 int32_t bsp_plan_num_splits(bsp_plan_t pl) { return pl && pl->planned ? pl->n_split : -1; }
+int32_t bsp_plan_split_keys(bsp_plan_t pl) { return pl && pl->planned ? pl->split_keys : -1; }
 int32_t bsp_plan_tail_len(bsp_plan_t pl) { return pl && pl->planned ? pl->tail_pad : -1; }
 
 bsp_status_t bsp_plan_prefill(bsp_plan_t pl, int32_t C, const int32_t* q_len_h,
@@ -516,7 +543,7 @@ bsp_status_t bsp_plan_prefill(bsp_plan_t pl, int32_t C, const int32_t* q_len_h,
   for (; mb > 1; --mb) {
     int64_t n = 0;
     for (int b = 0; b < C; ++b) n += ceil_div((int64_t)std::max(q_len_h[b], 0) * G, 64 * mb);
-    if (n * d.num_kv_heads >= bsp::kPrefillMinBlocks) break;
+    if (n * d.num_kv_heads >= bsp::kFillBlocks) break;
   }
   const int rpt = 64 * mb;
   std::vector<ReqInfo> req(C);
@@ -710,7 +737,7 @@ bsp_status_t bsp_prefix_attn(bsp_plan_t pl, const void* q, const void* k_pool, c
   p.page_shift = pl->page_shift;
   p.num_pages = d.num_pages;
   p.n_split = pl->n_split;
-  p.split_keys = d.kv_split;
+  p.split_keys = pl->split_keys;
   const int rows_per_tile = bsp::prefix_rows_per_tile(d.dtype, d.head_dim, pl->rows_per_req);
   p.n_qtiles = (int32_t)ceil_div(pl->rows_per_req, rows_per_tile);
   p.causal = d.mask == BSP_MASK_CAUSAL ? 1 : 0;
@@ -732,7 +759,7 @@ bsp_status_t bsp_decode_step(bsp_plan_t pl, const void* q, const void* k_new, co
     return fail(BSP_ERR_UNSUPPORTED, "bsp_decode_step runs bf16/f16; use the separate calls for f32");
   if (pl->q_len != 1) return fail(BSP_ERR_UNSUPPORTED, "bsp_decode_step needs q_len == 1");
   if (d.key_bucket > 0) return fail(BSP_ERR_UNSUPPORTED, "bsp_decode_step is beam mode only");
-  if (d.kv_split > 0) return fail(BSP_ERR_UNSUPPORTED, "bsp_decode_step takes no kv_split");
+  if (d.kv_split != 0) return fail(BSP_ERR_UNSUPPORTED, "bsp_decode_step takes no kv_split");
   if (!q || !k_new || !v_new || !k_pool || !v_pool || !block_tables_d || !cache_indirection_d ||
       !o_out)
     return fail(BSP_ERR_ARG, "null pointer");

@@ -170,7 +170,8 @@ int prefix_rows_per_tile(int dtype, int head_dim, int rows_per_req);
 // (64 * mb query rows per work item); the plan takes fewer when the batch is
 // too small to give every CU two workgroups.
 constexpr int prefill_max_mb(int head_dim) { return head_dim == 256 ? 2 : 3; }
-constexpr int kPrefillMinBlocks = 512;
+// Workgroups that fill the chip once: two per CU on the 256 CUs of an MI355X.
+constexpr int kFillBlocks = 512;
 hipError_t launch_prefill(const PrefixParams& p, const FusedParams& f, int dtype, int head_dim,
                           int mb, int n_items, hipStream_t s);
 hipError_t launch_tail(const TailParams& p, int dtype, int head_dim, hipStream_t s);

@@ -19,21 +19,26 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   const int c = (int)(idx % chunks);
   const int64_t rh = idx / chunks;  // row * heads + head
 
+  // Both passes are unrolled so that a group's loads are in flight together:
+  // with many parts and few rows (a split one-row decode) each dependent load
+  // would otherwise cost a full memory round trip.
   float m = -INFINITY;
+#pragma unroll 8
   for (int part = 0; part < p.n_parts; ++part)
     m = fmaxf(m, p.lse_parts[part * p.lse_stride + rh]);
-
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float lse = -INFINITY;
   if (m != -INFINITY) {
     float denom = 0.f;
+#pragma unroll 8
     for (int part = 0; part < p.n_parts; ++part) {
       const float l = p.lse_parts[part * p.lse_stride + rh];
-      const float w = fast_exp2((l - m) * kLog2e);  // exp(-inf) -> 0
-      if (w == 0.f) continue;                          // an empty part adds nothing
       const f32x4 o = *reinterpret_cast<const f32x4*>(p.o_parts + part * p.o_stride +
                                                        rh * p.d + c * 4);
-      acc += w * o;
+      const float w = fast_exp2((l - m) * kLog2e);  // exp(-inf) -> 0
+      // an empty part adds nothing, whatever its o holds (a select, not w * o)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = w > 0.f ? fmaf(w, o[e], acc[e]) : acc[e];
       denom += w;
     }
     acc *= 1.f / denom;
@@ -45,8 +50,83 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   if (p.lse_out != nullptr && c == 0) p.lse_out[rh] = lse;
 }
 
+// Few (row, head) pairs and many parts (a one-row decode split into dozens of
+// key chunks): one workgroup per (row, head). The parts are spread over the
+// threads for the max and the denominator (block reductions), then over 8
+// slices of 32 threads for the weighted sum, each slice covering head_dim in
+// 4-element chunks and every eighth part; the slices are summed through LDS.
+constexpr int kMergeSlices = 8;
+template <typename T>
+__global__ __launch_bounds__(256) void merge_wide_kernel(MergeParams p) {
+  __shared__ float red[4];
+  __shared__ float acc_s[kMergeSlices][256];  // head_dim <= 256
+  const int64_t rh = blockIdx.x;  // row * heads + head
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const float* lse_p = p.lse_parts + rh;
+
+  float m = -INFINITY;
+  for (int part = tid; part < p.n_parts; part += 256) m = fmaxf(m, lse_p[part * p.lse_stride]);
+  m = wave_max(m);
+  if ((tid & 63) == 0) red[wave] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  if (m == -INFINITY) {  // every part empty
+    T* out = static_cast<T*>(p.o_out) + rh * p.d;
+    for (int i = tid; i < p.d; i += 256) out[i] = Traits<T>::from_f(0.f);
+    if (p.lse_out != nullptr && tid == 0) p.lse_out[rh] = -INFINITY;
+    return;
+  }
+  float den = 0.f;
+  for (int part = tid; part < p.n_parts; part += 256)
+    den += fast_exp2((lse_p[part * p.lse_stride] - m) * kLog2e);
+  den = wave_sum(den);
+  if ((tid & 63) == 0) red[wave] = den;
+  __syncthreads();
+  den = (red[0] + red[1]) + (red[2] + red[3]);
+
+  const int slice = tid / 32;
+  const int cl = tid % 32;
+  const int chunks = p.d / 4;
+  for (int c = cl; c < chunks; c += 32) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int part = slice; part < p.n_parts; part += kMergeSlices) {
+      const float w = fast_exp2((lse_p[part * p.lse_stride] - m) * kLog2e);
+      const f32x4 o = *reinterpret_cast<const f32x4*>(p.o_parts + part * p.o_stride + rh * p.d + c * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = w > 0.f ? fmaf(w, o[e], acc[e]) : acc[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc_s[slice][c * 4 + e] = acc[e];
+  }
+  __syncthreads();
+  const float inv = 1.f / den;
+  T* out = static_cast<T*>(p.o_out) + rh * p.d;
+  for (int i = tid; i < p.d; i += 256) {
+    float v = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < kMergeSlices; ++sl) v += acc_s[sl][i];
+    out[i] = Traits<T>::from_f(v * inv);
+  }
+  if (p.lse_out != nullptr && tid == 0) p.lse_out[rh] = m + __logf(den);
+}
+
 hipError_t launch_merge(const MergeParams& p, int out_dtype, hipStream_t s) {
-  const int64_t total = (int64_t)p.rows * p.heads * (p.d / 4);
+  const int64_t pairs = (int64_t)p.rows * p.heads;
+  if (pairs == 0) return hipSuccess;
+  if (pairs <= 4096 && p.n_parts > kMergeSlices && p.d <= 256) {
+    const unsigned blocks = (unsigned)pairs;
+    if (out_dtype == BSP_F32)
+      merge_wide_kernel<float><<<blocks, 256, 0, s>>>(p);
+    else if (out_dtype == BSP_F16)
+      merge_wide_kernel<_Float16><<<blocks, 256, 0, s>>>(p);
+    else
+      merge_wide_kernel<__bf16><<<blocks, 256, 0, s>>>(p);
+    return hipGetLastError();
+  }
+  const int64_t total = pairs * (p.d / 4);
   const unsigned blocks = (unsigned)((total + 255) / 256);
   if (out_dtype == BSP_F32)
     merge_kernel<float><<<blocks, 256, 0, s>>>(p);

@@ -190,7 +190,8 @@ def upload_cached_prefix(inp, device="cuda", page_size: int = 32, key_bucket: in
     The cache allocation ``[max_cache_rows, Hkv, D]`` becomes pages
     ``0 .. cache_pages-1`` (page p holds rows p*ps .. p*ps+ps-1); this call's
     rows go to scratch pages after them through ``bsp_write_kv``.
-    ``kv_split`` defaults to 256 keys per chunk for one-row decode, else 0.
+    ``kv_split`` defaults to -1: the plan picks the chunk per step (the
+    smallest multiple of 64 keys whose work items fill one round of the chip).
     """
     from synth import paged_from_rows  # layout only
 
@@ -201,7 +202,7 @@ def upload_cached_prefix(inp, device="cuda", page_size: int = 32, key_bucket: in
     cache_pages = -(-rows // ps)
     new_pages = -(-Sq // ps)
     num_pages = cache_pages + new_pages
-    split = (256 if Sq == 1 else 0) if kv_split is None else kv_split
+    split = -1 if kv_split is None else kv_split
     mk = lambda **kw: B.make_desc(Hq, Hkv, D, ps, num_pages, inp.dtype, **kw)  # noqa: E731
     d_cache = mk(key_bucket=key_bucket, max_cache_rows=rows, kv_split=split)
     d_new = mk(mask=B.BSP_MASK_CAUSAL if causal else B.BSP_MASK_NONE)

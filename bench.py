@@ -48,8 +48,16 @@ WORKLOADS = {
     "mixed": "mixed step: the qwen3_0p6b beam step (64 requests x beam 30, prompts U{400..600}, "
              "tails U{0..4}) plus 4 newly arrived requests whose prompts U{400..600} run as "
              "whole-prompt chunks (write + causal prefill) beside it on a second stream",
+    "cached_decode": "masked cached-prefix decode (beam 1): 24 Q / 8 KV heads, head_dim 128, fp16, "
+                     "10368-row allocation with all 10368 rows valid, 1 new row; the key range is "
+                     "split into chunks the plan picks (kv_split = -1) and merged",
+    "cached_prefill": "masked cached-prefix prefill (beam 1): 24 Q / 8 KV heads, head_dim 128, "
+                      "fp16, 10368 valid cached rows plus 2000 new prompt rows (causal)",
 }
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+CACHED_ROWS = 10368
+CACHED_PREFILL_ROWS = 2000
 PREFILL_SHAPE = dict(batch=8, chunk_range=(1500, 2500), cached_range=(0, 0))
 MIXED_CTX_SHAPE = dict(batch=4, chunk_range=(400, 600), cached_range=(0, 0))
 
@@ -345,6 +353,144 @@ def bench_mixed(args, torch, synth, B, S) -> dict:
     return res
 
 
+def cached_work(L: int, Sq: int, Hq: int, Hkv: int, D: int, e: int):
+    """FLOPs and algorithmic bytes of one cached-prefix call: L valid cached rows
+    (K+V read once per KV head) and Sq new rows (written, read), each new row i
+    attending L + i + 1 keys; Q read, O written, fp32 partials not counted."""
+    keys = Sq * L + Sq * (Sq + 1) // 2
+    flops = 4 * keys * Hq * D
+    nbytes = (L + Sq) * Hkv * D * e * 2 + Sq * Hkv * D * e * 2 + 2 * Sq * Hq * D * e
+    return flops, nbytes
+
+
+def bench_cached(args, torch, synth, B, S, prefill: bool) -> dict:
+    """The masked cached-prefix call: bsp_write_kv + bsp_prefix_attn (cache chunks)
+    + bsp_prefix_attn (new rows) + bsp_merge, rotating over layer copies."""
+    import oracle
+
+    dev = "cuda"
+    Sq = CACHED_PREFILL_ROWS if prefill else 1
+    L = CACHED_ROWS
+    inp = synth.make_cached_prefix(args.seed, valid_rows=L, q_len=Sq, garbage="unit")
+    Hq, D = inp.q.shape[1], inp.q.shape[2]
+    Hkv = inp.cache_k.shape[1]
+    flops, nbytes = cached_work(L, Sq, Hq, Hkv, D, EBYTES[inp.dtype])
+
+    def copies_for(split):
+        base = S.upload_cached_prefix(inp, dev, kv_split=split)
+        pool = base.k_pool.numel() * base.k_pool.element_size() * 2
+        layers = args.layers or max(2, int(np.ceil(1.0e9 / pool)))
+        cs = [base]
+        for _ in range(layers - 1):
+            c = S.CachedPrefixDevice(**{**base.__dict__})
+            c.k_pool = base.k_pool.clone()
+            c.v_pool = base.v_pool.clone()
+            c.q = base.q.clone()
+            cs.append(c)
+        S.plan_cached_prefix(base)
+        for c in cs[1:]:
+            c.o_part, c.lse_part, c.out, c.lse_out, c.n_split = (
+                base.o_part.clone(), base.lse_part.clone(), base.out.clone(),
+                base.lse_out.clone(), base.n_split)
+        return base, cs, layers
+
+    main_stream = torch.cuda.current_stream()
+    res_t = {}
+    for name, split in (("auto", -1), ("fixed_256", 256)):
+        base, cs, layers = copies_for(split)
+
+        def sync():
+            B.bsp_check(base.plan_cache)
+
+        # The four launches of a call, through the C entry points with their
+        # arguments marshalled once per layer copy (the Python wrapper costs more
+        # than the GPU work of a one-row call).
+        lib = B.load_library()
+        sh = main_stream.cuda_stream
+        ns = base.n_split
+        hd = base.num_kv_heads * base.head_dim
+        rows = base.q_len
+        calls = []
+        for c in cs:
+            calls.append((
+                (lib.bsp_write_kv, (c.plan_new.handle, c.new_k.data_ptr(), c.new_v.data_ptr(), hd,
+                                    c.slots.data_ptr(), rows, c.k_pool.data_ptr(),
+                                    c.v_pool.data_ptr(), sh)),
+                (lib.bsp_prefix_attn, (c.plan_cache.handle, c.q.data_ptr(), c.k_pool.data_ptr(),
+                                       c.v_pool.data_ptr(), c.o_part.data_ptr(),
+                                       c.lse_part.data_ptr(), sh)),
+                (lib.bsp_prefix_attn, (c.plan_new.handle, c.q.data_ptr(), c.k_pool.data_ptr(),
+                                       c.v_pool.data_ptr(), c.o_part[ns].data_ptr(),
+                                       c.lse_part[ns].data_ptr(), sh)),
+                (lib.bsp_merge, (rows, base.num_q_heads, base.head_dim, ns + 1,
+                                 c.o_part.data_ptr(), c.lse_part.data_ptr(),
+                                 rows * base.num_q_heads * base.head_dim, rows * base.num_q_heads,
+                                 c.out.data_ptr(), B.DTYPE_CODE[base.dtype], c.lse_out.data_ptr(),
+                                 sh))))
+
+        def call(i):
+            for fn, a in calls[i % layers]:
+                if fn(*a) != 0:
+                    raise RuntimeError(B.load_library().bsp_last_error().decode())
+
+        def cache_seg(i):
+            fn, a = calls[i % layers][1]
+            if fn(*a) != 0:
+                raise RuntimeError(B.load_library().bsp_last_error().decode())
+
+        sec, _ = _timed_loop(torch, call, args.steps, args.warmup,
+                             args.warm_seconds if name == "auto" else 0.2, main_stream, sync)
+        _, seg_ms = _timed_loop(torch, cache_seg, args.steps, args.warmup, 0.0, main_stream, sync)
+        res_t[name] = dict(ms=sec / args.steps * 1e3, seg_ms=seg_ms, n_split=base.n_split,
+                           split_keys=base.plan_cache.split_keys, layers=layers)
+        del cs, base
+    a = res_t["auto"]
+    seg_bytes = L * Hkv * D * EBYTES[inp.dtype] * 2 + Sq * Hq * D * EBYTES[inp.dtype]
+    if prefill:
+        seg_flops = 4 * Sq * L * Hq * D
+        achieved = seg_flops / (a["seg_ms"] * 1e-3) / 1e12
+        roof = {"kernel": "prefix_mfma_kernel<MODE 0> (bsp_prefix_attn, cache chunks)",
+                "bound": "mfma", "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / MFMA_F16_PEAK_TFLOPS, "traffic": None,
+                "avg_launch_us": a["seg_ms"] * 1e3, "flops_per_launch": seg_flops}
+    else:
+        achieved = seg_bytes / (a["seg_ms"] * 1e-3) / 1e9
+        roof = {"kernel": "prefix_mfma_kernel<MODE 0> (bsp_prefix_attn, cache chunks)",
+                "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                "avg_launch_us": a["seg_ms"] * 1e3, "alg_bytes_per_launch": seg_bytes}
+    cfg = "cached_prefill" if prefill else "cached_decode"
+    res = {
+        "metric": "masked cached-prefix calls/s per layer (write + cache chunks + new rows + merge)",
+        "value": 1e3 / a["ms"], "unit": "calls/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": a["ms"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": inp.dtype, "data": "synthetic",
+        "config": {"workload": WORKLOADS[cfg], "name": cfg, "valid_rows": L, "new_rows": Sq,
+                   "layers_rotated": a["layers"], "chunks": a["n_split"],
+                   "chunk_keys": a["split_keys"], "flops": flops, "alg_bytes": nbytes,
+                   "fixed_256_chunks": res_t["fixed_256"]["n_split"],
+                   "fixed_256_ms_per_step": res_t["fixed_256"]["ms"],
+                   "fixed_256_cache_segment_us": res_t["fixed_256"]["seg_ms"] * 1e3},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+        n = Sq if Sq <= 16 else 16
+        small = synth.make_cached_prefix(args.seed, valid_rows=L, q_len=n, garbage="unit")
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < args.cpu_budget / 2 or reps == 0:
+            oracle.cached_prefix_attention(small)
+            reps += 1
+        t = (time.perf_counter() - t0) / reps * (Sq / n)
+        threads = max([int(x.get("num_threads", 1)) for x in threadpool_info()] or [1])
+        res["cpu_baseline"] = {"value": 1.0 / t, "unit": "calls/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": f"the first {n} of {Sq} new rows over the same "
+                                         f"{L} cached rows, {reps} passes, scaled by rows"}
+    return res
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -381,6 +527,10 @@ def main() -> None:
     if args.config in ("prefill", "mixed"):
         fn = bench_prefill if args.config == "prefill" else bench_mixed
         print(json.dumps(fn(args, torch, synth, B, S)), flush=True)
+        return
+    if args.config in ("cached_decode", "cached_prefill"):
+        res = bench_cached(args, torch, synth, B, S, args.config == "cached_prefill")
+        print(json.dumps(res), flush=True)
         return
     dev = "cuda"
     inp = synth.make_beam_step(args.config, args.seed, garbage="unit")

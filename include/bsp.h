@@ -95,7 +95,12 @@ typedef struct {
   int32_t mask;           /* bsp_mask_t of the query rows (q_len > 1)                 */
   int32_t kv_split;       /* 0: one pass over the shared keys; > 0: split them into
                              chunks of this many keys (a multiple of 64), each
-                             giving its own partial (o, lse) to merge afterwards      */
+                             giving its own partial (o, lse) to merge afterwards;
+                             -1: bsp_plan picks the chunk per step, the smallest
+                             multiple of 64 keys whose work items (request, KV
+                             head, chunk, query tile) fit one round of 512
+                             workgroups (two per CU), no split if none is smaller
+                             than the longest key range (bsp_prefix_attn only)      */
 } bsp_layer_desc_t;
 
 typedef struct bsp_plan_s* bsp_plan_t;
@@ -159,8 +164,11 @@ bsp_status_t bsp_plan(bsp_plan_t plan, int32_t B, int32_t W, int32_t q_len,
                       size_t workspace_bytes, hipStream_t stream);
 
 /* Number of partial states bsp_prefix_attn writes for the current plan (1 when
- * kv_split is 0), and the tail length each beam is padded to. -1 if unplanned. */
+ * kv_split is 0), the keys per split (0: one pass; the chosen chunk when
+ * kv_split is -1), and the tail length each beam is padded to. -1 if
+ * unplanned. */
 int32_t bsp_plan_num_splits(bsp_plan_t plan);
+int32_t bsp_plan_split_keys(bsp_plan_t plan);
 int32_t bsp_plan_tail_len(bsp_plan_t plan);
 
 /*

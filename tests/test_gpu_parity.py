@@ -37,7 +37,7 @@ def _applied(inp):
 # ------------------------------------------------------------------ merge
 
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16", "f16"])
-@pytest.mark.parametrize("n_parts", [1, 2, 5])
+@pytest.mark.parametrize("n_parts", [1, 2, 5, 13, 55])
 def test_merge_matches_oracle(out_dtype, n_parts):
     say(f"merge out={out_dtype} parts={n_parts}")
     rng = np.random.default_rng(n_parts)
@@ -49,6 +49,8 @@ def test_merge_matches_oracle(out_dtype, n_parts):
     o[0, :5] = 0.0
     o[:, 5:7] = 0.0
     ref_o, ref_l = oracle.merge_states(list(o), list(lse))
+    o[0, :5] = np.nan                      # an empty part's o is never used
+    o[:, 5:7] = np.inf
     og = torch.from_numpy(o).to(DEV)
     lg = torch.from_numpy(lse).to(DEV)
     out = torch.empty((rows, heads, D), device=DEV, dtype=S.TORCH_DTYPE[out_dtype])
@@ -59,6 +61,31 @@ def test_merge_matches_oracle(out_dtype, n_parts):
     tol_o = TOL[out_dtype][0]
     o_gpu = out.float().cpu().numpy()
     assert np.abs(o_gpu - ref_o).max() <= tol_o
+    l_gpu = lout.cpu().numpy()
+    fin = np.isfinite(ref_l)
+    assert np.array_equal(np.isneginf(l_gpu), ~fin)
+    assert np.abs(l_gpu[fin] - ref_l[fin]).max() <= 1e-5
+
+
+@pytest.mark.parametrize("D,n_parts", [(64, 20), (96, 41), (128, 54), (256, 20)])
+def test_merge_one_row_many_parts(D, n_parts):
+    """A split one-row decode: 1 row x 24 heads and dozens of parts (the
+    workgroup-per-head merge), empty parts holding NaN."""
+    rng = np.random.default_rng(D + n_parts)
+    o = rng.standard_normal((n_parts, 1, 24, D)).astype(np.float32)
+    lse = (rng.standard_normal((n_parts, 1, 24)) * 3).astype(np.float32)
+    lse[::3, :, :5] = -np.inf
+    lse[:, :, 7] = -np.inf                 # every part empty for one head
+    o[lse == -np.inf] = 0.0
+    ref_o, ref_l = oracle.merge_states(list(o), list(lse))
+    o[lse == -np.inf] = np.nan
+    og = torch.from_numpy(o).to(DEV)
+    lg = torch.from_numpy(lse).to(DEV)
+    out = torch.empty((1, 24, D), device=DEV, dtype=torch.bfloat16)
+    lout = torch.empty((1, 24), device=DEV)
+    B.bsp_merge(1, 24, D, n_parts, og, lg, 24 * D, 24, out, "bf16", lout)
+    torch.cuda.synchronize()
+    assert np.abs(out.float().cpu().numpy() - ref_o).max() <= TOL["bf16"][0]
     l_gpu = lout.cpu().numpy()
     fin = np.isfinite(ref_l)
     assert np.array_equal(np.isneginf(l_gpu), ~fin)
@@ -226,13 +253,18 @@ def _cached_small(seed, L, q_len, **kw):
     return synth.make_cached_prefix(seed, valid_rows=L, q_len=q_len, **kw)
 
 
+@pytest.mark.parametrize("split", [256, -1])
 @pytest.mark.parametrize("L", CACHED_L)
-def test_cached_prefix_decode_matches_oracle(L):
+def test_cached_prefix_decode_matches_oracle(L, split):
+    """Fixed 256-key chunks, and the chunk the plan picks (kv_split = -1)."""
     R = oracle.bucket_rows(L, 256, 10368)
     inp = synth.make_cached_prefix(L % 7, valid_rows=L, q_len=1, nan_from_row=R)
-    say(f"cached decode L={L} R={R}")
-    c = S.upload_cached_prefix(inp, DEV)
+    c = S.upload_cached_prefix(inp, DEV, kv_split=split)
     S.plan_cached_prefix(c)
+    sk = c.plan_cache.split_keys
+    say(f"cached decode L={L} R={R} split={split}: {c.n_split} chunks of {sk} keys")
+    if split > 0:
+        assert sk == split
     S.run_cached_prefix(c)
     B.bsp_check(c.plan_cache)
     B.bsp_check(c.plan_new)
@@ -240,19 +272,22 @@ def test_cached_prefix_decode_matches_oracle(L):
     assert_close(c.out.reshape(1, 24, 128), c.lse_out.reshape(1, 24), o, lse, "f16",
                  f"decode L={L}")
     # every split partial against the oracle's partial over the same key chunk
+    step = sk if sk > 0 else max(L, 1)
     for sp in range(c.n_split):
-        po, pl = oracle.cached_prefix_partial(inp, "cache", key_range=(256 * sp, 256 * (sp + 1)))
+        po, pl = oracle.cached_prefix_partial(inp, "cache", key_range=(step * sp, step * (sp + 1)))
         assert_close(c.o_part[sp], c.lse_part[sp], po, pl, "f16", f"decode L={L} split {sp}")
 
 
-@pytest.mark.parametrize("L,Sq,causal", [(0, 37, True), (300, 64, True), (777, 200, True),
-                                          (1024, 130, False), (513, 1, True)])
-def test_cached_prefix_prefill_matches_oracle(L, Sq, causal):
+@pytest.mark.parametrize("L,Sq,causal,split", [(0, 37, True, 0), (300, 64, True, 0),
+                                                (777, 200, True, 0), (1024, 130, False, 0),
+                                                (513, 1, True, 256), (777, 200, True, -1),
+                                                (1024, 130, False, -1), (900, 3, True, -1)])
+def test_cached_prefix_prefill_matches_oracle(L, Sq, causal, split):
     R = oracle.bucket_rows(L, 256, 1024)
     inp = synth.make_cached_prefix(Sq, valid_rows=L, q_len=Sq, max_cache_rows=1024,
                                    nan_from_row=R)
-    say(f"cached prefill L={L} Sq={Sq} causal={causal}")
-    c = S.upload_cached_prefix(inp, DEV, kv_split=0 if Sq > 1 else 256, causal=causal)
+    c = S.upload_cached_prefix(inp, DEV, kv_split=split, causal=causal)
+    say(f"cached prefill L={L} Sq={Sq} causal={causal} split={split}")
     S.plan_cached_prefix(c)
     S.run_cached_prefix(c)
     B.bsp_check(c.plan_cache)

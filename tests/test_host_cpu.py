@@ -356,3 +356,26 @@ def test_prefill_plan_rejects_bad_input():
     assert status(lambda: B.bsp_plan_prefill(plan, 4, inp.q_len, inp.cached_len,
                                              inp.block_tables)) == "BSP_ERR_ARG"
     B.bsp_plan_prefill(plan, 3, inp.q_len, inp.cached_len, inp.block_tables)
+
+
+# ------------------------------------------ automatic key split (kv_split = -1)
+
+@pytest.mark.parametrize("L,Sq,want", [
+    (10368, 1, 54),    # 192-key chunks: 54 x 8 KV heads = 432 items <= 512
+    (2000, 1, 32),     # 64-key chunks fill 256 items; none smaller exists
+    (100, 1, 2),
+    (64, 1, 1),        # no chunk is shorter than the whole range
+    (0, 1, 1),
+    (10368, 2000, 2),  # 2000 x 3 rows = 32 tiles of 192 per KV head: 2 chunks
+])
+def test_auto_split_fills_one_round(L, Sq, want):
+    """kv_split = -1: the smallest multiple of 64 keys whose (request, KV head,
+    chunk, query tile) items fit 512 workgroups."""
+    desc = B.make_desc(24, 8, 128, 32, 400, "f16", key_bucket=256, max_cache_rows=10368,
+                       kv_split=-1)
+    nb = 10368 // 32
+    plan = B.Plan(desc, 1, 1, nb, 10368, 2000, host_only=True)
+    bt = (np.arange(nb, dtype=np.int32) % 400).reshape(1, 1, nb)
+    Lh = np.array([L], np.int32)
+    B.bsp_plan(plan, 1, 1, Sq, Lh, Lh, bt)
+    assert plan.num_splits == want
