@@ -82,6 +82,8 @@ _SIGS = {
     "bsp_naive_beam_attn": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "bsp_decode_step": (_I32, [_P, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "bsp_plan_prefill": (_I32, [_P, _I32, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "bsp_mixed_step": (_I32, [_P, _P, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                              _P, _P]),
     "bsp_prefill_attn": (_I32, [_P, _P, _P, _P, _P, _P, _P]),
     "bsp_check": (_I32, [_P, _P]),
     "bsp_debug_plan_tables": (_I32, [_P, _P, _P, _P, _P, _P]),
@@ -274,6 +276,17 @@ def bsp_plan_prefill(plan: Plan, C: int, q_len, cached_len, block_tables, worksp
 def bsp_prefill_attn(plan: Plan, q, k_pool, v_pool, o_out, lse_out=None, stream=None) -> None:
     _check(load_library().bsp_prefill_attn(plan.handle, _ptr(q), _ptr(k_pool), _ptr(v_pool),
                                            _ptr(o_out), _ptr(lse_out), _stream(stream)))
+
+
+def bsp_mixed_step(gen: Plan, ctx: Plan, q, k_new, v_new, new_row_stride: int, k_pool, v_pool,
+                   block_tables, cache_indirection, o_out, lse_out, q_ctx, k_pool_ctx, v_pool_ctx,
+                   o_ctx, lse_ctx=None, stream=None) -> None:
+    _check(load_library().bsp_mixed_step(gen.handle, ctx.handle, _ptr(q), _ptr(k_new),
+                                         _ptr(v_new), new_row_stride, _ptr(k_pool), _ptr(v_pool),
+                                         _ptr(block_tables), _ptr(cache_indirection), _ptr(o_out),
+                                         _ptr(lse_out), _ptr(q_ctx), _ptr(k_pool_ctx),
+                                         _ptr(v_pool_ctx), _ptr(o_ctx), _ptr(lse_ctx),
+                                         _stream(stream)))
 
 
 def bsp_check(plan: Plan, stream=None) -> None:

@@ -640,45 +640,6 @@ bsp_status_t bsp_plan_prefill(bsp_plan_t pl, int32_t C, const int32_t* q_len_h,
   return ok();
 }
 
-bsp_status_t bsp_prefill_attn(bsp_plan_t pl, const void* q, const void* k_pool, const void* v_pool,
-                              void* o_out, float* lse_out, hipStream_t stream) {
-  bsp_status_t st = check_device_ready(pl);
-  if (st != BSP_OK) return st;
-  if (!pl->prefill) return fail(BSP_ERR_STALE_PLAN, "plan holds no prefill step: call bsp_plan_prefill");
-  const bsp_layer_desc_t& d = pl->desc;
-  if (d.dtype == BSP_F32) return fail(BSP_ERR_UNSUPPORTED, "bsp_prefill_attn is bf16/f16 only");
-  if (!q || !k_pool || !v_pool || !o_out) return fail(BSP_ERR_ARG, "null pointer");
-  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o_out))
-    return fail(BSP_ERR_ARG, "q, the pools and o_out must be 16-byte aligned");
-  bsp::PrefixParams p{};
-  p.q = q;
-  p.k_pool = k_pool;
-  p.v_pool = v_pool;
-  p.req = dev_req(pl);
-  p.pages = dev_pages(pl);
-  p.hdr = dev_header(pl);
-  p.items = reinterpret_cast<const int32_t*>(static_cast<char*>(pl->ws_d) + pl->items_off);
-  p.B = pl->B;
-  p.W = 1;
-  p.q_len = 1;
-  p.hq = d.num_q_heads;
-  p.hkv = d.num_kv_heads;
-  p.group = d.num_q_heads / d.num_kv_heads;
-  p.page_shift = pl->page_shift;
-  p.num_pages = d.num_pages;
-  p.n_split = 1;
-  p.split_keys = 0;
-  p.n_qtiles = 1;
-  p.causal = 1;
-  p.rows_total = pl->rows_total;
-  p.scale = d.sm_scale;
-  p.scale_log2e = d.sm_scale * 1.4426950408889634f;
-  bsp::FusedParams f{};
-  f.o_out = o_out;
-  f.lse_out = lse_out;
-  return after_launch(pl, bsp::launch_prefill(p, f, d.dtype, d.head_dim, pl->prefill_mb, pl->n_items, stream),
-                      "prefill launch", stream);
-}
 
 bsp_status_t bsp_write_kv(bsp_plan_t pl, const void* k_new, const void* v_new,
                           int64_t src_row_stride, const int32_t* slots_d, int32_t n, void* k_pool,
@@ -748,10 +709,16 @@ bsp_status_t bsp_prefix_attn(bsp_plan_t pl, const void* q, const void* k_pool, c
                       "prefix launch", stream);
 }
 
-bsp_status_t bsp_decode_step(bsp_plan_t pl, const void* q, const void* k_new, const void* v_new,
-                             int64_t new_row_stride, void* k_pool, void* v_pool,
-                             const int32_t* block_tables_d, const int32_t* cache_indirection_d,
-                             void* o_out, float* lse_out, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and kernel parameters of the fused beam step (bsp_decode_step).
+bsp_status_t decode_params(bsp_plan_s* pl, const void* q, const void* k_new, const void* v_new,
+                           int64_t new_row_stride, void* k_pool, void* v_pool,
+                           const int32_t* block_tables_d, const int32_t* cache_indirection_d,
+                           void* o_out, float* lse_out, bsp::PrefixParams& p,
+                           bsp::FusedParams& f) {
   bsp_status_t st = check_beam_ready(pl);
   if (st != BSP_OK) return st;
   const bsp_layer_desc_t& d = pl->desc;
@@ -770,8 +737,7 @@ bsp_status_t bsp_decode_step(bsp_plan_t pl, const void* q, const void* k_new, co
   if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) ||
       !aligned16(v_pool) || (reinterpret_cast<uintptr_t>(o_out) & 7u) != 0)
     return fail(BSP_ERR_ARG, "q, k_new, v_new and the pools must be 16-byte aligned, o_out 8-byte");
-  bsp::PrefixParams p{};
-  std::memset(&p, 0, sizeof(p));
+  p = bsp::PrefixParams{};
   p.q = q;
   p.k_pool = k_pool;
   p.v_pool = v_pool;
@@ -794,7 +760,7 @@ bsp_status_t bsp_decode_step(bsp_plan_t pl, const void* q, const void* k_new, co
   p.rows_total = pl->B * pl->W;
   p.scale = d.sm_scale;
   p.scale_log2e = d.sm_scale * 1.4426950408889634f;
-  bsp::FusedParams f;
+  f = bsp::FusedParams{};
   f.k_new = k_new;
   f.v_new = v_new;
   f.new_stride = new_row_stride;
@@ -818,8 +784,115 @@ bsp_status_t bsp_decode_step(bsp_plan_t pl, const void* q, const void* k_new, co
     f.pair_part = reinterpret_cast<float*>(ws + pl->pair_part_off);
     f.n_pairs = pl->n_pairs;
   }
+  return BSP_OK;
+}
+
+// Validation and kernel parameters of the context prefill (bsp_prefill_attn).
+bsp_status_t prefill_params(bsp_plan_s* pl, const void* q, const void* k_pool, const void* v_pool,
+                            void* o_out, float* lse_out, bsp::PrefixParams& p,
+                            bsp::FusedParams& f) {
+  bsp_status_t st = check_device_ready(pl);
+  if (st != BSP_OK) return st;
+  if (!pl->prefill)
+    return fail(BSP_ERR_STALE_PLAN, "plan holds no prefill step: call bsp_plan_prefill");
+  const bsp_layer_desc_t& d = pl->desc;
+  if (d.dtype == BSP_F32) return fail(BSP_ERR_UNSUPPORTED, "bsp_prefill_attn is bf16/f16 only");
+  if (!q || !k_pool || !v_pool || !o_out) return fail(BSP_ERR_ARG, "null pointer");
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o_out))
+    return fail(BSP_ERR_ARG, "q, the pools and o_out must be 16-byte aligned");
+  p = bsp::PrefixParams{};
+  p.q = q;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.req = dev_req(pl);
+  p.pages = dev_pages(pl);
+  p.hdr = dev_header(pl);
+  p.items = reinterpret_cast<const int32_t*>(static_cast<char*>(pl->ws_d) + pl->items_off);
+  p.B = pl->B;
+  p.W = 1;
+  p.q_len = 1;
+  p.hq = d.num_q_heads;
+  p.hkv = d.num_kv_heads;
+  p.group = d.num_q_heads / d.num_kv_heads;
+  p.page_shift = pl->page_shift;
+  p.num_pages = d.num_pages;
+  p.n_split = 1;
+  p.split_keys = 0;
+  p.n_qtiles = 1;
+  p.causal = 1;
+  p.rows_total = pl->rows_total;
+  p.scale = d.sm_scale;
+  p.scale_log2e = d.sm_scale * 1.4426950408889634f;
+  f = bsp::FusedParams{};
+  f.o_out = o_out;
+  f.lse_out = lse_out;
+  return BSP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+bsp_status_t bsp_decode_step(bsp_plan_t pl, const void* q, const void* k_new, const void* v_new,
+                             int64_t new_row_stride, void* k_pool, void* v_pool,
+                             const int32_t* block_tables_d, const int32_t* cache_indirection_d,
+                             void* o_out, float* lse_out, hipStream_t stream) {
+  bsp::PrefixParams p;
+  bsp::FusedParams f;
+  const bsp_status_t st = decode_params(pl, q, k_new, v_new, new_row_stride, k_pool, v_pool,
+                                        block_tables_d, cache_indirection_d, o_out, lse_out, p, f);
+  if (st != BSP_OK) return st;
+  const bsp_layer_desc_t& d = pl->desc;
   return after_launch(
       pl, bsp::launch_decode_step(p, f, d.dtype, d.head_dim, pl->rows_per_req, pl->tail_pad, stream),
+      "decode step launch", stream);
+}
+
+bsp_status_t bsp_prefill_attn(bsp_plan_t pl, const void* q, const void* k_pool, const void* v_pool,
+                              void* o_out, float* lse_out, hipStream_t stream) {
+  bsp::PrefixParams p;
+  bsp::FusedParams f;
+  const bsp_status_t st = prefill_params(pl, q, k_pool, v_pool, o_out, lse_out, p, f);
+  if (st != BSP_OK) return st;
+  const bsp_layer_desc_t& d = pl->desc;
+  return after_launch(pl, bsp::launch_prefill(p, f, d.dtype, d.head_dim, pl->prefill_mb, pl->n_items, stream),
+                      "prefill launch", stream);
+}
+
+bsp_status_t bsp_mixed_step(bsp_plan_t gen, bsp_plan_t ctx, const void* q, const void* k_new,
+                            const void* v_new, int64_t new_row_stride, void* k_pool, void* v_pool,
+                            const int32_t* block_tables_d, const int32_t* cache_indirection_d,
+                            void* o_out, float* lse_out, const void* q_ctx, const void* k_pool_ctx,
+                            const void* v_pool_ctx, void* o_ctx, float* lse_ctx,
+                            hipStream_t stream) {
+  if (gen == nullptr || ctx == nullptr) return fail(BSP_ERR_ARG, "null plan");
+  if (gen == ctx) return fail(BSP_ERR_ARG, "a mixed step needs two plans");
+  bsp::PrefixParams dp, pp;
+  bsp::FusedParams df, pf;
+  bsp_status_t st = decode_params(gen, q, k_new, v_new, new_row_stride, k_pool, v_pool,
+                                  block_tables_d, cache_indirection_d, o_out, lse_out, dp, df);
+  if (st != BSP_OK) return st;
+  st = prefill_params(ctx, q_ctx, k_pool_ctx, v_pool_ctx, o_ctx, lse_ctx, pp, pf);
+  if (st != BSP_OK) return st;
+  const bsp_layer_desc_t& d = gen->desc;
+  const bsp_layer_desc_t& dc = ctx->desc;
+  if (d.dtype != dc.dtype || d.head_dim != dc.head_dim)
+    return fail(BSP_ERR_ARG, "the two plans of a mixed step need the same dtype and head_dim");
+  if (bsp::mixed_step_supported(dp, df, d.dtype, d.head_dim, gen->rows_per_req, gen->tail_pad,
+                                ctx->prefill_mb)) {
+    const hipError_t e =
+        bsp::launch_mixed_step(dp, df, pp, pf, d.dtype, d.head_dim, ctx->n_items, stream);
+    st = after_launch(gen, e, "mixed step launch", stream);
+    if (st == BSP_OK && ctx->check_mode) st = bsp_check(ctx, stream);
+    return st;
+  }
+  // otherwise the context phase, then the beam step, on the stream
+  st = after_launch(ctx, bsp::launch_prefill(pp, pf, dc.dtype, dc.head_dim, ctx->prefill_mb,
+                                             ctx->n_items, stream),
+                    "prefill launch", stream);
+  if (st != BSP_OK) return st;
+  return after_launch(
+      gen, bsp::launch_decode_step(dp, df, d.dtype, d.head_dim, gen->rows_per_req, gen->tail_pad, stream),
       "decode step launch", stream);
 }
 

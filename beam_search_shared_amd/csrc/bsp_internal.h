@@ -174,6 +174,14 @@ constexpr int prefill_max_mb(int head_dim) { return head_dim == 256 ? 2 : 3; }
 constexpr int kFillBlocks = 512;
 hipError_t launch_prefill(const PrefixParams& p, const FusedParams& f, int dtype, int head_dim,
                           int mb, int n_items, hipStream_t s);
+// A mixed step in one launch (beam-step workgroups beside context workgroups):
+// one query block per wave on both sides, head_dim <= 128, the beam step's
+// tails in the LDS slot table and no balanced pairs.
+bool mixed_step_supported(const PrefixParams& dp, const FusedParams& df, int dtype, int head_dim,
+                          int rows_per_req, int tail_pad, int pre_mb);
+hipError_t launch_mixed_step(const PrefixParams& dp, const FusedParams& df, const PrefixParams& pp,
+                             const FusedParams& pf, int dtype, int head_dim, int n_pre_items,
+                             hipStream_t s);
 hipError_t launch_tail(const TailParams& p, int dtype, int head_dim, hipStream_t s);
 hipError_t launch_tail_slots(const TailParams& p, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, int out_dtype, hipStream_t s);

@@ -176,11 +176,19 @@ __device__ __forceinline__ int32_t resolve_fused_slot(const PrefixParams& p, con
 // causally, the chunk's rows up to its own; work items (request, query tile)
 // come from the plan's list and key tiles past a tile's last visible key are
 // never loaded; the output is written in the storage dtype.
+// MODE 4: a mixed step in one launch: each workgroup is either a MODE 1 item
+// of the beam step or a MODE 3 item of the context requests (`pre`), with
+// that part's parameters.
 template <typename T, int D, int MB, int KT, int NST, int MODE, bool PAIR>
-__global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma_kernel(PrefixParams p,
-                                                                                          FusedParams f) {
-  constexpr bool FUSED = MODE == 1 || MODE == 2;
-  constexpr bool PREFILL = MODE == 3;
+__device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int block, bool pre) {
+  // FUSED / PREFILL: the workgroup may be a beam-step / context item; `fused`
+  // and `is_pre` say which one it is.
+  constexpr bool FUSED = MODE == 1 || MODE == 2 || MODE == 4;
+  constexpr bool PREFILL = MODE == 3 || MODE == 4;
+  constexpr bool TAILS1 = MODE == 1 || MODE == 4;  // tails through the LDS slot table
+  const bool is_pre = MODE == 3 || (MODE == 4 && pre);
+  const bool fused = FUSED && !is_pre;
+  static_assert(MODE != 4 || (MB == 1 && !PAIR), "mixed steps take one query block per wave");
   static_assert(!PAIR || (MODE == 1 && MB <= kPairMaxMB), "pairs run in the fused step, MB <= 2");
   using V8 = typename Mfma<T>::V8;
   constexpr int NDS = D / 32;                       // contraction steps of S^T
@@ -195,7 +203,7 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
   static_assert(NST >= 2 && NST <= 4 && 2 * LPT < 64, "pipeline depth");
   __shared__ __attribute__((aligned(1024))) T lds_kv[NST][2][TILE];
   __shared__ int lds_pages[kPageWin];
-  __shared__ int lds_tail[MODE == 1 ? kTailSlots : 1];
+  __shared__ int lds_tail[TAILS1 ? kTailSlots : 1];
 
   // ---- work: one (request, KV head, key split, query tile) item; with
   // balanced pairs (PairInfo), one or two segments of a pair for one KV head.
@@ -205,7 +213,7 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
   int pair_idx = 0, pair_role = 0;
   WorkItem w;
   {
-    int bid = blockIdx.x;
+    int bid = block;
     if constexpr (PAIR) {
       // Every Y workgroup comes before every X workgroup in the grid, so an X
       // never waits for a Y that could not be dispatched yet.
@@ -231,7 +239,7 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
         sg_b0 = pr.b; sg_lo0 = 0; sg_hi0 = p.req[pr.b].valid;
         nseg = 1;
       }
-    } else if constexpr (PREFILL) {
+    } else if (PREFILL && is_pre) {
       w.g = bid % p.hkv;
       const int item = bid / p.hkv;
       sg_b0 = p.items[2 * item];
@@ -276,12 +284,12 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
   const int l4 = lane >> 4;
   const ReqInfo ri = p.req[w.b];
 
-  const int M = PREFILL ? ri.tail * p.group : p.W * p.q_len * p.group;
+  const int M = is_pre ? ri.tail * p.group : p.W * p.q_len * p.group;
   // Rows per wave: 16 per query block; in the fused step with one block per
   // wave and at most 32 (16) query rows per request, 8 (4) per wave, so that
   // all four waves share the beams' tails instead of two (one) of them. Lanes
   // past a wave's rows are treated like rows past M.
-  const int rpw = MODE == 1 && MB == 1 && p.n_qtiles == 1 ? (M <= 16 ? 4 : M <= 32 ? 8 : 16) : 16;
+  const int rpw = TAILS1 && !is_pre && MB == 1 && p.n_qtiles == 1 ? (M <= 16 ? 4 : M <= 32 ? 8 : 16) : 16;
   const int row0 = w.qt * (64 * MB) + wave * (rpw * MB);
   const bool wave_active = row0 < M;
   const int row_end = min(M, row0 + rpw * MB);  // this wave's rows: [row0, row_end)
@@ -300,7 +308,7 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
   // all page lookups, then the table entries (the host checked that the table
   // holds them).
   constexpr int TR = 4;
-  const int n_sl = MODE == 1 && finishes ? nbt * ri.tail : 0;
+  const int n_sl = TAILS1 && fused && finishes ? nbt * ri.tail : 0;
   auto sl_parents = [&](int base, int32_t (&src)[TR]) {
 #pragma unroll
     for (int i = 0; i < TR; ++i) {
@@ -352,7 +360,7 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
   // overlap gains: measured at MB = 2, not free at MB = 3.)
   constexpr bool DEFER = MODE == 1 && MB == 1;
   int32_t t_src[TR], t_page[TR];
-  if constexpr (MODE == 1 && !DEFER) {
+  if constexpr (TAILS1 && !DEFER) {
     for (int base = 0; base < n_sl; base += 256 * TR) {
       sl_parents(base, t_src);
       sl_pages(base, t_src, t_page);
@@ -371,7 +379,7 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
       const int hh = r % p.group;
       const int t = r / p.group;
       int64_t qrow;
-      if constexpr (PREFILL) {  // packed rows; chunk position t sees keys up to valid - rows + t
+      if (PREFILL && is_pre) {  // packed rows; chunk position t sees keys up to valid - rows + t
         qrow = ((int64_t)ri.q_off + t) * p.hq + w.g * p.group + hh;
         climit[qb] = ri.valid - ri.tail + t;
       } else {
@@ -518,10 +526,10 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
   constexpr bool ROT = MB >= 2 && NST >= 4;
   constexpr int AHEAD = ROT ? NST - 2 : NST - 1;  // tiles in flight beyond the one computed
 
-  const int n_tail = FUSED ? ri.tail : 0;
+  const int n_tail = fused ? ri.tail : 0;
   // prefill: the smallest causal limit among this wave's rows (its first row);
   // a key tile at or below it needs no mask
-  const int c_first = PREFILL ? ri.valid - ri.tail + row0 / p.group : 0;
+  const int c_first = is_pre ? ri.valid - ri.tail + row0 / p.group : 0;
   const int win_first = w.k_lo / keys_per_win;
   const int n_win = w.k_hi > w.k_lo ? (w.k_hi - 1) / keys_per_win - win_first + 1 : 0;
 
@@ -626,7 +634,7 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
       f32x4 sacc[NKB][MB];
       s_tile(lds_kv[t % NST][0], sacc);
       if (ROT && t > 0) o_tile(lds_kv[(t - 1) % NST][1], pb);
-      softmax_tile(sacc, (t0 + KT <= w.k_hi) && (PREFILL ? t0 + KT - 1 <= c_first : !p.causal),
+      softmax_tile(sacc, (t0 + KT <= w.k_hi) && (is_pre ? t0 + KT - 1 <= c_first : !p.causal),
                    [&](int qb, int kk) { return (t0 + kk < w.k_hi) & (t0 + kk <= climit[qb]); }, pb);
       if (!ROT) o_tile(lds_kv[t % NST][1], pb);
     }
@@ -725,7 +733,7 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
   // round trips, measured slower.)
   const int kw_lo = (w.qt * rt + p.group - 1) / p.group;
   const int kw_hi = min(p.W, ((w.qt + 1) * rt + p.group - 1) / p.group);
-  const int n_tw = FUSED && n_tail > 0 && finishes ? (kw_hi - kw_lo) * CPR : 0;
+  const int n_tw = fused && n_tail > 0 && finishes ? (kw_hi - kw_lo) * CPR : 0;
   auto tw_load = [&](int base, auto& page, auto& kd, auto& vd) {
     constexpr int N = (int)(sizeof(page) / sizeof(int32_t));
 #pragma unroll
@@ -764,7 +772,7 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
   // u = (beam - kb_first) * n_tail + t) in 16-key sub-tiles, double-buffered
   // in its quarter of the now idle tile ring, with no workgroup barrier. A
   // tail key is visible only to its own beam's query rows.
-  if constexpr (MODE == 1) {
+  if constexpr (TAILS1) {
     __syncthreads();  // every wave is done with the ring; the slot table is visible
     if (n_tail > 0 && wave_active) {
       constexpr int KW = 16;                                       // keys per sub-tile
@@ -1003,7 +1011,7 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
     if (!wave_active || r >= row_end) continue;
     const int hh = r % p.group;
     const int t = r / p.group;
-    const int64_t grow = PREFILL ? (int64_t)ri.q_off + t
+    const int64_t grow = is_pre ? (int64_t)ri.q_off + t
                                  : ((int64_t)w.b * p.W + t / p.q_len) * p.q_len + t % p.q_len;
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const float lse = lt > 0.f ? mrow[qb] * p.scale + __logf(lt) : -INFINITY;
@@ -1041,7 +1049,40 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma
     }
   }
   }  // segments
+}
 
+template <typename T, int D, int MB, int KT, int NST, int MODE, bool PAIR>
+__global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma_kernel(PrefixParams p,
+                                                                                          FusedParams f) {
+  prefix_body<T, D, MB, KT, NST, MODE, PAIR>(p, f, blockIdx.x, false);
+}
+
+// A mixed step in one launch: n_dec beam-step workgroups (dp, df) and n_pre
+// context workgroups (pp, pf). Chunks of 256 of each alternate while both
+// last, so that the first round puts a beam-step workgroup (bandwidth-bound)
+// and a context workgroup (latency- and matrix-bound) side by side on a CU
+// rather than one kind after the other.
+template <typename T, int D, int KT, int NST>
+__global__ __launch_bounds__(256, (prefix_min_blocks<D, 1>())) void mixed_step_kernel(
+    PrefixParams dp, FusedParams df, PrefixParams pp, FusedParams pf, int n_dec, int n_pre) {
+  constexpr int C = 256;
+  int rem = blockIdx.x, done_d = 0, done_p = 0;
+  bool pre = false;
+  int idx = 0;
+  for (int c = 0;; ++c) {  // at most (n_dec + n_pre) / 256 + 2 chunks; rem < n_dec + n_pre
+    const bool dec_turn = done_d < n_dec && ((c & 1) == 0 || done_p >= n_pre);
+    const int cnt = dec_turn ? min(C, n_dec - done_d) : min(C, n_pre - done_p);
+    if (rem < cnt) {
+      pre = !dec_turn;
+      idx = (dec_turn ? done_d : done_p) + rem;
+      break;
+    }
+    rem -= cnt;
+    if (dec_turn) done_d += cnt;
+    else done_p += cnt;
+  }
+  // one copy of the body; the parameters are picked per workgroup
+  prefix_body<T, D, 1, KT, NST, 4, false>(pre ? pp : dp, pre ? pf : df, idx, pre);
 }
 
 // f32: one wave per query row, lanes split head_dim, keys in chunks of 8.
@@ -1205,7 +1246,7 @@ hipError_t launch_prefill(const PrefixParams& p, const FusedParams& f, int dtype
   const unsigned blocks = (unsigned)(n_items * p.hkv);
   if (blocks == 0) return hipSuccess;
 #define BSP_PRE(TT, DD, MBB, KTT) \
-  prefix_mfma_kernel<TT, DD, MBB, KTT, 4, 3, false><<<blocks, 256, 0, s>>>(p, f)
+  prefix_mfma_kernel<TT, DD, MBB, KTT, (DD == 256 && MBB == 1 ? 2 : 4), 3, false><<<blocks, 256, 0, s>>>(p, f)
 #define BSP_PRE_T(TT)                                      \
   if (head_dim == 64) {                                    \
     if (mb == 1) BSP_PRE(TT, 64, 1, 64);                   \
@@ -1228,6 +1269,35 @@ hipError_t launch_prefill(const PrefixParams& p, const FusedParams& f, int dtype
   }
 #undef BSP_PRE_T
 #undef BSP_PRE
+  return hipGetLastError();
+}
+
+bool mixed_step_supported(const PrefixParams& dp, const FusedParams& df, int dtype, int head_dim,
+                          int rows_per_req, int tail_pad, int pre_mb) {
+  if (dtype == BSP_F32 || head_dim > 128 || pre_mb != 1) return false;
+  if (pick_mb(head_dim, rows_per_req) != 1 || dp.n_qtiles != 1) return false;
+  if (df.pairs != nullptr && df.n_pairs > 0) return false;
+  const int nbt_max = min(dp.W, 63 / dp.group + 2);
+  return (int64_t)nbt_max * tail_pad <= kTailSlots;  // the beam step's tails in the LDS table
+}
+
+hipError_t launch_mixed_step(const PrefixParams& dp, const FusedParams& df, const PrefixParams& pp,
+                             const FusedParams& pf, int dtype, int head_dim, int n_pre_items,
+                             hipStream_t s) {
+  const int n_dec = dp.B * dp.hkv * dp.n_qtiles;
+  const int n_pre = n_pre_items * pp.hkv;
+  const unsigned blocks = (unsigned)(n_dec + n_pre);
+  if (blocks == 0) return hipSuccess;
+#define BSP_MIX(TT, DD, KTT) \
+  mixed_step_kernel<TT, DD, KTT, 4><<<blocks, 256, 0, s>>>(dp, df, pp, pf, n_dec, n_pre)
+  if (dtype == BSP_F16) {  // head_dim 64 or 128 (mixed_step_supported)
+    if (head_dim == 64) BSP_MIX(_Float16, 64, 64);
+    else BSP_MIX(_Float16, 128, 32);
+  } else {
+    if (head_dim == 64) BSP_MIX(__bf16, 64, 64);
+    else BSP_MIX(__bf16, 128, 32);
+  }
+#undef BSP_MIX
   return hipGetLastError();
 }
 

@@ -320,6 +320,18 @@ def run_prefill(c: PrefillDevice, stream=None, write: bool = True) -> None:
     B.bsp_prefill_attn(c.plan, c.q, c.k_pool, c.v_pool, c.out, c.lse_out, stream)
 
 
+def run_mixed_step_fused(ctx: PrefillDevice, gen: BeamStepDevice, stream=None) -> None:
+    """One mixed step through bsp_mixed_step: the context chunks' KV write, then
+    the prefill and the beam step in one launch (two when the shapes do not
+    allow it)."""
+    B.bsp_write_kv(ctx.plan, ctx.new_k, ctx.new_v, ctx.num_kv_heads * ctx.head_dim, ctx.slots,
+                   ctx.rows, ctx.k_pool, ctx.v_pool, stream)
+    B.bsp_mixed_step(gen.plan, ctx.plan, gen.q, gen.k_new_beams, gen.v_new_beams,
+                     gen.num_kv_heads * gen.head_dim, gen.k_pool, gen.v_pool, gen.block_tables,
+                     gen.cache_indirection, gen.out, gen.lse_out, ctx.q, ctx.k_pool, ctx.v_pool,
+                     ctx.out, ctx.lse_out, stream)
+
+
 def run_mixed_step(ctx: PrefillDevice, gen: BeamStepDevice, stream=None,
                    ctx_stream=None) -> None:
     """One mixed step: the context requests' prefill and the generation requests'

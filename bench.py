@@ -47,7 +47,8 @@ WORKLOADS = {
                "as whole-prompt chunks, causal",
     "mixed": "mixed step: the qwen3_0p6b beam step (64 requests x beam 30, prompts U{400..600}, "
              "tails U{0..4}) plus 4 newly arrived requests whose prompts U{400..600} run as "
-             "whole-prompt chunks (write + causal prefill) beside it on a second stream",
+             "whole-prompt chunks (KV write, then causal prefill beside the beam step in one "
+             "launch)",
     "cached_decode": "masked cached-prefix decode (beam 1): 24 Q / 8 KV heads, head_dim 128, fp16, "
                      "10368-row allocation with all 10368 rows valid, 1 new row; the key range is "
                      "split into chunks the plan picks (kv_split = -1) and merged",
@@ -317,11 +318,15 @@ def bench_mixed(args, torch, synth, B, S) -> dict:
                                                                gcopies[i % layers], main, cs),
                              args.steps, args.warmup, args.warm_seconds, main, sync)
         res_t[name] = sec / args.steps * 1e3
+    sec, _ = _timed_loop(torch, lambda i: S.run_mixed_step_fused(ccopies[i % layers],
+                                                                 gcopies[i % layers], main),
+                         args.steps, args.warmup, 0.0, main, sync)
+    res_t["one_launch"] = sec / args.steps * 1e3
     sec_g, gen_ms = _timed_loop(torch, lambda i: S.run_decode_step(gcopies[i % layers], main),
                                 args.steps, args.warmup, 0.0, main, sync)
     sec_c, _ = _timed_loop(torch, lambda i: S.run_prefill(ccopies[i % layers], main),
                            args.steps, args.warmup, 0.0, main, sync)
-    ms = res_t["two_streams"]
+    ms = res_t["one_launch"]
     achieved = step_bytes / (gen_ms * 1e-3) / 1e9
     res = {
         "metric": "mixed steps/s per layer (context prefill + beam decode step)",
@@ -330,9 +335,11 @@ def bench_mixed(args, torch, synth, B, S) -> dict:
         "vs_baseline": None, "dtype": gen.dtype, "data": "synthetic",
         "config": {"workload": WORKLOADS["mixed"], "name": "mixed",
                    "context_prompts": ctx.q_len.tolist(), "layers_rotated": layers,
-                   "step": "bsp_write_kv + bsp_prefill_attn (second stream) || bsp_decode_step",
-                   "one_stream_ms_per_step": res_t["one_stream"],
-                   "two_streams_ms_per_step": ms,
+                   "step": "bsp_write_kv (context rows) + bsp_mixed_step (context and beam-step "
+                           "workgroups in one launch)",
+                   "one_launch_ms_per_step": ms,
+                   "separate_launches_one_stream_ms_per_step": res_t["one_stream"],
+                   "separate_launches_two_streams_ms_per_step": res_t["two_streams"],
                    "decode_step_alone_ms": sec_g / args.steps * 1e3,
                    "context_phase_alone_ms": sec_c / args.steps * 1e3,
                    "context_flops": flops, "context_alg_bytes": ctx_bytes,

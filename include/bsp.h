@@ -298,6 +298,28 @@ bsp_status_t bsp_prefill_attn(bsp_plan_t plan, const void* q, const void* k_pool
                               hipStream_t stream);
 
 /*
+ * A whole mixed step of one layer (PR #21738, mixed-batches commit): the beam
+ * step of the generation requests (`gen`, planned by bsp_plan; the arguments of
+ * bsp_decode_step) and the causal prefill of the context requests (`ctx`,
+ * planned by bsp_plan_prefill; the arguments of bsp_prefill_attn, whose chunk
+ * rows the caller has written with bsp_write_kv on this stream before). The
+ * two parts touch disjoint rows and may share one pool (pass it twice). When
+ * both parts take one 16-row query block per wave (the beam step's W * G <= 64
+ * rows per request, the prefill plan's 64-row items), head_dim <= 128, the
+ * beam step's tails fit its slot table and it has no balanced pairs, this is
+ * one launch in which beam-step and context workgroups share the CUs (the
+ * first bandwidth-bound, the second latency- and matrix-bound); otherwise the
+ * prefill, then the beam step, on the stream. Results and errors as for the
+ * two calls; the plans must have the same dtype and head_dim.
+ */
+bsp_status_t bsp_mixed_step(bsp_plan_t gen, bsp_plan_t ctx, const void* q, const void* k_new,
+                            const void* v_new, int64_t new_row_stride, void* k_pool, void* v_pool,
+                            const int32_t* block_tables_d, const int32_t* cache_indirection_d,
+                            void* o_out, float* lse_out, const void* q_ctx, const void* k_pool_ctx,
+                            const void* v_pool_ctx, void* o_ctx, float* lse_ctx,
+                            hipStream_t stream);
+
+/*
  * Comparator, not part of the cascade: per-beam attention over each beam's
  * whole sequence, reading the shared prompt once per (beam, KV head) through
  * the beam's own block table, as the decode kernel that the cascade replaces

@@ -152,3 +152,77 @@ def test_prefill_degenerate_shapes(name, page_size, kw):
     inp = synth.make_prefill(cfg, 13, **kw)
     say(f"prefill {name} Sq={inp.q_len.tolist()} L={inp.cached_len.tolist()}")
     _check_prefill(inp, name)
+
+
+def _mixed_refs(ctx_inp, gen_cfg, seed, **gen_kw):
+    fo_c, fl_c = oracle.prefill_attention(ctx_inp)
+    ref = synth.make_beam_step(gen_cfg, seed, **gen_kw)
+    ref.k_pool, ref.v_pool = oracle.write_kv(ref.k_pool, ref.v_pool, ref.slots, ref.k_new,
+                                             ref.v_new, ref.page_size)
+    return fo_c, fl_c, ref
+
+
+@pytest.mark.parametrize("gen_cfg,gen_kw,one_launch", [
+    ("qwen3_0p6b", dict(batch=6), True),            # W*G = 60 rows: one query block per wave
+    ("qwen3_4b", dict(batch=3), False),             # 120 rows: two blocks, two launches
+    ("nsample", dict(batch=5), True),               # 32 rows over four waves
+])
+def test_mixed_step_entry_point(gen_cfg, gen_kw, one_launch):
+    """bsp_mixed_step: context workgroups beside beam-step workgroups in one launch
+    (or two where the shapes do not allow it); both parts match the oracle on two
+    launches in a row, and the beam step's token write is bit-exact."""
+    ctx_inp = synth.make_prefill(gen_cfg, 6, batch=4, chunk_range=(100, 600), cached_range=(0, 300))
+    gen_inp = synth.make_beam_step(gen_cfg, 6, **gen_kw)
+    say(f"mixed entry {gen_cfg}: ctx Sq={ctx_inp.q_len.tolist()} gen P={gen_inp.prefix_len.tolist()}")
+    c = S.upload_prefill(ctx_inp, DEV)
+    g = S.upload_beam_step(gen_inp, DEV)
+    S.plan_prefill(c)
+    S.plan_beam_step(g)
+    fo_c, fl_c, ref = _mixed_refs(ctx_inp, gen_cfg, 6, **gen_kw)
+    fo_g, fl_g = oracle.beam_decode_attention(ref)
+    for rep in range(2):
+        S.run_mixed_step_fused(c, g)
+        B.bsp_check(c.plan)
+        B.bsp_check(g.plan)
+        torch.cuda.synchronize()
+        assert_close(c.out, c.lse_out, fo_c, fl_c, ctx_inp.dtype, f"mixed ctx {rep}")
+        assert_close(g.out, g.lse_out, fo_g, fl_g, gen_inp.dtype, f"mixed gen {rep}")
+    assert torch.equal(g.k_pool.cpu(), S.to_device(ref.k_pool, gen_inp.dtype, "cpu"))
+    assert torch.equal(g.v_pool.cpu(), S.to_device(ref.v_pool, gen_inp.dtype, "cpu"))
+
+
+def test_full_size_mixed_step_sampled():
+    """The bench's mixed step in one launch: 64 x 30 beams (512 beam-step
+    workgroups) beside four ~500-token prompts (~500 context workgroups); the
+    chunks of the two kinds alternate. Sampled rows of both against the oracle."""
+    ctx_inp = synth.make_prefill("qwen3_0p6b", 1, batch=4, chunk_range=(400, 600), garbage="unit")
+    gen_inp = synth.make_beam_step("qwen3_0p6b", 0, garbage="unit")
+    c = S.upload_prefill(ctx_inp, DEV)
+    g = S.upload_beam_step(gen_inp, DEV)
+    S.plan_prefill(c)
+    S.plan_beam_step(g)
+    S.run_mixed_step_fused(c, g)
+    B.bsp_check(c.plan)
+    B.bsp_check(g.plan)
+    torch.cuda.synchronize()
+    ref = gen_inp
+    ref.k_pool, ref.v_pool = oracle.write_kv(ref.k_pool, ref.v_pool, ref.slots, ref.k_new,
+                                             ref.v_new, ref.page_size)
+    to, tl = TOL["bf16"]
+    out = g.out.float().cpu().numpy().reshape(64, 30, 16, 128)
+    lse = g.lse_out.cpu().numpy().reshape(64, 30, 16)
+    rng = np.random.default_rng(4)
+    for b, k in [(0, 0), (63, 29)] + [(int(x), int(y)) for x, y in
+                                      zip(rng.integers(0, 64, 8), rng.integers(0, 30, 8))]:
+        fo, fl = oracle.beam_attention_one(ref, b, k)
+        assert np.abs(out[b, k] - fo[0]).max() <= to, (b, k)
+        assert np.abs(lse[b, k] - fl[0]).max() <= tl, (b, k)
+    cout = c.out.float().cpu().numpy()
+    clse = c.lse_out.cpu().numpy()
+    for b in range(ctx_inp.batch):
+        n = int(ctx_inp.q_len[b])
+        for i in [0, n - 1, int(rng.integers(0, n))]:
+            fo, fl = oracle.prefill_attention_one(ctx_inp, b, i)
+            r = int(ctx_inp.q_off[b]) + i
+            assert np.abs(cout[r] - fo).max() <= to, (b, i)
+            assert np.abs(clse[r] - fl).max() <= tl, (b, i)
