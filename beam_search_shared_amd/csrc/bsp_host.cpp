@@ -99,6 +99,7 @@ struct bsp_plan_s {
   bool planned = false;
   int32_t B = 0, W = 0, q_len = 0, tail_pad = 0, n_split = 1, rows_per_req = 0, n_pairs = 0;
   int32_t split_keys = 0;  // keys per split of the current step (0: one pass)
+  int32_t prefix_rpt = 0;  // query rows per work item of bsp_prefix_attn
   void* ws_d = nullptr;
   void* zeroed_ws = nullptr;  // workspace whose header this plan has cleared
   std::vector<ReqInfo> h_req;
@@ -411,6 +412,16 @@ bsp_status_t bsp_plan(bsp_plan_t pl, int32_t B, int32_t W, int32_t q_len,
     r.n_split = split_keys > 0 ? (int32_t)(r.valid > 0 ? ceil_div(r.valid, split_keys) : 1) : 1;
     if (r.n_split > n_split) n_split = r.n_split;
   }
+  // Query rows per work item of bsp_prefix_attn: the tallest tile whose grid
+  // still gives every CU two workgroups (without a key split), else one 16-row
+  // block per wave. A one-request causal segment of 2000 rows then runs as 752
+  // items of 64 rows instead of 256 items of 192, one per CU.
+  const int rows_req = W * q_len * (d.num_q_heads / d.num_kv_heads);
+  int32_t prefix_rpt = bsp::prefix_rows_per_tile(d.dtype, d.head_dim, rows_req);
+  if (d.dtype != BSP_F32 && split_keys == 0) {
+    for (; prefix_rpt > 64; prefix_rpt -= 64)
+      if ((int64_t)B * d.num_kv_heads * ceil_div(rows_req, prefix_rpt) >= bsp::kFillBlocks) break;
+  }
 
   // Fill the staging buffer: header (zero), request info, page table.
   const int slot = pl->ring;
@@ -496,6 +507,7 @@ bsp_status_t bsp_plan(bsp_plan_t pl, int32_t B, int32_t W, int32_t q_len,
   pl->tail_pad = d.max_tail > 0 ? d.max_tail : max_tail_seen;
   pl->n_split = n_split;
   pl->split_keys = split_keys;
+  pl->prefix_rpt = prefix_rpt;
   pl->rows_per_req = W * q_len * (d.num_q_heads / d.num_kv_heads);
   pl->n_pairs = n_pairs;
   pl->h_pairs = std::move(pairs);
@@ -699,13 +711,12 @@ bsp_status_t bsp_prefix_attn(bsp_plan_t pl, const void* q, const void* k_pool, c
   p.num_pages = d.num_pages;
   p.n_split = pl->n_split;
   p.split_keys = pl->split_keys;
-  const int rows_per_tile = bsp::prefix_rows_per_tile(d.dtype, d.head_dim, pl->rows_per_req);
-  p.n_qtiles = (int32_t)ceil_div(pl->rows_per_req, rows_per_tile);
+  p.n_qtiles = (int32_t)ceil_div(pl->rows_per_req, pl->prefix_rpt);
   p.causal = d.mask == BSP_MASK_CAUSAL ? 1 : 0;
   p.rows_total = pl->B * pl->W * pl->q_len;
   p.scale = d.sm_scale;
   p.scale_log2e = d.sm_scale * 1.4426950408889634f;
-  return after_launch(pl, bsp::launch_prefix(p, d.dtype, d.head_dim, pl->rows_per_req, stream),
+  return after_launch(pl, bsp::launch_prefix(p, d.dtype, d.head_dim, pl->prefix_rpt, stream),
                       "prefix launch", stream);
 }
 

@@ -159,12 +159,14 @@ struct MergeParams {
 // launch error; shape checks are done by the host entry points beforehand.
 // ---------------------------------------------------------------------------
 hipError_t launch_write_kv(const WriteKvParams& p, int dtype, hipStream_t s);
-hipError_t launch_prefix(const PrefixParams& p, int dtype, int head_dim, int rows_per_req,
+// `rows_per_tile`: query rows per work item as the plan chose it (a multiple of 64
+// on the matrix cores, prefix_rows_per_tile() or fewer).
+hipError_t launch_prefix(const PrefixParams& p, int dtype, int head_dim, int rows_per_tile,
                          hipStream_t s);
 hipError_t launch_decode_step(const PrefixParams& p, const FusedParams& f, int dtype,
                               int head_dim, int rows_per_req, int tail_pad, hipStream_t s);
-// Rows per workgroup the prefix kernel picks for this shape (so the host can
-// size the grid before launching).
+// Rows per workgroup the prefix kernel takes at most for this shape (so the host
+// can size the grid before launching).
 int prefix_rows_per_tile(int dtype, int head_dim, int rows_per_req);
 // Prefill (bsp_prefill_attn): at most this many 16-row query blocks per wave
 // (64 * mb query rows per work item); the plan takes fewer when the batch is

@@ -250,6 +250,23 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
       const int last = min((w.qt + 1) * 64 * MB, rb.tail * p.group) - 1;
       sg_lo0 = 0;
       sg_hi0 = min(rb.valid, rb.valid - rb.tail + last / p.group + 1);
+    } else if (!FUSED && p.causal && p.W == 1) {
+      // Causal rows of one sequence: row r is position r / group and sees keys
+      // up to n_keys - q_len + r / group, so a tile streams only the keys up to
+      // its last row's limit. Tiles go longest first (query tile slowest,
+      // descending), so the short ones fill the last round.
+      w.g = bid % p.hkv;
+      bid /= p.hkv;
+      w.split = bid % p.n_split;
+      bid /= p.n_split;
+      sg_b0 = bid % p.B;
+      w.qt = p.n_qtiles - 1 - bid / p.B;
+      const ReqInfo rb = p.req[sg_b0];
+      const int r_last = min((w.qt + 1) * 64 * MB, p.q_len * p.group) - 1;
+      const int lim = min(rb.valid, rb.n_keys - p.q_len + r_last / p.group + 1);
+      sg_lo0 = p.split_keys > 0 ? w.split * p.split_keys : 0;
+      sg_hi0 = p.split_keys > 0 ? min(lim, sg_lo0 + p.split_keys) : lim;
+      if (sg_hi0 < sg_lo0) sg_hi0 = sg_lo0;
     } else {
       w.qt = bid % p.n_qtiles;
       bid /= p.n_qtiles;
@@ -527,9 +544,11 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
   constexpr int AHEAD = ROT ? NST - 2 : NST - 1;  // tiles in flight beyond the one computed
 
   const int n_tail = fused ? ri.tail : 0;
-  // prefill: the smallest causal limit among this wave's rows (its first row);
-  // a key tile at or below it needs no mask
-  const int c_first = is_pre ? ri.valid - ri.tail + row0 / p.group : 0;
+  // prefill, and causal rows of one sequence: the smallest causal limit among
+  // this wave's rows (its first row); a key tile at or below it needs no mask
+  const bool causal1 = !FUSED && !is_pre && p.causal && p.W == 1;
+  const int c_first = is_pre ? ri.valid - ri.tail + row0 / p.group
+                             : causal1 ? ri.n_keys - p.q_len + row0 / p.group : 0;
   const int win_first = w.k_lo / keys_per_win;
   const int n_win = w.k_hi > w.k_lo ? (w.k_hi - 1) / keys_per_win - win_first + 1 : 0;
 
@@ -634,7 +653,7 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
       f32x4 sacc[NKB][MB];
       s_tile(lds_kv[t % NST][0], sacc);
       if (ROT && t > 0) o_tile(lds_kv[(t - 1) % NST][1], pb);
-      softmax_tile(sacc, (t0 + KT <= w.k_hi) && (is_pre ? t0 + KT - 1 <= c_first : !p.causal),
+      softmax_tile(sacc, (t0 + KT <= w.k_hi) && (is_pre || causal1 ? t0 + KT - 1 <= c_first : !p.causal),
                    [&](int qb, int kk) { return (t0 + kk < w.k_hi) & (t0 + kk <= climit[qb]); }, pb);
       if (!ROT) o_tile(lds_kv[t % NST][1], pb);
     }
@@ -1224,7 +1243,7 @@ static void launch_mfma(const PrefixParams& p, const FusedParams& f, int head_di
 #undef BSP_PFX
 }
 
-hipError_t launch_prefix(const PrefixParams& p, int dtype, int head_dim, int rows_per_req,
+hipError_t launch_prefix(const PrefixParams& p, int dtype, int head_dim, int rows_per_tile,
                          hipStream_t s) {
   const unsigned blocks = (unsigned)(p.B * p.hkv * p.n_split * p.n_qtiles);
   if (blocks == 0) return hipSuccess;
@@ -1233,7 +1252,9 @@ hipError_t launch_prefix(const PrefixParams& p, int dtype, int head_dim, int row
     else if (head_dim == 128) prefix_simt_kernel<128><<<blocks, 256, 0, s>>>(p);
     else prefix_simt_kernel<256><<<blocks, 256, 0, s>>>(p);
   } else {
-    const int mb = pick_mb(head_dim, rows_per_req);
+    const int mb = rows_per_tile / 64;
+    if (mb < 1 || mb > pick_mb(head_dim, 64 * 3) || rows_per_tile % 64 != 0)
+      return hipErrorInvalidValue;
     const FusedParams none{};
     if (dtype == BSP_F16) launch_mfma<_Float16, 0, false>(p, none, head_dim, mb, blocks, s);
     else launch_mfma<__bf16, 0, false>(p, none, head_dim, mb, blocks, s);
