@@ -77,6 +77,7 @@ _SIGS = {
     "bsp_plan_tail_len": (_I32, [_P]),
     "bsp_write_kv": (_I32, [_P, _P, _P, _I64, _P, _I32, _P, _P, _P]),
     "bsp_prefix_attn": (_I32, [_P, _P, _P, _P, _P, _P, _P]),
+    "bsp_prefix_attn_two": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "bsp_tail_attn": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "bsp_merge": (_I32, [_I32, _I32, _I32, _I32, _P, _P, _I64, _I64, _P, _I32, _P, _P]),
     "bsp_naive_beam_attn": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P]),
@@ -228,6 +229,13 @@ def bsp_write_kv(plan: Plan, k_new, v_new, src_row_stride: int, slots, n: int, k
 def bsp_prefix_attn(plan: Plan, q, k_pool, v_pool, o_part, lse_part, stream=None) -> None:
     _check(load_library().bsp_prefix_attn(plan.handle, _ptr(q), _ptr(k_pool), _ptr(v_pool),
                                           _ptr(o_part), _ptr(lse_part), _stream(stream)))
+
+
+def bsp_prefix_attn_two(plan_a: Plan, plan_b: Plan, q, k_pool, v_pool, o_part_a, lse_part_a,
+                        o_part_b, lse_part_b, stream=None) -> None:
+    _check(load_library().bsp_prefix_attn_two(plan_a.handle, plan_b.handle, _ptr(q), _ptr(k_pool),
+                                              _ptr(v_pool), _ptr(o_part_a), _ptr(lse_part_a),
+                                              _ptr(o_part_b), _ptr(lse_part_b), _stream(stream)))
 
 
 def bsp_tail_attn(plan: Plan, q, k_pool, v_pool, block_tables, cache_indirection, o_tail,

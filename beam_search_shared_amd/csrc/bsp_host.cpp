@@ -684,15 +684,17 @@ bsp_status_t bsp_write_kv(bsp_plan_t pl, const void* k_new, const void* v_new,
   return after_launch(pl, bsp::launch_write_kv(p, d.dtype, stream), "write_kv launch", stream);
 }
 
-bsp_status_t bsp_prefix_attn(bsp_plan_t pl, const void* q, const void* k_pool, const void* v_pool,
-                             float* o_part, float* lse_part, hipStream_t stream) {
+// Validation and kernel parameters of bsp_prefix_attn for one plan.
+static bsp_status_t prefix_params(bsp_plan_s* pl, const void* q, const void* k_pool,
+                                  const void* v_pool, float* o_part, float* lse_part,
+                                  bsp::PrefixParams& p) {
   bsp_status_t st = check_beam_ready(pl);
   if (st != BSP_OK) return st;
   if (!q || !k_pool || !v_pool || !o_part || !lse_part) return fail(BSP_ERR_ARG, "null pointer");
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o_part))
     return fail(BSP_ERR_ARG, "q, the pools and o_part must be 16-byte aligned");
   const bsp_layer_desc_t& d = pl->desc;
-  bsp::PrefixParams p{};
+  p = bsp::PrefixParams{};
   p.q = q;
   p.k_pool = k_pool;
   p.v_pool = v_pool;
@@ -716,7 +718,46 @@ bsp_status_t bsp_prefix_attn(bsp_plan_t pl, const void* q, const void* k_pool, c
   p.rows_total = pl->B * pl->W * pl->q_len;
   p.scale = d.sm_scale;
   p.scale_log2e = d.sm_scale * 1.4426950408889634f;
+  return BSP_OK;
+}
+
+bsp_status_t bsp_prefix_attn(bsp_plan_t pl, const void* q, const void* k_pool, const void* v_pool,
+                             float* o_part, float* lse_part, hipStream_t stream) {
+  bsp::PrefixParams p{};
+  const bsp_status_t st = prefix_params(pl, q, k_pool, v_pool, o_part, lse_part, p);
+  if (st != BSP_OK) return st;
+  const bsp_layer_desc_t& d = pl->desc;
   return after_launch(pl, bsp::launch_prefix(p, d.dtype, d.head_dim, pl->prefix_rpt, stream),
+                      "prefix launch", stream);
+}
+
+bsp_status_t bsp_prefix_attn_two(bsp_plan_t a, bsp_plan_t b, const void* q, const void* k_pool,
+                                 const void* v_pool, float* o_part_a, float* lse_part_a,
+                                 float* o_part_b, float* lse_part_b, hipStream_t stream) {
+  if (a == nullptr || b == nullptr) return fail(BSP_ERR_ARG, "null plan");
+  if (a == b) return fail(BSP_ERR_ARG, "bsp_prefix_attn_two needs two plans");
+  bsp::PrefixParams pa{}, pb{};
+  bsp_status_t st = prefix_params(a, q, k_pool, v_pool, o_part_a, lse_part_a, pa);
+  if (st != BSP_OK) return st;
+  st = prefix_params(b, q, k_pool, v_pool, o_part_b, lse_part_b, pb);
+  if (st != BSP_OK) return st;
+  const bsp_layer_desc_t& da = a->desc;
+  const bsp_layer_desc_t& db = b->desc;
+  if (da.dtype != db.dtype || da.head_dim != db.head_dim || da.num_q_heads != db.num_q_heads ||
+      da.num_kv_heads != db.num_kv_heads || a->B * a->W * a->q_len != b->B * b->W * b->q_len)
+    return fail(BSP_ERR_ARG,
+                "the two plans need the same dtype, heads, head_dim and query rows");
+  if (da.dtype != BSP_F32 && a->prefix_rpt == 64 && b->prefix_rpt == 64) {
+    st = after_launch(a, bsp::launch_prefix_two(pa, pb, da.dtype, da.head_dim, stream),
+                      "two-plan prefix launch", stream);
+    if (st == BSP_OK && b->check_mode) st = bsp_check(b, stream);
+    return st;
+  }
+  // other tile heights: one launch per plan
+  st = after_launch(a, bsp::launch_prefix(pa, da.dtype, da.head_dim, a->prefix_rpt, stream),
+                    "prefix launch", stream);
+  if (st != BSP_OK) return st;
+  return after_launch(b, bsp::launch_prefix(pb, db.dtype, db.head_dim, b->prefix_rpt, stream),
                       "prefix launch", stream);
 }
 

@@ -163,6 +163,10 @@ hipError_t launch_write_kv(const WriteKvParams& p, int dtype, hipStream_t s);
 // on the matrix cores, prefix_rows_per_tile() or fewer).
 hipError_t launch_prefix(const PrefixParams& p, int dtype, int head_dim, int rows_per_tile,
                          hipStream_t s);
+// Two plans' bsp_prefix_attn work in one launch; both take 64 query rows per
+// work item (bf16/f16 only).
+hipError_t launch_prefix_two(const PrefixParams& a, const PrefixParams& b, int dtype, int head_dim,
+                             hipStream_t s);
 hipError_t launch_decode_step(const PrefixParams& p, const FusedParams& f, int dtype,
                               int head_dim, int rows_per_req, int tail_pad, hipStream_t s);
 // Rows per workgroup the prefix kernel takes at most for this shape (so the host

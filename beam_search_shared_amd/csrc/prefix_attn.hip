@@ -1104,6 +1104,19 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, 1>())) void mixed_step_k
   prefix_body<T, D, 1, KT, NST, 4, false>(pre ? pp : dp, pre ? pf : df, idx, pre);
 }
 
+// Two plans' shared-key attention in one launch (MODE 0, one 16-row query
+// block per wave): the first n_a workgroups are plan a's work items, the rest
+// plan b's; each writes its own plan's partial states. For two small segments
+// of one call (the cached rows and this call's rows) one launch instead of two.
+template <typename T, int D, int KT, int NST>
+__global__ __launch_bounds__(256, (prefix_min_blocks<D, 1>())) void prefix_two_kernel(
+    PrefixParams a, PrefixParams b, int n_a) {
+  const FusedParams none{};
+  const bool second = (int)blockIdx.x >= n_a;
+  prefix_body<T, D, 1, KT, NST, 0, false>(second ? b : a, none,
+                                          second ? (int)blockIdx.x - n_a : (int)blockIdx.x, false);
+}
+
 // f32: one wave per query row, lanes split head_dim, keys in chunks of 8.
 template <int D>
 __global__ __launch_bounds__(256) void prefix_simt_kernel(PrefixParams p) {
@@ -1259,6 +1272,27 @@ hipError_t launch_prefix(const PrefixParams& p, int dtype, int head_dim, int row
     if (dtype == BSP_F16) launch_mfma<_Float16, 0, false>(p, none, head_dim, mb, blocks, s);
     else launch_mfma<__bf16, 0, false>(p, none, head_dim, mb, blocks, s);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefix_two(const PrefixParams& a, const PrefixParams& b, int dtype, int head_dim,
+                             hipStream_t s) {
+  const int n_a = a.B * a.hkv * a.n_split * a.n_qtiles;
+  const int n_b = b.B * b.hkv * b.n_split * b.n_qtiles;
+  const unsigned blocks = (unsigned)(n_a + n_b);
+  if (blocks == 0) return hipSuccess;
+  if (dtype != BSP_F16 && dtype != BSP_BF16) return hipErrorInvalidValue;
+#define BSP_TWO(TT, DD, KTT, NS) prefix_two_kernel<TT, DD, KTT, NS><<<blocks, 256, 0, s>>>(a, b, n_a)
+  if (dtype == BSP_F16) {
+    if (head_dim == 64) BSP_TWO(_Float16, 64, 64, 4);
+    else if (head_dim == 128) BSP_TWO(_Float16, 128, 32, 4);
+    else BSP_TWO(_Float16, 256, 32, 2);
+  } else {
+    if (head_dim == 64) BSP_TWO(__bf16, 64, 64, 4);
+    else if (head_dim == 128) BSP_TWO(__bf16, 128, 32, 4);
+    else BSP_TWO(__bf16, 256, 32, 2);
+  }
+#undef BSP_TWO
   return hipGetLastError();
 }
 

@@ -242,15 +242,22 @@ def plan_cached_prefix(c: CachedPrefixDevice, stream=None) -> None:
         c.lse_out = torch.zeros((rows, Hq), device=dev, dtype=torch.float32)
 
 
-def run_cached_prefix(c: CachedPrefixDevice, stream=None) -> None:
-    """write new rows + cache segment + new-row segment + n-way merge."""
+def run_cached_prefix(c: CachedPrefixDevice, stream=None, two_launches: bool = False) -> None:
+    """write new rows + cache segment and new-row segment (one launch when both take
+    64-row tiles, as in a one-row decode; ``two_launches`` forces one launch each)
+    + n-way merge."""
     Hkv, D = c.num_kv_heads, c.head_dim
     B.bsp_write_kv(c.plan_new, c.new_k, c.new_v, Hkv * D, c.slots, c.q_len, c.k_pool, c.v_pool,
                    stream)
     ns = c.n_split
-    B.bsp_prefix_attn(c.plan_cache, c.q, c.k_pool, c.v_pool, c.o_part[:ns], c.lse_part[:ns],
-                      stream)
-    B.bsp_prefix_attn(c.plan_new, c.q, c.k_pool, c.v_pool, c.o_part[ns], c.lse_part[ns], stream)
+    if two_launches:
+        B.bsp_prefix_attn(c.plan_cache, c.q, c.k_pool, c.v_pool, c.o_part[:ns], c.lse_part[:ns],
+                          stream)
+        B.bsp_prefix_attn(c.plan_new, c.q, c.k_pool, c.v_pool, c.o_part[ns], c.lse_part[ns],
+                          stream)
+    else:
+        B.bsp_prefix_attn_two(c.plan_cache, c.plan_new, c.q, c.k_pool, c.v_pool, c.o_part[:ns],
+                              c.lse_part[:ns], c.o_part[ns], c.lse_part[ns], stream)
     rows = c.q_len
     B.bsp_merge(rows, c.num_q_heads, D, ns + 1, c.o_part, c.lse_part, rows * c.num_q_heads * D,
                 rows * c.num_q_heads, c.out, c.dtype, c.lse_out, stream)

@@ -371,8 +371,9 @@ def cached_work(L: int, Sq: int, Hq: int, Hkv: int, D: int, e: int):
 
 
 def bench_cached(args, torch, synth, B, S, prefill: bool) -> dict:
-    """The masked cached-prefix call: bsp_write_kv + bsp_prefix_attn (cache chunks)
-    + bsp_prefix_attn (new rows) + bsp_merge, rotating over layer copies."""
+    """The masked cached-prefix call: bsp_write_kv + bsp_prefix_attn_two (cache chunks
+    and new rows) + bsp_merge, rotating over layer copies; beside it the same call with
+    one bsp_prefix_attn per segment, and the cache chunks alone (the roofline entry)."""
     import oracle
 
     dev = "cuda"
@@ -417,39 +418,48 @@ def bench_cached(args, torch, synth, B, S, prefill: bool) -> dict:
         ns = base.n_split
         hd = base.num_kv_heads * base.head_dim
         rows = base.q_len
-        calls = []
+        calls, calls4 = [], []
         for c in cs:
-            calls.append((
-                (lib.bsp_write_kv, (c.plan_new.handle, c.new_k.data_ptr(), c.new_v.data_ptr(), hd,
-                                    c.slots.data_ptr(), rows, c.k_pool.data_ptr(),
-                                    c.v_pool.data_ptr(), sh)),
-                (lib.bsp_prefix_attn, (c.plan_cache.handle, c.q.data_ptr(), c.k_pool.data_ptr(),
-                                       c.v_pool.data_ptr(), c.o_part.data_ptr(),
-                                       c.lse_part.data_ptr(), sh)),
-                (lib.bsp_prefix_attn, (c.plan_new.handle, c.q.data_ptr(), c.k_pool.data_ptr(),
-                                       c.v_pool.data_ptr(), c.o_part[ns].data_ptr(),
-                                       c.lse_part[ns].data_ptr(), sh)),
-                (lib.bsp_merge, (rows, base.num_q_heads, base.head_dim, ns + 1,
-                                 c.o_part.data_ptr(), c.lse_part.data_ptr(),
-                                 rows * base.num_q_heads * base.head_dim, rows * base.num_q_heads,
-                                 c.out.data_ptr(), B.DTYPE_CODE[base.dtype], c.lse_out.data_ptr(),
-                                 sh))))
+            write = (lib.bsp_write_kv, (c.plan_new.handle, c.new_k.data_ptr(), c.new_v.data_ptr(),
+                                        hd, c.slots.data_ptr(), rows, c.k_pool.data_ptr(),
+                                        c.v_pool.data_ptr(), sh))
+            cache = (lib.bsp_prefix_attn, (c.plan_cache.handle, c.q.data_ptr(), c.k_pool.data_ptr(),
+                                           c.v_pool.data_ptr(), c.o_part.data_ptr(),
+                                           c.lse_part.data_ptr(), sh))
+            new = (lib.bsp_prefix_attn, (c.plan_new.handle, c.q.data_ptr(), c.k_pool.data_ptr(),
+                                         c.v_pool.data_ptr(), c.o_part[ns].data_ptr(),
+                                         c.lse_part[ns].data_ptr(), sh))
+            both = (lib.bsp_prefix_attn_two, (c.plan_cache.handle, c.plan_new.handle,
+                                              c.q.data_ptr(), c.k_pool.data_ptr(),
+                                              c.v_pool.data_ptr(), c.o_part.data_ptr(),
+                                              c.lse_part.data_ptr(), c.o_part[ns].data_ptr(),
+                                              c.lse_part[ns].data_ptr(), sh))
+            merge = (lib.bsp_merge, (rows, base.num_q_heads, base.head_dim, ns + 1,
+                                     c.o_part.data_ptr(), c.lse_part.data_ptr(),
+                                     rows * base.num_q_heads * base.head_dim,
+                                     rows * base.num_q_heads, c.out.data_ptr(),
+                                     B.DTYPE_CODE[base.dtype], c.lse_out.data_ptr(), sh))
+            # the call: write, both key segments (one launch when their tiles
+            # allow it), merge; and the same as one bsp_prefix_attn per segment
+            calls.append((write, both, merge, cache))
+            calls4.append((write, cache, new, merge))
 
-        def call(i):
-            for fn, a in calls[i % layers]:
-                if fn(*a) != 0:
-                    raise RuntimeError(B.load_library().bsp_last_error().decode())
+        def runner(table, sel):
+            def run(i):
+                for fn, a in (table[i % layers][j] for j in sel):
+                    if fn(*a) != 0:
+                        raise RuntimeError(B.load_library().bsp_last_error().decode())
+            return run
 
-        def cache_seg(i):
-            fn, a = calls[i % layers][1]
-            if fn(*a) != 0:
-                raise RuntimeError(B.load_library().bsp_last_error().decode())
-
-        sec, _ = _timed_loop(torch, call, args.steps, args.warmup,
+        sec, _ = _timed_loop(torch, runner(calls, (0, 1, 2)), args.steps, args.warmup,
                              args.warm_seconds if name == "auto" else 0.2, main_stream, sync)
-        _, seg_ms = _timed_loop(torch, cache_seg, args.steps, args.warmup, 0.0, main_stream, sync)
-        res_t[name] = dict(ms=sec / args.steps * 1e3, seg_ms=seg_ms, n_split=base.n_split,
-                           split_keys=base.plan_cache.split_keys, layers=layers)
+        sec4, _ = _timed_loop(torch, runner(calls4, (0, 1, 2, 3)), args.steps, args.warmup, 0.0,
+                              main_stream, sync)
+        _, seg_ms = _timed_loop(torch, runner(calls, (3,)), args.steps, args.warmup, 0.0,
+                                main_stream, sync)
+        res_t[name] = dict(ms=sec / args.steps * 1e3, ms4=sec4 / args.steps * 1e3, seg_ms=seg_ms,
+                           n_split=base.n_split, split_keys=base.plan_cache.split_keys,
+                           layers=layers)
         del cs, base
     a = res_t["auto"]
     seg_bytes = L * Hkv * D * EBYTES[inp.dtype] * 2 + Sq * Hq * D * EBYTES[inp.dtype]
@@ -468,13 +478,14 @@ def bench_cached(args, torch, synth, B, S, prefill: bool) -> dict:
                 "avg_launch_us": a["seg_ms"] * 1e3, "alg_bytes_per_launch": seg_bytes}
     cfg = "cached_prefill" if prefill else "cached_decode"
     res = {
-        "metric": "masked cached-prefix calls/s per layer (write + cache chunks + new rows + merge)",
+        "metric": "masked cached-prefix calls/s per layer (write + cache chunks and new rows + merge)",
         "value": 1e3 / a["ms"], "unit": "calls/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": a["ms"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": inp.dtype, "data": "synthetic",
         "config": {"workload": WORKLOADS[cfg], "name": cfg, "valid_rows": L, "new_rows": Sq,
                    "layers_rotated": a["layers"], "chunks": a["n_split"],
                    "chunk_keys": a["split_keys"], "flops": flops, "alg_bytes": nbytes,
+                   "segments_one_launch_each_ms_per_step": a["ms4"],
                    "fixed_256_chunks": res_t["fixed_256"]["n_split"],
                    "fixed_256_ms_per_step": res_t["fixed_256"]["ms"],
                    "fixed_256_cache_segment_us": res_t["fixed_256"]["seg_ms"] * 1e3},

@@ -202,6 +202,23 @@ bsp_status_t bsp_prefix_attn(bsp_plan_t plan, const void* q, const void* k_pool,
                              hipStream_t stream);
 
 /*
+ * bsp_prefix_attn for two plans of the same layer and query rows in one
+ * launch: plan a writes o_part_a / lse_part_a, plan b writes o_part_b /
+ * lse_part_b, exactly as two bsp_prefix_attn calls would. For the two key
+ * segments of one masked cached-prefix call (PR #2202, Implementation: the
+ * cached rows up to the bound, then this call's rows), whose partials are
+ * then merged with bsp_merge. Both plans must be planned, with the same
+ * dtype, head counts, head_dim and B * W * q_len; q and the pools are shared.
+ * When both plans take one 64-row query tile per work item (bf16/f16) the
+ * work of both runs in one launch; otherwise the call makes one launch per
+ * plan. Errors as for bsp_prefix_attn, checked for both plans before any
+ * launch.
+ */
+bsp_status_t bsp_prefix_attn_two(bsp_plan_t a, bsp_plan_t b, const void* q, const void* k_pool,
+                                 const void* v_pool, float* o_part_a, float* lse_part_a,
+                                 float* o_part_b, float* lse_part_b, hipStream_t stream);
+
+/*
  * Tail attention: each beam's G query rows against its own tail positions
  * P_b <= j < S_b, gathered through cache_indirection: position j of beam k is
  * read from beam src = cache_indirection[b][k][j], page

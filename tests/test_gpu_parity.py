@@ -295,6 +295,47 @@ def test_cached_prefix_prefill_matches_oracle(L, Sq, causal, split):
     assert_close(c.out, c.lse_out, o, lse, "f16", f"prefill L={L} Sq={Sq}")
 
 
+@pytest.mark.parametrize("L,Sq", [(10368, 1), (5000, 1), (0, 1), (777, 200)])
+def test_prefix_attn_two_equals_two_calls(L, Sq):
+    """bsp_prefix_attn_two writes exactly what two bsp_prefix_attn calls write: one
+    launch for a one-row decode (both segments in 64-row tiles), one per plan for a
+    prefill whose cache segment takes taller tiles."""
+    rows_alloc = 10368 if Sq == 1 else 1024
+    inp = synth.make_cached_prefix(L % 11, valid_rows=L, q_len=Sq, max_cache_rows=rows_alloc)
+    say(f"prefix_attn_two L={L} Sq={Sq}")
+    outs = []
+    for two in (False, True):
+        c = S.upload_cached_prefix(inp, DEV)
+        S.plan_cached_prefix(c)
+        c.o_part.fill_(7.0)
+        c.lse_part.fill_(7.0)
+        S.run_cached_prefix(c, two_launches=not two)
+        B.bsp_check(c.plan_cache)
+        B.bsp_check(c.plan_new)
+        torch.cuda.synchronize()
+        outs.append((c.o_part.clone(), c.lse_part.clone(), c.out.clone(), c.lse_out.clone()))
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)
+    o, lse = oracle.cached_prefix_attention(inp, causal=True)
+    assert_close(outs[1][2], outs[1][3], o, lse, "f16", f"two-plan L={L} Sq={Sq}")
+
+
+def test_prefix_attn_two_rejects_mismatched_plans():
+    inp = synth.make_cached_prefix(3, valid_rows=300, q_len=1)
+    c = S.upload_cached_prefix(inp, DEV)
+    S.plan_cached_prefix(c)
+    ns = c.n_split
+    with pytest.raises(RuntimeError):  # the same plan twice
+        B.bsp_prefix_attn_two(c.plan_cache, c.plan_cache, c.q, c.k_pool, c.v_pool, c.o_part[:ns],
+                              c.lse_part[:ns], c.o_part[ns], c.lse_part[ns])
+    other = synth.make_cached_prefix(3, valid_rows=300, q_len=4)
+    d = S.upload_cached_prefix(other, DEV)
+    S.plan_cached_prefix(d)
+    with pytest.raises(RuntimeError):  # different query rows
+        B.bsp_prefix_attn_two(c.plan_cache, d.plan_new, c.q, c.k_pool, c.v_pool, c.o_part[:ns],
+                              c.lse_part[:ns], c.o_part[ns], c.lse_part[ns])
+
+
 def test_cached_prefix_garbage_rows_do_not_matter():
     L = 700
     a = synth.make_cached_prefix(1, valid_rows=L, q_len=1)
