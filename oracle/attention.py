@@ -207,7 +207,8 @@ def _cached_visible(i: int, L: int, q_len: int, causal: bool):
     return list(range(L)), list(new)
 
 
-def cached_prefix_attention(inp, causal: bool = True, scale: Optional[float] = None):
+def cached_prefix_attention(inp, causal: bool = True, scale: Optional[float] = None,
+                            rows: Optional[list] = None):
     """Beam-1 attention over the valid cached prefix plus this call's rows.
 
     Keys are the concatenation of the bound cache rows and the ``Sq`` new rows
@@ -220,7 +221,8 @@ def cached_prefix_attention(inp, causal: bool = True, scale: Optional[float] = N
 
     ``inp`` carries ``q [Sq, Hq, D]``, ``cache_k/cache_v [rows, Hkv, D]``,
     ``valid_rows`` and ``new_k/new_v [Sq, Hkv, D]``. Returns ``o [Sq, Hq, D]``,
-    ``lse [Sq, Hq]``.
+    ``lse [Sq, Hq]``; with ``rows`` (query row indices) only those rows, in that
+    order, ``o [len(rows), Hq, D]`` and ``lse [len(rows), Hq]``.
     """
     q = inp.q
     Sq, Hq, D = q.shape
@@ -228,17 +230,18 @@ def cached_prefix_attention(inp, causal: bool = True, scale: Optional[float] = N
     G = Hq // Hkv
     sc = default_scale(D) if scale is None else scale
     L = int(inp.valid_rows)
-    o = np.zeros((Sq, Hq, D))
-    lse = np.full((Sq, Hq), NEG_INF)
-    for i in range(Sq):
+    which = list(range(Sq)) if rows is None else [int(i) for i in rows]
+    o = np.zeros((len(which), Hq, D))
+    lse = np.full((len(which), Hq), NEG_INF)
+    for n, i in enumerate(which):
         crow, nrow = _cached_visible(i, L, Sq, causal)
         for g in range(Hkv):             # query heads g*G .. g*G+G-1 read KV head g
             heads = slice(g * G, (g + 1) * G)
             K = np.concatenate([inp.cache_k[crow, g, :], inp.new_k[nrow, g, :]]).astype(np.float64)
             V = np.concatenate([inp.cache_v[crow, g, :], inp.new_v[nrow, g, :]]).astype(np.float64)
             oo, ll = attend(q[i, heads], K, V, sc)
-            o[i, heads] = oo
-            lse[i, heads] = ll
+            o[n, heads] = oo
+            lse[n, heads] = ll
     return o, lse
 
 

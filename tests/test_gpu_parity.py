@@ -336,6 +336,25 @@ def test_prefix_attn_two_rejects_mismatched_plans():
                               c.lse_part[:ns], c.o_part[ns], c.lse_part[ns])
 
 
+def test_full_size_cached_prefill_sampled():
+    """The bench's cached-prefix prefill: 10368 valid cached rows + 2000 causal new rows,
+    the automatic key split; sampled query rows (first, last, tile edges, random)."""
+    inp = synth.make_cached_prefix(0, valid_rows=10368, q_len=2000)
+    c = S.upload_cached_prefix(inp, DEV)
+    S.plan_cached_prefix(c)
+    say(f"full-size cached prefill: {c.n_split} chunks of {c.plan_cache.split_keys} keys")
+    S.run_cached_prefix(c)
+    B.bsp_check(c.plan_cache)
+    B.bsp_check(c.plan_new)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    rows = sorted({0, 1, 21, 63, 64, 191, 192, 1000, 1998, 1999} |
+                  {int(r) for r in rng.integers(0, 2000, 10)})
+    o, lse = oracle.cached_prefix_attention(inp, causal=True, rows=rows)
+    idx = torch.tensor(rows, device=DEV)
+    assert_close(c.out[idx], c.lse_out[idx], o, lse, "f16", "full-size cached prefill")
+
+
 def test_cached_prefix_garbage_rows_do_not_matter():
     L = 700
     a = synth.make_cached_prefix(1, valid_rows=L, q_len=1)

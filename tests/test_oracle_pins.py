@@ -499,3 +499,12 @@ def test_prefill_pool_and_slots_hold_the_logical_rows():
         want = np.concatenate([inp.cache_k[b], inp.new_k[r0:r0 + n]])
         got = np.stack([kp[inp.block_tables[b, j // ps], :, j % ps] for j in range(L + n)])
         assert np.array_equal(got, want)
+
+
+def test_cached_prefix_row_subset_is_the_full_result_restricted():
+    """Asking for some query rows gives exactly those rows of the full result."""
+    inp = synth.make_cached_prefix(5, valid_rows=300, q_len=40, max_cache_rows=512)
+    o, lse = oracle.cached_prefix_attention(inp, causal=True)
+    rows = [39, 0, 17, 18]
+    so, sl = oracle.cached_prefix_attention(inp, causal=True, rows=rows)
+    assert np.array_equal(so, o[rows]) and np.array_equal(sl, lse[rows])
