@@ -1245,12 +1245,14 @@ static void launch_mfma(const PrefixParams& p, const FusedParams& f, int head_di
       else if (mb == 2) BSP_PFX(64, 2, 64, 4);
       else BSP_PFX(64, 3, 64, 4);
     } else if (head_dim == 128) {
-      // The fused step at one or two query blocks per wave streams 64-key tiles
-      // through a two-stage ring (the same LDS as four stages of 32 keys, half
-      // the barriers, waits and row-max reductions per key): 3-4% faster at one
-      // block, ~1-2% at two. At three blocks the 64-key tile spills registers.
+      // The fused step at one or two query blocks per wave, and the partial-state
+      // kernel at one, stream 64-key tiles through a two-stage ring (the same LDS
+      // as four stages of 32 keys, half the barriers, waits and row-max
+      // reductions per key): 3-4% faster at one block (fused), ~1-2% at two and
+      // ~2.5% for the partial-state kernel. At three blocks the 64-key tile
+      // spills registers.
       if (mb == 1) {
-        if constexpr (MODE == 1) BSP_PFX(128, 1, 64, 2);
+        if constexpr (MODE == 1 || MODE == 0) BSP_PFX(128, 1, 64, 2);
         else BSP_PFX(128, 1, 32, 4);
       } else if (mb == 2) {
         if constexpr (MODE == 1) BSP_PFX(128, 2, 64, 2);
@@ -1295,11 +1297,11 @@ hipError_t launch_prefix_two(const PrefixParams& a, const PrefixParams& b, int d
 #define BSP_TWO(TT, DD, KTT, NS) prefix_two_kernel<TT, DD, KTT, NS><<<blocks, 256, 0, s>>>(a, b, n_a)
   if (dtype == BSP_F16) {
     if (head_dim == 64) BSP_TWO(_Float16, 64, 64, 4);
-    else if (head_dim == 128) BSP_TWO(_Float16, 128, 32, 4);
+    else if (head_dim == 128) BSP_TWO(_Float16, 128, 64, 2);
     else BSP_TWO(_Float16, 256, 32, 2);
   } else {
     if (head_dim == 64) BSP_TWO(__bf16, 64, 64, 4);
-    else if (head_dim == 128) BSP_TWO(__bf16, 128, 32, 4);
+    else if (head_dim == 128) BSP_TWO(__bf16, 128, 64, 2);
     else BSP_TWO(__bf16, 256, 32, 2);
   }
 #undef BSP_TWO
