@@ -1312,16 +1312,20 @@ hipError_t launch_prefill(const PrefixParams& p, const FusedParams& f, int dtype
                           int mb, int n_items, hipStream_t s) {
   const unsigned blocks = (unsigned)(n_items * p.hkv);
   if (blocks == 0) return hipSuccess;
-#define BSP_PRE(TT, DD, MBB, KTT) \
-  prefix_mfma_kernel<TT, DD, MBB, KTT, (DD == 256 && MBB == 1 ? 2 : 4), 3, false><<<blocks, 256, 0, s>>>(p, f)
+// 64-key tiles in two stages at head_dim 128 and one or two query blocks per
+// wave (as in the fused step: ~5% faster on short chunks), else four stages.
+#define BSP_PRE(TT, DD, MBB, KTT)                                                   \
+  prefix_mfma_kernel<TT, DD, MBB, KTT,                                             \
+                     (KTT == 64 && DD == 128) || (DD == 256 && MBB == 1) ? 2 : 4, 3, \
+                     false><<<blocks, 256, 0, s>>>(p, f)
 #define BSP_PRE_T(TT)                                      \
   if (head_dim == 64) {                                    \
     if (mb == 1) BSP_PRE(TT, 64, 1, 64);                   \
     else if (mb == 2) BSP_PRE(TT, 64, 2, 64);              \
     else BSP_PRE(TT, 64, 3, 64);                           \
   } else if (head_dim == 128) {                            \
-    if (mb == 1) BSP_PRE(TT, 128, 1, 32);                  \
-    else if (mb == 2) BSP_PRE(TT, 128, 2, 32);             \
+    if (mb == 1) BSP_PRE(TT, 128, 1, 64);                  \
+    else if (mb == 2) BSP_PRE(TT, 128, 2, 64);             \
     else BSP_PRE(TT, 128, 3, 32);                          \
   } else {                                                 \
     if (mb == 1) BSP_PRE(TT, 256, 1, 32);                  \
@@ -1355,14 +1359,14 @@ hipError_t launch_mixed_step(const PrefixParams& dp, const FusedParams& df, cons
   const int n_pre = n_pre_items * pp.hkv;
   const unsigned blocks = (unsigned)(n_dec + n_pre);
   if (blocks == 0) return hipSuccess;
-#define BSP_MIX(TT, DD, KTT) \
-  mixed_step_kernel<TT, DD, KTT, 4><<<blocks, 256, 0, s>>>(dp, df, pp, pf, n_dec, n_pre)
+#define BSP_MIX(TT, DD, KTT, NS) \
+  mixed_step_kernel<TT, DD, KTT, NS><<<blocks, 256, 0, s>>>(dp, df, pp, pf, n_dec, n_pre)
   if (dtype == BSP_F16) {  // head_dim 64 or 128 (mixed_step_supported)
-    if (head_dim == 64) BSP_MIX(_Float16, 64, 64);
-    else BSP_MIX(_Float16, 128, 32);
+    if (head_dim == 64) BSP_MIX(_Float16, 64, 64, 4);
+    else BSP_MIX(_Float16, 128, 64, 2);
   } else {
-    if (head_dim == 64) BSP_MIX(__bf16, 64, 64);
-    else BSP_MIX(__bf16, 128, 32);
+    if (head_dim == 64) BSP_MIX(__bf16, 64, 64, 4);
+    else BSP_MIX(__bf16, 128, 64, 2);
   }
 #undef BSP_MIX
   return hipGetLastError();

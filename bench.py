@@ -39,6 +39,10 @@ WORKLOADS = {
                  "pages shuffled, 128 requests x beam 96, prompts U{2800..3200}, tails U{0..8}",
     "qwen3_4b": "Qwen3-4B-like layer: 32 Q / 8 KV heads, head_dim 128, fp16, 32-token pages, "
                 "64 requests x beam 30, prompts U{1600..2400}, tails U{1..4}",
+    "qwen3_4b_d64": "Qwen3-4B-like layer at head_dim 64: 32 Q / 8 KV heads, fp16, 32-token pages, "
+                    "64 requests x beam 30, prompts U{1600..2400}, tails U{1..4}",
+    "qwen3_4b_d256": "Qwen3-4B-like layer at head_dim 256: 32 Q / 8 KV heads, fp16, 32-token pages, "
+                     "64 requests x beam 30, prompts U{1600..2400}, tails U{1..4}",
     "nsample": "n-sample prefix sharing (parallel sampling): 16 Q / 8 KV heads, head_dim 128, bf16, "
                "32-token pages, 64 prompts x 16 samples, prompts U{400..600}, each sample's own "
                "tail U{8..32}",

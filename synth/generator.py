@@ -124,6 +124,11 @@ BEAM_CONFIGS = {
     # Qwen3-4B-like layer (head_dim 64/256 variants via make_beam_step(head_dim=...)).
     "qwen3_4b": BeamConfig("qwen3_4b", 64, 30, 32, 8, 128, "f16", 32,
                            (1600, 2400), (1, 4), False),
+    # the same layer at head_dim 64 and 256 (same token counts)
+    "qwen3_4b_d64": BeamConfig("qwen3_4b_d64", 64, 30, 32, 8, 64, "f16", 32,
+                               (1600, 2400), (1, 4), False),
+    "qwen3_4b_d256": BeamConfig("qwen3_4b_d256", 64, 30, 32, 8, 256, "f16", 32,
+                                (1600, 2400), (1, 4), False),
     # n-sample prefix sharing (parallel sampling): 16 samples of each prompt,
     # each attending the shared prompt and its own 8-32 generated tokens.
     "nsample": BeamConfig("nsample", 64, 16, 16, 8, 128, "bf16", 32,
