@@ -36,12 +36,15 @@ def _applied(inp):
 
 # ------------------------------------------------------------------ merge
 
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16", "f16"])
-@pytest.mark.parametrize("n_parts", [1, 2, 5, 13, 55])
-def test_merge_matches_oracle(out_dtype, n_parts):
-    say(f"merge out={out_dtype} parts={n_parts}")
+@pytest.mark.parametrize("n_parts", [1, 2, 5, 13, 55, 64, 65, 130])
+def test_merge_matches_oracle(out_dtype, n_parts, D):
+    """Both merge kernels: per-element (<= 8 parts) and per (row, head) workgroup,
+    its register form (<= 64 parts) and its looping form (more)."""
+    say(f"merge out={out_dtype} parts={n_parts} D={D}")
     rng = np.random.default_rng(n_parts)
-    rows, heads, D = 37, 6, 128
+    rows, heads = 37, 6
     o = rng.standard_normal((n_parts, rows, heads, D)).astype(np.float32)
     lse = (rng.standard_normal((n_parts, rows, heads)) * 3).astype(np.float32)
     lse[0, :5] = -np.inf                   # some parts empty
