@@ -178,6 +178,20 @@ def test_kernel_entry_points_refuse_unplanned_plan_before_any_launch():
         == "BSP_ERR_ARG"
 
 
+def test_prefix_attn_two_checks_its_plans_before_any_launch():
+    inp = synth.make_beam_step(PLAN_CFG, 5)
+    a, b = _host_plan(inp), _host_plan(inp)
+    fake = 1 << 20  # never dereferenced: the status is returned before any launch
+    two = lambda x, y: _status(lambda: B.bsp_prefix_attn_two(  # noqa: E731
+        x, y, fake, fake, fake, fake, fake, fake, fake, stream=0))[0]
+    assert two(a, a) == "BSP_ERR_ARG"                   # the same plan twice
+    assert two(a, b) == "BSP_ERR_STALE_PLAN"            # neither planned
+    B.bsp_plan(b, inp.batch, inp.beam, 1, inp.prefix_len, inp.seq_len, inp.block_tables)
+    assert two(a, b) == "BSP_ERR_STALE_PLAN"            # the first not planned
+    B.bsp_plan(a, inp.batch, inp.beam, 1, inp.prefix_len, inp.seq_len, inp.block_tables)
+    assert two(a, b) == "BSP_ERR_ARG"                   # host-only plans never launch
+
+
 def test_plan_create_rejects_bad_geometry():
     def create(**kw):
         base = dict(num_q_heads=4, num_kv_heads=2, head_dim=128, page_size=32, num_pages=10,
