@@ -714,6 +714,7 @@ static bsp_status_t prefix_params(bsp_plan_s* pl, const void* q, const void* k_p
   p.n_split = pl->n_split;
   p.split_keys = pl->split_keys;
   p.n_qtiles = (int32_t)ceil_div(pl->rows_per_req, pl->prefix_rpt);
+  p.xcd_remap = p.n_qtiles > 1 && (int64_t)p.B * p.hkv * p.n_split % 8 == 0 ? 1 : 0;
   p.causal = d.mask == BSP_MASK_CAUSAL ? 1 : 0;
   p.rows_total = pl->B * pl->W * pl->q_len;
   p.scale = d.sm_scale;
@@ -808,6 +809,7 @@ bsp_status_t decode_params(bsp_plan_s* pl, const void* q, const void* k_new, con
   p.split_keys = 0;
   const int rows_per_tile = bsp::prefix_rows_per_tile(d.dtype, d.head_dim, pl->rows_per_req);
   p.n_qtiles = (int32_t)ceil_div(pl->rows_per_req, rows_per_tile);
+  p.xcd_remap = p.n_qtiles > 1 && (int64_t)p.B * p.hkv % 8 == 0 ? 1 : 0;
   p.causal = 0;
   p.rows_total = pl->B * pl->W;
   p.scale = d.sm_scale;

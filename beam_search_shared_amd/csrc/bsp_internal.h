@@ -101,6 +101,9 @@ struct PrefixParams {
   int32_t page_shift;   // log2(page_size)
   int32_t num_pages;
   int32_t n_split, split_keys, n_qtiles;
+  // 1: the query tiles of one work item take block ids 8 apart (one XCD, one
+  // L2 for the keys they all read); needs B * hkv * n_split % 8 == 0
+  int32_t xcd_remap;
   int32_t causal;
   int32_t rows_total;   // B * W * q_len (prefill: packed rows)
   const int32_t* items; // prefill: work list, (request, query tile) int32 pairs

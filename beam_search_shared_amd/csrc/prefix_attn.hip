@@ -268,8 +268,18 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
       sg_hi0 = p.split_keys > 0 ? min(lim, sg_lo0 + p.split_keys) : lim;
       if (sg_hi0 < sg_lo0) sg_hi0 = sg_lo0;
     } else {
-      w.qt = bid % p.n_qtiles;
-      bid /= p.n_qtiles;
+      if (p.xcd_remap) {
+        // Workgroups are dealt to the 8 XCDs in turn, so block ids 8 apart
+        // share an XCD and its L2: the query tiles of one work item go there
+        // and read its keys from one L2 rather than from eight.
+        const int lo = bid & 7;
+        const int rest = bid >> 3;
+        w.qt = rest % p.n_qtiles;
+        bid = (rest / p.n_qtiles) * 8 + lo;
+      } else {
+        w.qt = bid % p.n_qtiles;
+        bid /= p.n_qtiles;
+      }
       w.split = bid % p.n_split;
       bid /= p.n_split;
       w.g = bid % p.hkv;
@@ -1214,9 +1224,12 @@ __global__ __launch_bounds__(256) void prefix_simt_kernel(PrefixParams p) {
 }
 
 // Query-row blocks of 16 per wave for an M-row item (4 waves per workgroup).
+// At head_dim 256 a 128-row tile needs more than half a SIMD's registers (one
+// workgroup per CU); 64-row tiles at two per CU, the tiles of a request on one
+// XCD, measured 6% faster (280 vs 297 us on the 4B-like layer at head_dim 256).
 static int pick_mb(int head_dim, int rows_per_req) {
   const int mb = (rows_per_req + 63) / 64;
-  const int cap = head_dim == 256 ? 2 : 3;
+  const int cap = head_dim == 256 ? 1 : 3;
   return mb < 1 ? 1 : (mb > cap ? cap : mb);
 }
 
@@ -1260,9 +1273,8 @@ static void launch_mfma(const PrefixParams& p, const FusedParams& f, int head_di
       } else {
         BSP_PFX(128, 3, 32, 4);
       }
-    } else {
-      if (mb == 1) BSP_PFX(256, 1, 32, 2);
-      else BSP_PFX(256, 2, 32, 4);
+    } else {  // pick_mb: one query block per wave at head_dim 256
+      BSP_PFX(256, 1, 32, 2);
     }
   }
 #undef BSP_PFX
