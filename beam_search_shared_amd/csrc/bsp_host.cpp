@@ -100,6 +100,7 @@ struct bsp_plan_s {
   int32_t B = 0, W = 0, q_len = 0, tail_pad = 0, n_split = 1, rows_per_req = 0, n_pairs = 0;
   int32_t split_keys = 0;  // keys per split of the current step (0: one pass)
   int32_t prefix_rpt = 0;  // query rows per work item of bsp_prefix_attn
+  bool order_on = false;   // the fused step takes requests longest prompt first
   void* ws_d = nullptr;
   void* zeroed_ws = nullptr;  // workspace whose header this plan has cleared
   std::vector<ReqInfo> h_req;
@@ -113,11 +114,16 @@ struct bsp_plan_s {
 namespace {
 
 size_t req_offset() { return bsp::kHeaderBytes; }
-size_t pages_offset(int32_t B) { return align_up(bsp::kHeaderBytes + sizeof(ReqInfo) * B, 16); }
+// header | ReqInfo[B] | ReqInfo[B] longest prompt first (beam plans) | page table
+size_t order_offset(int32_t B) { return bsp::kHeaderBytes + sizeof(ReqInfo) * B; }
+size_t pages_offset(int32_t B) { return align_up(bsp::kHeaderBytes + 2 * sizeof(ReqInfo) * B, 16); }
 
 DevHeader* dev_header(const bsp_plan_s* pl) { return static_cast<DevHeader*>(pl->ws_d); }
 const ReqInfo* dev_req(const bsp_plan_s* pl) {
   return reinterpret_cast<const ReqInfo*>(static_cast<char*>(pl->ws_d) + req_offset());
+}
+const ReqInfo* dev_req_order(const bsp_plan_s* pl) {
+  return reinterpret_cast<const ReqInfo*>(static_cast<char*>(pl->ws_d) + order_offset(pl->B));
 }
 const int32_t* dev_pages(const bsp_plan_s* pl) {
   return reinterpret_cast<const int32_t*>(static_cast<char*>(pl->ws_d) + pages_offset(pl->B));
@@ -433,6 +439,33 @@ bsp_status_t bsp_plan(bsp_plan_t pl, int32_t B, int32_t W, int32_t q_len,
   char* st = static_cast<char*>(pl->staging[slot]);
   std::memset(st, 0, bsp::kHeaderBytes);
   std::memcpy(st + req_offset(), req.data(), sizeof(ReqInfo) * B);
+  // The fused step's work order: longest prompt first, when the step is one
+  // round of workgroups over long prompts. Blocks are dispatched in order, so
+  // the longest requests then start first and the shorter ones fill in behind:
+  // 3% faster on 64 requests of 1.6-2.4k-token prompts (head_dim 64 and 128),
+  // 2% slower on 400-600-token prompts, where the lookup of the request before
+  // its own loads costs more than the order gains.
+  int32_t p_longest = 0;
+  for (int b = 0; b < B; ++b) p_longest = std::max(p_longest, req[b].prefix);
+  const int rows_g = W * q_len * (d.num_q_heads / d.num_kv_heads);
+  const int64_t fused_blocks =
+      (int64_t)B * d.num_kv_heads *
+      ceil_div(rows_g, bsp::prefix_rows_per_tile(d.dtype, d.head_dim, rows_g));
+  const bool order_on = q_len == 1 && !cached && d.dtype != BSP_F32 && p_longest >= 1024 &&
+                        fused_blocks <= bsp::kFillBlocks && d.head_dim <= 128 &&
+                        bsp::prefix_rows_per_tile(d.dtype, d.head_dim, rows_g) == 128;
+  if (order_on) {
+    // each entry carries its request index in q_off (unused by beam plans)
+    std::vector<int32_t> order(B);
+    for (int b = 0; b < B; ++b) order[b] = b;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int32_t x, int32_t y) { return req[x].prefix > req[y].prefix; });
+    ReqInfo* ro = reinterpret_cast<ReqInfo*>(st + order_offset(B));
+    for (int k = 0; k < B; ++k) {
+      ro[k] = req[order[k]];
+      ro[k].q_off = order[k];
+    }
+  }
   int32_t* pg_out = reinterpret_cast<int32_t*>(st + pages_offset(B));
   std::vector<int32_t> pages((size_t)total_pages);
   for (int b = 0; b < B; ++b)
@@ -508,6 +541,7 @@ bsp_status_t bsp_plan(bsp_plan_t pl, int32_t B, int32_t W, int32_t q_len,
   pl->n_split = n_split;
   pl->split_keys = split_keys;
   pl->prefix_rpt = prefix_rpt;
+  pl->order_on = order_on;
   pl->rows_per_req = W * q_len * (d.num_q_heads / d.num_kv_heads);
   pl->n_pairs = n_pairs;
   pl->h_pairs = std::move(pairs);
@@ -641,6 +675,7 @@ bsp_status_t bsp_plan_prefill(bsp_plan_t pl, int32_t C, const int32_t* q_len_h,
   pl->rows_per_req = 0;
   pl->n_pairs = 0;
   pl->h_pairs.clear();
+  pl->order_on = false;
   pl->prefill = true;
   pl->rows_total = (int32_t)rows;
   pl->n_items = (int32_t)items.size();
@@ -795,6 +830,7 @@ bsp_status_t decode_params(bsp_plan_s* pl, const void* q, const void* k_new, con
   p.k_pool = k_pool;
   p.v_pool = v_pool;
   p.req = dev_req(pl);
+  p.req_order = pl->order_on ? dev_req_order(pl) : nullptr;
   p.pages = dev_pages(pl);
   p.hdr = dev_header(pl);
   p.B = pl->B;

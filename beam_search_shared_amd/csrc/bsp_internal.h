@@ -95,6 +95,10 @@ struct PrefixParams {
   float* o_part;
   float* lse_part;
   const ReqInfo* req;
+  // fused step: the same requests, longest prompt first, each with q_off = its
+  // request index (blocks are dispatched in order, so the longest start first);
+  // null: plan order
+  const ReqInfo* req_order;
   const int32_t* pages;
   DevHeader* hdr;
   int32_t B, W, q_len, hq, hkv, group;

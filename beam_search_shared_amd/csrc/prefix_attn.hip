@@ -179,7 +179,9 @@ __device__ __forceinline__ int32_t resolve_fused_slot(const PrefixParams& p, con
 // MODE 4: a mixed step in one launch: each workgroup is either a MODE 1 item
 // of the beam step or a MODE 3 item of the context requests (`pre`), with
 // that part's parameters.
-template <typename T, int D, int MB, int KT, int NST, int MODE, bool PAIR>
+// ORD: the fused step takes its requests from the plan's longest-first copy
+// (a variant of its own, so that the other kernels compile without the lookup).
+template <typename T, int D, int MB, int KT, int NST, int MODE, bool PAIR, bool ORD = false>
 __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int block, bool pre) {
   // FUSED / PREFILL: the workgroup may be a beam-step / context item; `fused`
   // and `is_pre` say which one it is.
@@ -212,6 +214,9 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
   bool sg_share0 = false, sg_share1 = false;
   int pair_idx = 0, pair_role = 0;
   WorkItem w;
+  // the fused step reads its request from the plan's longest-first copy
+  const bool fused_order = ORD && FUSED && !PAIR && !is_pre && p.req_order != nullptr;
+  ReqInfo ri_ord{};
   {
     int bid = block;
     if constexpr (PAIR) {
@@ -284,7 +289,11 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
       bid /= p.n_split;
       w.g = bid % p.hkv;
       sg_b0 = bid / p.hkv;
-      const int valid = p.req[sg_b0].valid;
+      if (fused_order) {  // the fused step: longest prompts in the first blocks
+        ri_ord = p.req_order[sg_b0];
+        sg_b0 = ri_ord.q_off;
+      }
+      const int valid = fused_order ? ri_ord.valid : p.req[sg_b0].valid;
       sg_lo0 = p.split_keys > 0 ? w.split * p.split_keys : 0;
       sg_hi0 = p.split_keys > 0 ? min(valid, sg_lo0 + p.split_keys) : valid;
       if (sg_hi0 < sg_lo0) sg_hi0 = sg_lo0;
@@ -309,7 +318,7 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform by construction
   const int l16 = lane & 15;
   const int l4 = lane >> 4;
-  const ReqInfo ri = p.req[w.b];
+  const ReqInfo ri = fused_order ? ri_ord : p.req[w.b];
 
   const int M = is_pre ? ri.tail * p.group : p.W * p.q_len * p.group;
   // Rows per wave: 16 per query block; in the fused step with one block per
@@ -1080,10 +1089,10 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
   }  // segments
 }
 
-template <typename T, int D, int MB, int KT, int NST, int MODE, bool PAIR>
+template <typename T, int D, int MB, int KT, int NST, int MODE, bool PAIR, bool ORD = false>
 __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma_kernel(PrefixParams p,
                                                                                           FusedParams f) {
-  prefix_body<T, D, MB, KT, NST, MODE, PAIR>(p, f, blockIdx.x, false);
+  prefix_body<T, D, MB, KT, NST, MODE, PAIR, ORD>(p, f, blockIdx.x, false);
 }
 
 // A mixed step in one launch: n_dec beam-step workgroups (dp, df) and n_pre
@@ -1244,6 +1253,18 @@ static void launch_mfma(const PrefixParams& p, const FusedParams& f, int head_di
                         unsigned blocks, hipStream_t s) {
 #define BSP_PFX(DD, MBB, KTT, NS) \
   prefix_mfma_kernel<T, DD, MBB, KTT, NS, MODE, PAIR><<<blocks, 256, 0, s>>>(p, f)
+  // the fused step in the plan's longest-first order (only where the plan turns
+  // it on: two query blocks per wave, head_dim 64 or 128)
+  if constexpr (MODE == 1 && !PAIR) {
+    if (p.req_order != nullptr && mb == 2 && head_dim == 128) {
+      prefix_mfma_kernel<T, 128, 2, 64, 2, 1, false, true><<<blocks, 256, 0, s>>>(p, f);
+      return;
+    }
+    if (p.req_order != nullptr && mb == 2 && head_dim == 64) {
+      prefix_mfma_kernel<T, 64, 2, 64, 4, 1, false, true><<<blocks, 256, 0, s>>>(p, f);
+      return;
+    }
+  }
   if constexpr (PAIR) {  // MB <= 2, head_dim <= 128
     if (head_dim == 64) {
       if (mb == 1) BSP_PFX(64, 1, 64, 4);
