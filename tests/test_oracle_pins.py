@@ -508,3 +508,139 @@ def test_cached_prefix_row_subset_is_the_full_result_restricted():
     rows = [39, 0, 17, 18]
     so, sl = oracle.cached_prefix_attention(inp, causal=True, rows=rows)
     assert np.array_equal(so, o[rows]) and np.array_equal(sl, lse[rows])
+
+
+# --------------------------- pins of the partial-state and sampling helpers
+
+def test_beam_attention_one_equals_the_full_result_bit_for_bit():
+    """Every beam's ``beam_attention_one`` is exactly that beam's slice of
+    ``beam_decode_attention`` (the full-size GPU tests compare sampled beams
+    against it)."""
+    inp = _applied(synth.make_beam_step(PIN_CFG, 12, keep_logical=True, page_stride=2))
+    o, lse = oracle.beam_decode_attention(inp)
+    for b in range(inp.batch):
+        for k in range(inp.beam):
+            ob, lb = oracle.beam_attention_one(inp, b, k)
+            assert np.array_equal(ob, o[b, k]) and np.array_equal(lb, lse[b, k])
+
+
+def test_beam_attention_one_matches_50_digit_brute_force():
+    """One beam against an independent evaluation over its logical sequence: a
+    wrong key count (``range(seq_len)`` off by one) would drop or add a key."""
+    inp = _applied(synth.make_beam_step(PIN_CFG, 13, keep_logical=True, tail_range=(2, 4)))
+    scale = 1.0 / math.sqrt(inp.head_dim)
+    G = inp.num_q_heads // inp.num_kv_heads
+    for b, k in ((0, 0), (inp.batch - 1, inp.beam - 1), (1, 1)):
+        K, V = _logical_sequence(inp, b, k)
+        assert K.shape[0] == int(inp.seq_len[b])
+        ob, lb = oracle.beam_attention_one(inp, b, k)
+        for h in range(inp.num_q_heads):
+            mo, ml = _mp_attention(inp.q[b, k, 0, h], K[:, h // G], V[:, h // G], scale)
+            assert abs(float(ml) - lb[0, h]) <= 1e-12
+            assert max(abs(float(x) - y) for x, y in zip(mo, ob[0, h])) <= 1e-12
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_beam_partial_attention_matches_brute_force_on_each_side_of_the_prompt_end(seed):
+    """The prefix part is the prompt rows ``j < P_b`` and the tail part the rows
+    ``P_b <= j < S_b`` read through the parents, both rebuilt from the
+    generator's logical draws (no page table): a boundary off by one at ``P_b``
+    moves a key from one part to the other and fails both checks, although the
+    merge of the two would still equal the whole."""
+    inp = _applied(synth.make_beam_step(PIN_CFG, seed, keep_logical=True, tail_range=(1, 4)))
+    po, pl = oracle.beam_partial_attention(inp, "prefix")
+    to, tl = oracle.beam_partial_attention(inp, "tail")
+    scale = 1.0 / math.sqrt(inp.head_dim)
+    G = inp.num_q_heads // inp.num_kv_heads
+    for b in range(inp.batch):
+        P = int(inp.prefix_len[b])
+        for k in range(inp.beam):
+            K, V = _logical_sequence(inp, b, k)
+            for h in range(inp.num_q_heads):
+                g = h // G
+                for part_o, part_l, rows in ((po, pl, slice(0, P)), (to, tl, slice(P, None))):
+                    mo, ml = _mp_attention(inp.q[b, k, 0, h], K[rows, g], V[rows, g], scale)
+                    if K[rows].shape[0] == 0:
+                        assert np.isneginf(part_l[b, k, 0, h])
+                        assert (part_o[b, k, 0, h] == 0).all()
+                        continue
+                    assert abs(float(ml) - part_l[b, k, 0, h]) <= 1e-12
+                    assert max(abs(float(x) - y)
+                               for x, y in zip(mo, part_o[b, k, 0, h])) <= 1e-12
+
+
+def test_beam_partial_attention_prompt_part_ignores_the_tail():
+    """Changing every tail row (and the current token) leaves the prefix part
+    bit-identical and changes the tail part: the two parts really split at P_b."""
+    a = _applied(synth.make_beam_step(PIN_CFG, 4, tail_range=(2, 4)))
+    b = _applied(synth.make_beam_step(PIN_CFG, 4, tail_range=(2, 4)))
+    for r in range(b.batch):
+        P, S = int(b.prefix_len[r]), int(b.seq_len[r])
+        for k in range(b.beam):
+            pages, rows = oracle.sequence_slots(r, k, b.prefix_len, b.seq_len, b.block_tables,
+                                                b.cache_indirection, b.page_size, range(P, S))
+            b.k_pool[pages, :, rows, :] += 1.0
+            b.v_pool[pages, :, rows, :] -= 1.0
+    pa = oracle.beam_partial_attention(a, "prefix")
+    pb = oracle.beam_partial_attention(b, "prefix")
+    assert np.array_equal(pa[0], pb[0]) and np.array_equal(pa[1], pb[1])
+    ta = oracle.beam_partial_attention(a, "tail")
+    tb = oracle.beam_partial_attention(b, "tail")
+    assert np.abs(ta[0] - tb[0]).max() > 0.1
+
+
+def _mp_cached_rows(inp, i, h, rows, new_rows, scale):
+    g = h // (inp.num_q_heads // inp.num_kv_heads)
+    K = np.concatenate([inp.cache_k[list(rows), g], inp.new_k[list(new_rows), g]]).astype(np.float64)
+    V = np.concatenate([inp.cache_v[list(rows), g], inp.new_v[list(new_rows), g]]).astype(np.float64)
+    return _mp_attention(inp.q[i, h], K, V, scale)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_cached_prefix_partial_matches_50_digit_brute_force(causal):
+    """The cache segment over explicit key ranges (including ranges that cross
+    the valid length, start past it, or hold one row) and the new-row segment,
+    each against an independent evaluation over the rows the definition names:
+    cache rows ``lo <= r < min(hi, L)`` and new rows ``i' <= i`` (causal) or all."""
+    L, Sq = 13, 4
+    inp = synth.make_cached_prefix(21, valid_rows=L, q_len=Sq, num_q_heads=4, num_kv_heads=2,
+                                   head_dim=8, dtype="f32", max_cache_rows=32)
+    scale = 1.0 / math.sqrt(8)
+    ranges = [None, (0, 5), (5, 13), (12, 13), (4, 20), (13, 32), (0, 1)]
+    for kr in ranges:
+        o, lse = oracle.cached_prefix_partial(inp, "cache", causal=causal, key_range=kr)
+        lo, hi = (0, L) if kr is None else (kr[0], min(kr[1], L))
+        rows = range(lo, hi)
+        for i in range(Sq):
+            for h in range(4):
+                if len(rows) == 0:
+                    assert np.isneginf(lse[i, h]) and (o[i, h] == 0).all()
+                    continue
+                mo, ml = _mp_cached_rows(inp, i, h, rows, [], scale)
+                assert abs(float(ml) - lse[i, h]) <= 1e-12, (kr, i, h)
+                assert max(abs(float(x) - y) for x, y in zip(mo, o[i, h])) <= 1e-12
+    o, lse = oracle.cached_prefix_partial(inp, "new", causal=causal)
+    for i in range(Sq):
+        new = range(i + 1) if causal else range(Sq)
+        for h in range(4):
+            mo, ml = _mp_cached_rows(inp, i, h, [], new, scale)
+            assert abs(float(ml) - lse[i, h]) <= 1e-12
+            assert max(abs(float(x) - y) for x, y in zip(mo, o[i, h])) <= 1e-12
+
+
+@pytest.mark.parametrize("L,cuts", [(0, [0, 256]), (1, [0, 64, 128]), (300, [0, 64, 256, 512]),
+                                    (777, [0, 192, 384, 576, 768, 960]),
+                                    (1024, [0, 256, 512, 768, 1024])])
+def test_cached_prefix_partials_merge_to_the_whole_call(L, cuts):
+    """Splitting the cache segment at chunk boundaries and merging every chunk's
+    partial with the new-row segment gives the whole call (to rounding), for
+    chunks that end inside, at or past the valid length."""
+    inp = synth.make_cached_prefix(L + 3, valid_rows=L, q_len=5, num_q_heads=6, num_kv_heads=2,
+                                   head_dim=16, dtype="f16", max_cache_rows=1024)
+    for causal in (True, False):
+        full_o, full_l = oracle.cached_prefix_attention(inp, causal=causal)
+        parts = [oracle.cached_prefix_partial(inp, "cache", causal=causal, key_range=(a, b))
+                 for a, b in zip(cuts[:-1], cuts[1:])]
+        parts.append(oracle.cached_prefix_partial(inp, "new", causal=causal))
+        mo, ml = oracle.merge_states([p[0] for p in parts], [p[1] for p in parts])
+        assert np.abs(mo - full_o).max() <= 1e-12 and np.abs(ml - full_l).max() <= 1e-12
