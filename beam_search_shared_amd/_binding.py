@@ -17,7 +17,9 @@ from typing import Optional
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libbsp.so")
+# BSP_LIBRARY names another build of the same ABI (the sanitized host-only build
+# the CPU tests load); by default the in-tree gfx950 library.
+LIB_PATH = os.environ.get("BSP_LIBRARY") or os.path.join(HERE, "libbsp.so")
 HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "bsp.h")
 
 BSP_F32, BSP_F16, BSP_BF16 = 0, 1, 2

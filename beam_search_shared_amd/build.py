@@ -61,6 +61,49 @@ def build(jobs: int = 8, verbose: bool = True) -> str:
     return OUT
 
 
+HOST_ONLY_SOURCES = ["bsp_host.cpp", "host_only_stubs.cpp"]
+SANITIZE = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer"]
+
+
+def build_host_sanitized(out_dir: str) -> str:
+    """Build the host planner alone (no GPU code: every launcher is a stub) with a
+    plain C++ compiler and the address and undefined-behaviour sanitizers, for the
+    CPU tests of the host logic. Returns the path of the shared library; load it
+    with the sanitizer runtimes preloaded (``sanitizer_runtimes()``)."""
+    cxx = os.environ.get("CXX", "g++")
+    os.makedirs(out_dir, exist_ok=True)
+    objs = []
+    for src in HOST_ONLY_SOURCES:
+        obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".san.o")
+        cmd = [cxx, "-std=c++17", "-O1", "-g", "-fPIC", "-D__HIP_PLATFORM_AMD__",
+               "-I/opt/rocm/include", *SANITIZE, "-c", os.path.join(CSRC, src), "-o", obj]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+        objs.append(obj)
+    out = os.path.join(out_dir, "libbsp_host_sanitized.so")
+    cmd = [cxx, "-shared", *SANITIZE, *objs, "-L/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib",
+           "-lamdhip64", "-o", out]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    return out
+
+
+def sanitizer_runtimes() -> list:
+    """The compiler's address and undefined-behaviour sanitizer runtimes (to preload
+    into an uninstrumented Python that loads the sanitized library)."""
+    cxx = os.environ.get("CXX", "g++")
+    libs = []
+    for name in ("libasan.so", "libubsan.so"):
+        path = subprocess.run([cxx, f"-print-file-name={name}"], capture_output=True,
+                              text=True).stdout.strip()
+        if not os.path.isabs(path) or not os.path.exists(path):
+            raise RuntimeError(f"{name} not found for {cxx}")
+        libs.append(path)
+    return libs
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=min(8, os.cpu_count() or 1))

@@ -1232,21 +1232,6 @@ __global__ __launch_bounds__(256) void prefix_simt_kernel(PrefixParams p) {
   if (lane == 0) p.lse_part[ohead] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
 }
 
-// Query-row blocks of 16 per wave for an M-row item (4 waves per workgroup).
-// At head_dim 256 a 128-row tile needs more than half a SIMD's registers (one
-// workgroup per CU); 64-row tiles at two per CU, the tiles of a request on one
-// XCD, measured 6% faster (280 vs 297 us on the 4B-like layer at head_dim 256).
-static int pick_mb(int head_dim, int rows_per_req) {
-  const int mb = (rows_per_req + 63) / 64;
-  const int cap = head_dim == 256 ? 1 : 3;
-  return mb < 1 ? 1 : (mb > cap ? cap : mb);
-}
-
-int prefix_rows_per_tile(int dtype, int head_dim, int rows_per_req) {
-  if (dtype == BSP_F32) return 4;
-  return 64 * pick_mb(head_dim, rows_per_req);
-}
-
 // Tile size and pipeline depth per head_dim: 64 KB of K/V stages per workgroup.
 template <typename T, int MODE, bool PAIR>
 static void launch_mfma(const PrefixParams& p, const FusedParams& f, int head_dim, int mb,

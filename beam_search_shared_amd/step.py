@@ -153,6 +153,18 @@ def run_decode_step(s: BeamStepDevice, stream=None) -> None:
                       s.lse_out, stream)
 
 
+def paged_from_rows(rows: np.ndarray, page_size: int, num_pages: int,
+                    fill: float = float("nan")) -> np.ndarray:
+    """Lay a row array ``[n, Hkv, D]`` out as identity pages ``[num_pages, Hkv, ps, D]``
+    (host-side layout before the upload, no arithmetic on the values): page p
+    holds rows ``p*ps .. p*ps+ps-1``; rows past ``n`` hold ``fill``."""
+    n, hkv, d = rows.shape
+    assert num_pages * page_size >= n
+    out = np.full((num_pages * page_size, hkv, d), fill, dtype=np.float32)
+    out[:n] = rows
+    return np.ascontiguousarray(out.reshape(num_pages, page_size, hkv, d).transpose(0, 2, 1, 3))
+
+
 @dataclass
 class CachedPrefixDevice:
     dtype: str
@@ -193,8 +205,6 @@ def upload_cached_prefix(inp, device="cuda", page_size: int = 32, key_bucket: in
     ``kv_split`` defaults to -1: the plan picks the chunk per step (the
     smallest multiple of 64 keys whose work items fill one round of the chip).
     """
-    from synth import paged_from_rows  # layout only
-
     ps = page_size
     Sq, Hq, D = inp.q.shape
     Hkv = inp.cache_k.shape[1]

@@ -6,13 +6,19 @@ beam's tail, merged in one online softmax. The same step as four launches
 (bsp_write_kv + bsp_prefix_attn + bsp_tail_attn + bsp_merge) and the per-beam
 comparator are timed beside it. Consecutive timed steps rotate over
 several layers, each with its own KV pool, query and new-token buffers, so
-every step reads its prompt pages from HBM rather than from the 256 MB
-last-level cache (as consecutive layers of a model would). Inputs are seeded
-synthetic draws already resident in HBM when the timed region starts.
+that at least 512 MB of other layers' reads pass between two steps on the same
+layer and every step reads its prompt pages from HBM rather than from the
+256 MB last-level cache (as consecutive layers of a model would). Inputs are
+seeded synthetic draws already resident in HBM when the timed region starts.
+
+The default workload is the wide-beam recommendation shape (128 requests x
+beam 96, prompts of about 3k tokens: the largest single-GPU configuration);
+``--config`` selects the others.
 
 Prints one JSON line. The roofline entry is the step kernel: its algorithmic
 bytes per launch over its average duration from HIP events recorded on the
-launch stream around every timed launch.
+launch stream around the timed launches; a second pass with an event between
+consecutive launches gives the per-launch median, p10 and p90.
 """
 
 from __future__ import annotations
@@ -65,6 +71,33 @@ CACHED_ROWS = 10368
 CACHED_PREFILL_ROWS = 2000
 PREFILL_SHAPE = dict(batch=8, chunk_range=(1500, 2500), cached_range=(0, 0))
 MIXED_CTX_SHAPE = dict(batch=4, chunk_range=(400, 600), cached_range=(0, 0))
+# Bytes of other layers' data that pass between two reads of the same layer's
+# buffers: more than the 256 MB last-level cache, so that a timed step reads
+# its KV from HBM.
+FLUSH_BYTES = 512e6
+
+
+def rotation_layers(bytes_per_step: float, forced: int = 0) -> int:
+    """Layer copies to rotate over so that at least FLUSH_BYTES of other layers'
+    reads pass between two steps on the same copy."""
+    if forced:
+        return forced
+    return max(2, int(np.ceil(FLUSH_BYTES / max(bytes_per_step, 1.0))) + 1)
+
+
+def launch_percentiles(torch, fn, n, stream):
+    """Per-launch GPU durations (us) from HIP events recorded on the launch
+    stream between consecutive launches: median, p10, p90 over n launches."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(n):
+        fn(i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    d = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n)])
+    return {"median_us": float(np.median(d)), "p10_us": float(np.percentile(d, 10)),
+            "p90_us": float(np.percentile(d, 90)), "launches": n}
 
 
 KERNEL_SOURCES = ("beam_search_shared_amd/csrc/prefix_attn.hip",
@@ -252,8 +285,7 @@ def bench_prefill(args, torch, synth, B, S) -> dict:
     dev = "cuda"
     inp = synth.make_prefill("qwen3_0p6b", args.seed, garbage="unit", **PREFILL_SHAPE)
     flops, nbytes, _ = prefill_work(inp)
-    pool = inp.k_pool.size * 2 * EBYTES[inp.dtype]
-    layers = args.layers or max(2, int(np.ceil(1.0e9 / pool)))
+    layers = rotation_layers(nbytes, args.layers)
     base, copies = _prefill_copies(S, inp, dev, layers)
     stream = torch.cuda.current_stream()
     sync = lambda: B.bsp_check(base.plan)  # noqa: E731
@@ -296,8 +328,7 @@ def bench_mixed(args, torch, synth, B, S) -> dict:
     step_bytes, _ = algorithmic_bytes(gen)
     flops, ctx_bytes, _ = prefill_work(ctx)
     gbase = S.upload_beam_step(gen, dev)
-    pool = gbase.k_pool.numel() * gbase.k_pool.element_size() * 2
-    layers = args.layers or max(2, int(np.ceil(1.0e9 / pool)))
+    layers = rotation_layers(step_bytes + ctx_bytes, args.layers)
     gcopies = [gbase]
     for _ in range(layers - 1):
         c = S.BeamStepDevice(**{**gbase.__dict__})
@@ -390,8 +421,7 @@ def bench_cached(args, torch, synth, B, S, prefill: bool) -> dict:
 
     def copies_for(split):
         base = S.upload_cached_prefix(inp, dev, kv_split=split)
-        pool = base.k_pool.numel() * base.k_pool.element_size() * 2
-        layers = args.layers or max(2, int(np.ceil(1.0e9 / pool)))
+        layers = rotation_layers(nbytes, args.layers)
         cs = [base]
         for _ in range(layers - 1):
             c = S.CachedPrefixDevice(**{**base.__dict__})
@@ -518,11 +548,16 @@ def main() -> None:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="qwen3_0p6b", choices=sorted(WORKLOADS))
+    ap.add_argument("--config", default="wide_beam", choices=sorted(WORKLOADS))
     ap.add_argument("--layers", type=int, default=0,
-                    help="rotating layer copies (0: enough to exceed 1 GB of KV)")
+                    help="rotating layer copies (0: enough that 512 MB of other layers' reads "
+                         "pass between two steps on the same copy)")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--naive", action="store_true", help="also time the per-beam comparator")
+    ap.add_argument("--no-naive", action="store_true",
+                    help="do not time the per-beam comparator beside the step")
+    ap.add_argument("--naive-steps", type=int, default=5,
+                    help="timed steps of the per-beam comparator (it re-reads the prompt per "
+                         "beam and head: tens of ms per step on the wide-beam shape)")
     ap.add_argument("--skip-unfused", action="store_true",
                     help="do not time the four-launch (unfused) step beside the fused one")
     ap.add_argument("--warm-seconds", type=float, default=0.5,
@@ -558,8 +593,7 @@ def main() -> None:
     inp = synth.make_beam_step(args.config, args.seed, garbage="unit")
     step_bytes, _ = algorithmic_bytes(inp)
     base = S.upload_beam_step(inp, dev)
-    pool_bytes = base.k_pool.numel() * base.k_pool.element_size() * 2
-    layers = args.layers or max(2, int(np.ceil(1.0e9 / pool_bytes)))
+    layers = rotation_layers(step_bytes, args.layers)
     copies = [base]
     for _ in range(layers - 1):
         c = S.BeamStepDevice(**{**base.__dict__})
@@ -571,10 +605,16 @@ def main() -> None:
         c.k_new_beams = base.k_new_beams.clone()
         c.v_new_beams = base.v_new_beams.clone()
         copies.append(c)
-    t_plan = time.perf_counter()
-    S.plan_beam_step(base)
-    t_plan = time.perf_counter() - t_plan
+    # Host planning time (once per step for all layers): median of several plans of
+    # the same step, each after the previous plan's copy has completed.
+    plan_s = []
+    for _ in range(11):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        S.plan_beam_step(base)
+        plan_s.append(time.perf_counter() - t0)
     torch.cuda.synchronize()
+    t_plan = float(np.median(plan_s))
 
     stream = torch.cuda.current_stream()
 
@@ -647,7 +687,13 @@ def main() -> None:
         n_unf = max(10, args.steps // 4)
         usec, _ = timed(unfused, n_unf, 5)
         extra["unfused_4_launch_ms_per_step"] = usec / n_unf * 1e3
-    if args.naive:
+    # per-launch distribution of the step kernel (a separate pass with an event
+    # between consecutive launches)
+    pct = launch_percentiles(torch, fused, args.steps, stream)
+    B.bsp_check(base.plan)
+    if not args.no_naive:
+        # the per-beam comparator over the same KV: current-token write, then every
+        # beam attends its whole sequence, prompt re-read per beam and KV head
         out = torch.empty_like(base.out)
 
         def naive(i):
@@ -655,9 +701,10 @@ def main() -> None:
             S.write_current_tokens(c)
             B.bsp_naive_beam_attn(c.plan, c.q, c.k_pool, c.v_pool, c.block_tables,
                                   c.cache_indirection, out)
-        n_naive = max(3, min(20, args.steps // 10))
-        nsec, _ = timed(naive, n_naive, 2)
+        n_naive = max(1, args.naive_steps)
+        nsec, _ = timed(naive, n_naive, 1)
         extra["naive_per_beam_ms_per_step"] = nsec / n_naive * 1e3
+        extra["naive_steps_timed"] = n_naive
         extra["cascade_speedup_vs_naive"] = extra["naive_per_beam_ms_per_step"] / ms_per_step
 
     result = {
@@ -680,6 +727,7 @@ def main() -> None:
             "beam": inp.beam,
             "step": "bsp_decode_step (current-token write + shared prefix + tails, one launch)",
             "layers_rotated": layers,
+            "bytes_between_reuses": (layers - 1) * step_bytes,
             "warm_seconds": args.warm_seconds,
             "step_alg_bytes": step_bytes,
             "step_alg_gbps": step_bytes / (ms_per_step * 1e-3) / 1e9,
@@ -697,6 +745,9 @@ def main() -> None:
             "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "alg_bytes_per_launch": step_bytes,
             "avg_launch_us": fused_ms * 1e3,
+            "launch_us_median": pct["median_us"],
+            "launch_us_p10": pct["p10_us"],
+            "launch_us_p90": pct["p90_us"],
         },
     }
     if not args.no_cpu_baseline:

@@ -15,5 +15,4 @@ from .generator import (  # noqa: F401
     make_cached_prefix,
     make_prefill,
     round_to_dtype,
-    paged_from_rows,
 )

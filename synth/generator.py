@@ -493,19 +493,3 @@ def make_prefill(config, seed: int = 0, *, batch: int = 4, chunk_range: tuple = 
                          max_q_len=int(max_q_len if max_q_len is not None else chunk_range[1]),
                          q_len=Sq, cached_len=L, q=q, new_k=nk, new_v=nv, cache_k=ck, cache_v=cv,
                          k_pool=kp, v_pool=vp, block_tables=bt, slots=slots)
-
-
-def paged_from_rows(rows: np.ndarray, page_size: int, num_pages: Optional[int] = None,
-                    fill: float = np.nan) -> np.ndarray:
-    """Lay a row array ``[n, Hkv, D]`` out as identity pages ``[pages, Hkv, ps, D]``.
-
-    Page ``p`` holds rows ``p*ps .. p*ps+ps-1``; rows past ``n`` hold ``fill``.
-    Extra pages up to ``num_pages`` are filled with ``fill`` as well.
-    """
-    n, hkv, d = rows.shape
-    need = -(-n // page_size)
-    total = need if num_pages is None else num_pages
-    assert total >= need
-    out = np.full((total * page_size, hkv, d), fill, dtype=np.float32)
-    out[:n] = rows
-    return np.ascontiguousarray(out.reshape(total, page_size, hkv, d).transpose(0, 2, 1, 3))

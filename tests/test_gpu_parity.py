@@ -157,6 +157,46 @@ def test_tail_slots_bit_exact(seed):
         assert np.array_equal(_tail_slots_gpu(s, pad), ref)
 
 
+def test_tail_slots_bit_exact_1200_random_batches():
+    """The device's tail-slot resolution against the oracle's index function over
+    1200 random batches: page sizes 1..1024, page ids at stride 1 or 2 (pages at
+    even ids only), shuffled or in order, prompts that end exactly at a page
+    boundary (a full last prompt page) or one row into a page, empty tails and
+    tails that end at a page boundary."""
+    rng = np.random.default_rng(1200)
+    n_full_last = n_one_row = 0
+    for trial in range(1200):
+        ps = int(rng.choice([1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024]))
+        kind = trial % 4
+        if kind == 0:    # prompts that fill their last page
+            pr = (ps * int(rng.integers(0, 3)),) * 2
+        elif kind == 1:  # prompts one row into their last page
+            pr = (ps * int(rng.integers(0, 3)) + 1,) * 2
+        else:
+            pr = (0, int(rng.integers(1, 3 * ps + 2)))
+        cfg = BeamConfig("idx1200", batch=int(rng.integers(1, 5)), beam=int(rng.integers(1, 7)),
+                         num_q_heads=2, num_kv_heads=1, head_dim=64, dtype="bf16", page_size=ps,
+                         prefix_range=pr, tail_range=(0, int(rng.integers(0, 2 * ps + 3))),
+                         shuffle_pages=bool(rng.integers(0, 2)))
+        inp = synth.make_beam_step(cfg, trial, page_stride=int(rng.integers(1, 3)), garbage="unit")
+        n_full_last += int(((inp.prefix_len % ps) == 0).sum())
+        n_one_row += int(((inp.prefix_len % ps) == 1).sum())
+        s = S.upload_beam_step(inp, DEV)
+        S.plan_beam_step(s)
+        pad = s.plan.tail_len
+        ref = oracle.tail_slots(inp.prefix_len, inp.seq_len, inp.block_tables,
+                                inp.cache_indirection, inp.page_size, pad)
+        got = _tail_slots_gpu(s, pad)
+        if not np.array_equal(got, ref):
+            say(f"mismatch trial={trial} ps={ps} P={inp.prefix_len.tolist()} "
+                f"S={inp.seq_len.tolist()}")
+        assert np.array_equal(got, ref), trial
+        B.bsp_check(s.plan)
+    say(f"1200 batches: {n_full_last} prompts ending on a page boundary, "
+        f"{n_one_row} one row into a page")
+    assert n_full_last > 100 and n_one_row > 100
+
+
 def test_bad_cache_indirection_is_skipped_and_reported():
     inp = synth.make_beam_step("qwen3_0p6b", 5, batch=2, tail_range=(3, 4))
     s = S.upload_beam_step(inp, DEV)
@@ -279,6 +319,56 @@ def test_cached_prefix_decode_matches_oracle(L, split):
     for sp in range(c.n_split):
         po, pl = oracle.cached_prefix_partial(inp, "cache", key_range=(step * sp, step * (sp + 1)))
         assert_close(c.o_part[sp], c.lse_part[sp], po, pl, "f16", f"decode L={L} split {sp}")
+
+
+# 16 seeded draws of the valid length over the whole allocation, beside the edges
+RANDOM_L = [int(x) for x in np.random.default_rng(10368).integers(0, 10369, 16)]
+
+
+@pytest.mark.parametrize("L", RANDOM_L)
+def test_cached_prefix_decode_random_lengths(L):
+    """A one-row decode at the full 10368-row allocation, valid length drawn
+    uniformly: the output and every chunk's partial against the oracle."""
+    R = oracle.bucket_rows(L, 256, 10368)
+    inp = synth.make_cached_prefix(L % 13, valid_rows=L, q_len=1, nan_from_row=R)
+    c = S.upload_cached_prefix(inp, DEV)
+    S.plan_cached_prefix(c)
+    sk = c.plan_cache.split_keys
+    say(f"cached decode random L={L} R={R}: {c.n_split} chunks of {sk} keys")
+    S.run_cached_prefix(c)
+    B.bsp_check(c.plan_cache)
+    B.bsp_check(c.plan_new)
+    o, lse = oracle.cached_prefix_attention(inp, causal=True)
+    assert_close(c.out.reshape(1, 24, 128), c.lse_out.reshape(1, 24), o, lse, "f16",
+                 f"decode L={L}")
+    step = sk if sk > 0 else max(L, 1)
+    for sp in range(c.n_split):
+        po, pl = oracle.cached_prefix_partial(inp, "cache", key_range=(step * sp, step * (sp + 1)))
+        assert_close(c.o_part[sp], c.lse_part[sp], po, pl, "f16", f"decode L={L} split {sp}")
+
+
+@pytest.mark.parametrize("draw", range(16))
+def test_cached_prefix_prefill_random_lengths(draw):
+    """A prefill at the full 10368-row allocation with the valid length drawn from
+    U{0..10368} and the prompt from U{500..2000}: sampled query rows (first, last,
+    tile edges, random) against the oracle."""
+    rng = np.random.default_rng(7000 + draw)
+    L = int(rng.integers(0, 10369))
+    Sq = int(rng.integers(500, 2001))
+    R = oracle.bucket_rows(L, 256, 10368)
+    inp = synth.make_cached_prefix(draw, valid_rows=L, q_len=Sq, nan_from_row=R)
+    c = S.upload_cached_prefix(inp, DEV)
+    S.plan_cached_prefix(c)
+    say(f"cached prefill random L={L} Sq={Sq}: {c.n_split} chunks of {c.plan_cache.split_keys} keys")
+    S.run_cached_prefix(c)
+    B.bsp_check(c.plan_cache)
+    B.bsp_check(c.plan_new)
+    torch.cuda.synchronize()
+    rows = sorted({0, 1, 63, 64, Sq // 2, Sq - 2, Sq - 1} |
+                  {int(r) for r in rng.integers(0, Sq, 5)})
+    o, lse = oracle.cached_prefix_attention(inp, causal=True, rows=rows)
+    idx = torch.tensor(rows, device=DEV)
+    assert_close(c.out[idx], c.lse_out[idx], o, lse, "f16", f"prefill L={L} Sq={Sq}")
 
 
 @pytest.mark.parametrize("L,Sq,causal,split", [(0, 37, True, 0), (300, 64, True, 0),
