@@ -90,7 +90,7 @@ _SIGS = {
     "bsp_prefill_attn": (_I32, [_P, _P, _P, _P, _P, _P, _P]),
     "bsp_check": (_I32, [_P, _P]),
     "bsp_debug_plan_tables": (_I32, [_P, _P, _P, _P, _P, _P]),
-    "bsp_debug_plan_pairs": (_I32, [_P, _P, _P]),
+    "bsp_debug_plan_items": (_I32, [_P, _P, _P]),
     "bsp_debug_tail_slots": (_I32, [_P, _P, _P, _P, _P]),
 }
 
@@ -317,14 +317,15 @@ def bsp_debug_plan_tables(plan: Plan, B: int):
     return indptr, pages[:int(indptr[B])], n_keys, valid, tail
 
 
-def bsp_debug_plan_pairs(plan: Plan):
-    """The plan's balanced pairs as an int32 array [n_pairs][3] = (a, b, split)."""
+def bsp_debug_plan_items(plan: Plan):
+    """The fused step's work items as an int32 array [n_items][4] = (request,
+    first key, end key, chunks of that request), in dispatch order."""
     lib = load_library()
     n = np.zeros(1, np.int32)
-    _check(lib.bsp_debug_plan_pairs(plan.handle, _ptr(n), None))
-    pairs = np.zeros((max(int(n[0]), 1), 3), np.int32)
-    _check(lib.bsp_debug_plan_pairs(plan.handle, _ptr(n), _ptr(pairs)))
-    return pairs[:int(n[0])]
+    _check(lib.bsp_debug_plan_items(plan.handle, _ptr(n), None))
+    items = np.zeros((max(int(n[0]), 1), 4), np.int32)
+    _check(lib.bsp_debug_plan_items(plan.handle, _ptr(n), _ptr(items)))
+    return items[:int(n[0])]
 
 
 def bsp_debug_tail_slots(plan: Plan, block_tables, cache_indirection, slots_out,

@@ -15,6 +15,8 @@
 // Implementation).
 #include <algorithm>
 #include <array>
+#include <functional>
+#include <queue>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -69,8 +71,13 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 }  // namespace
 
-// automatic balanced pairs: longest prompt at least this many times the shortest
-constexpr int64_t kPairSpread = 3;
+// Cost model of the fused step's split (in keys of one KV head streamed by one
+// workgroup): the fixed work of a workgroup (its start, and the tails, output
+// and token write that end a request), and the partial-state traffic a split
+// adds, counted in keys of the same bytes. A split must shorten the modelled
+// step by this fraction to be taken.
+constexpr int64_t kItemOverheadKeys = 160;
+constexpr double kSplitMinGain = 0.05;
 
 struct bsp_plan_s {
   bsp_layer_desc_t desc;
@@ -80,11 +87,10 @@ struct bsp_plan_s {
   bool check_mode = false;
   int page_shift = 0;
   size_t ws_bytes = 0;
-  // balanced pairs of the fused step (reserved when the geometry allows them)
-  bool pair_capable = false;
-  int pair_mode = 2;  // 0 never, 1 always, 2 when the prompt lengths are spread wide
-  int32_t max_pairs = 0, pair_part_floats = 0;
-  size_t pairs_off = 0, pair_count_off = 0, pair_part_off = 0;
+  // the fused step's work items and split partial states (beam decode plans)
+  int32_t max_fitems = 0, max_qt = 0, max_slots = 0, part_floats = 0;
+  int32_t split_force = -1;  // BSP_SPLIT: -1 automatic, 0 never, > 0 chunk of that many keys
+  size_t fitems_off = 0, split_count_off = 0, split_part_off = 0;
   // prefill work list (bsp_plan_prefill): (request, query tile) int32 pairs
   int32_t max_items = 0;
   size_t items_off = 0;
@@ -97,14 +103,14 @@ struct bsp_plan_s {
 
   // current plan
   bool planned = false;
-  int32_t B = 0, W = 0, q_len = 0, tail_pad = 0, n_split = 1, rows_per_req = 0, n_pairs = 0;
+  int32_t B = 0, W = 0, q_len = 0, tail_pad = 0, n_split = 1, rows_per_req = 0;
+  int32_t n_fitems = 0, n_slots = 0;  // fused-step items and split partial slots in use
   int32_t split_keys = 0;  // keys per split of the current step (0: one pass)
   int32_t prefix_rpt = 0;  // query rows per work item of bsp_prefix_attn
-  bool order_on = false;   // the fused step takes requests longest prompt first
   void* ws_d = nullptr;
   void* zeroed_ws = nullptr;  // workspace whose header this plan has cleared
   std::vector<ReqInfo> h_req;
-  std::vector<bsp::PairInfo> h_pairs;
+  std::vector<bsp::FusedItem> h_fitems;
   std::vector<int32_t> h_pages;
   // prefill plans (bsp_plan_prefill): ragged query rows, work list
   bool prefill = false;
@@ -114,16 +120,14 @@ struct bsp_plan_s {
 namespace {
 
 size_t req_offset() { return bsp::kHeaderBytes; }
-// header | ReqInfo[B] | ReqInfo[B] longest prompt first (beam plans) | page table
-size_t order_offset(int32_t B) { return bsp::kHeaderBytes + sizeof(ReqInfo) * B; }
-size_t pages_offset(int32_t B) { return align_up(bsp::kHeaderBytes + 2 * sizeof(ReqInfo) * B, 16); }
+// header | ReqInfo[B] | page table | (fixed offsets, sized for the plan's
+// capacity) fused-step items | split counters | split partial states |
+// prefill work list
+size_t pages_offset(int32_t B) { return align_up(bsp::kHeaderBytes + sizeof(ReqInfo) * B, 16); }
 
 DevHeader* dev_header(const bsp_plan_s* pl) { return static_cast<DevHeader*>(pl->ws_d); }
 const ReqInfo* dev_req(const bsp_plan_s* pl) {
   return reinterpret_cast<const ReqInfo*>(static_cast<char*>(pl->ws_d) + req_offset());
-}
-const ReqInfo* dev_req_order(const bsp_plan_s* pl) {
-  return reinterpret_cast<const ReqInfo*>(static_cast<char*>(pl->ws_d) + order_offset(pl->B));
 }
 const int32_t* dev_pages(const bsp_plan_s* pl) {
   return reinterpret_cast<const int32_t*>(static_cast<char*>(pl->ws_d) + pages_offset(pl->B));
@@ -161,6 +165,24 @@ bsp_status_t after_launch(bsp_plan_s* pl, hipError_t launch, const char* what,
 }
 
 }  // namespace
+
+namespace bsp {
+
+bsp_status_t set_error(bsp_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+void forget_workspace(bsp_plan_t plan) {
+  if (plan != nullptr) plan->zeroed_ws = nullptr;
+}
+
+}  // namespace bsp
 
 extern "C" {
 
@@ -222,31 +244,36 @@ bsp_status_t bsp_plan_create(const bsp_layer_desc_t* desc, int32_t max_requests,
   pl->ws_bytes = align_up(pages_offset(max_requests) +
                               sizeof(int32_t) * (size_t)max_requests * max_blocks_per_seq,
                           256);
-  // Balanced pairs need, after the tables, a pair list, a flag per pair and
-  // KV head, and a partial-state slot per pair and KV head. They apply to
-  // beam decode with bf16/f16, head_dim <= 128 and at most 64 * kPairMaxMB
-  // query rows per request and KV head.
+  // The fused step's items (one per request, or one per chunk of a split
+  // prompt), then, when the geometry allows a split, an arrival counter per
+  // (request, KV head, query tile) and the partial states of split chunks,
+  // at most kSplitPartBudget bytes of them and 16 chunks per request on
+  // average.
   {
-    // BSP_PAIRS=0: never; BSP_PAIRS=1: whenever the geometry allows; otherwise
-    // the planner decides per step.
-    const char* env = std::getenv("BSP_PAIRS");
-    pl->pair_mode = env == nullptr ? 2 : env[0] == '0' ? 0 : env[0] == '1' ? 1 : 2;
     const int G = d.num_q_heads / d.num_kv_heads;
-    pl->pair_capable = d.key_bucket == 0 && d.dtype != BSP_F32 &&
-                       d.head_dim <= 128 && (int64_t)max_beam * G <= 64 * bsp::kPairMaxMB &&
-                       pl->pair_mode != 0;
-    if (pl->pair_capable) {
-      pl->max_pairs = (max_requests + 1) / 2;
-      pl->pair_part_floats = bsp::pair_part_floats(d.head_dim, bsp::kPairMaxMB);
-      pl->pairs_off = pl->ws_bytes;
-      pl->pair_count_off = align_up(pl->pairs_off + sizeof(bsp::PairInfo) * pl->max_pairs, 256);
-      pl->pair_part_off = align_up(
-          pl->pair_count_off + sizeof(int32_t) * (size_t)pl->max_pairs * d.num_kv_heads, 256);
-      pl->ws_bytes = align_up(pl->pair_part_off + sizeof(float) * (size_t)pl->max_pairs *
-                                                      d.num_kv_heads * 256 *
-                                                      pl->pair_part_floats,
-                              256);
-    }
+    const int64_t rows = (int64_t)max_beam * G;
+    // query blocks per wave and query tiles grow with the rows per request
+    const int mb = bsp::pick_mb(d.head_dim, (int)std::min<int64_t>(rows, INT32_MAX / 2));
+    pl->max_qt = (int32_t)ceil_div(rows, 64 * mb);
+    pl->part_floats = bsp::split_part_floats(d.head_dim, mb);
+    const size_t slot_bytes =
+        sizeof(float) * 256 * (size_t)pl->part_floats * d.num_kv_heads * pl->max_qt;
+    const bool capable = d.key_bucket == 0 && d.dtype != BSP_F32;
+    pl->max_slots = capable ? (int32_t)std::min<size_t>((size_t)16 * max_requests,
+                                                       bsp::kSplitPartBudget / slot_bytes)
+                            : 0;
+    if (pl->max_slots < 2) pl->max_slots = 0;
+    const char* env = std::getenv("BSP_SPLIT");
+    pl->split_force = env == nullptr || env[0] == '\0' ? -1 : std::atoi(env);
+    if (pl->split_force > 0) pl->split_force = (int32_t)(ceil_div(pl->split_force, 64) * 64);
+    pl->max_fitems = max_requests + pl->max_slots;
+    pl->fitems_off = pl->ws_bytes;
+    pl->split_count_off =
+        align_up(pl->fitems_off + sizeof(bsp::FusedItem) * (size_t)pl->max_fitems, 256);
+    pl->split_part_off = align_up(pl->split_count_off + sizeof(int32_t) * (size_t)max_requests *
+                                                            d.num_kv_heads * pl->max_qt,
+                                  256);
+    pl->ws_bytes = align_up(pl->split_part_off + slot_bytes * (size_t)pl->max_slots, 256);
   }
   // Prefill work list: at most one item per 64 query rows of each request.
   {
@@ -439,33 +466,6 @@ bsp_status_t bsp_plan(bsp_plan_t pl, int32_t B, int32_t W, int32_t q_len,
   char* st = static_cast<char*>(pl->staging[slot]);
   std::memset(st, 0, bsp::kHeaderBytes);
   std::memcpy(st + req_offset(), req.data(), sizeof(ReqInfo) * B);
-  // The fused step's work order: longest prompt first, when the step is one
-  // round of workgroups over long prompts. Blocks are dispatched in order, so
-  // the longest requests then start first and the shorter ones fill in behind:
-  // 3% faster on 64 requests of 1.6-2.4k-token prompts (head_dim 64 and 128),
-  // 2% slower on 400-600-token prompts, where the lookup of the request before
-  // its own loads costs more than the order gains.
-  int32_t p_longest = 0;
-  for (int b = 0; b < B; ++b) p_longest = std::max(p_longest, req[b].prefix);
-  const int rows_g = W * q_len * (d.num_q_heads / d.num_kv_heads);
-  const int64_t fused_blocks =
-      (int64_t)B * d.num_kv_heads *
-      ceil_div(rows_g, bsp::prefix_rows_per_tile(d.dtype, d.head_dim, rows_g));
-  const bool order_on = q_len == 1 && !cached && d.dtype != BSP_F32 && p_longest >= 1024 &&
-                        fused_blocks <= bsp::kFillBlocks && d.head_dim <= 128 &&
-                        bsp::prefix_rows_per_tile(d.dtype, d.head_dim, rows_g) == 128;
-  if (order_on) {
-    // each entry carries its request index in q_off (unused by beam plans)
-    std::vector<int32_t> order(B);
-    for (int b = 0; b < B; ++b) order[b] = b;
-    std::stable_sort(order.begin(), order.end(),
-                     [&](int32_t x, int32_t y) { return req[x].prefix > req[y].prefix; });
-    ReqInfo* ro = reinterpret_cast<ReqInfo*>(st + order_offset(B));
-    for (int k = 0; k < B; ++k) {
-      ro[k] = req[order[k]];
-      ro[k].q_off = order[k];
-    }
-  }
   int32_t* pg_out = reinterpret_cast<int32_t*>(st + pages_offset(B));
   std::vector<int32_t> pages((size_t)total_pages);
   for (int b = 0; b < B; ++b)
@@ -473,56 +473,124 @@ bsp_status_t bsp_plan(bsp_plan_t pl, int32_t B, int32_t W, int32_t q_len,
       pages[(size_t)req[b].page_off + i] = bt(b, 0, (int)i);
   if (!pages.empty()) std::memcpy(pg_out, pages.data(), sizeof(int32_t) * pages.size());
 
-  // Balanced pairs (beam decode): longest prompt with shortest, and so on. The
-  // long request's keys are split in half of the pair's total, so that X (its
-  // first keys, then completing it) and Y (its remaining keys, then the short
-  // request in full) stream about as many keys and complete one request each.
-  int32_t n_pairs = 0;
-  std::vector<bsp::PairInfo> pairs;
-  // Pairing pays only for a wide spread of prompt lengths: with the spread of
-  // a typical batch, the end phases of the shorter requests already overlap
-  // the longer ones' streaming, and the paired kernel costs about as much as
-  // the balance recovers. Automatic pairing needs the longest prompt to be at
-  // least three times the shortest.
-  bool want_pairs = pl->pair_capable && !cached && q_len == 1 && B >= 2;
-  if (want_pairs && pl->pair_mode == 2) {
-    int32_t p_min = req[0].prefix, p_max = req[0].prefix;
-    for (int b = 1; b < B; ++b) {
-      p_min = std::min(p_min, req[b].prefix);
-      p_max = std::max(p_max, req[b].prefix);
-    }
-    want_pairs = p_max >= kPairSpread * (int64_t)p_min && p_max > 0;
-  }
-  if (want_pairs) {
-    std::vector<int32_t> order(B);
-    for (int b = 0; b < B; ++b) order[b] = b;
-    std::stable_sort(order.begin(), order.end(),
-                     [&](int32_t x, int32_t y) { return req[x].prefix > req[y].prefix; });
-    n_pairs = (B + 1) / 2;
-    pairs.resize(n_pairs);
-    constexpr int32_t kAlign = 64;
-    for (int i = 0; i < n_pairs; ++i) {
-      bsp::PairInfo& q = pairs[i];
-      q.a = order[i];
-      q.b = (B - 1 - i) > i ? order[B - 1 - i] : -1;
-      const int32_t Pa = req[q.a].prefix;
-      const int32_t Pb = q.b >= 0 ? req[q.b].prefix : 0;
-      int32_t split = Pa;
-      if (q.b >= 0) {
-        const int64_t half = ((int64_t)Pa + Pb) / 2;
-        const int64_t s2 = (half + kAlign / 2) / kAlign * kAlign;  // nearest multiple
-        if (s2 >= kAlign && s2 < Pa) split = (int32_t)s2;
+  // The fused step's work items (beam decode, bf16/f16): one per request, or
+  // one per chunk of a request whose prompt the plan splits. Blocks are
+  // dispatched in order and a slot that frees up takes the next block, so the
+  // items are listed longest first (the longest-processing-time rule). A split
+  // is taken when it shortens the modelled step (items dealt longest first to
+  // the slots of one round of workgroups, each item costing its keys, a fixed
+  // per-workgroup amount and the partial-state traffic of a split) by
+  // kSplitMinGain, or always with BSP_SPLIT=<keys>, never with BSP_SPLIT=0.
+  std::vector<bsp::FusedItem> fitems;
+  int32_t n_slots = 0, fused_qt = 1;
+  const bool fused_ok = q_len == 1 && !cached && d.dtype != BSP_F32;
+  if (fused_ok) {
+    const int rows_g = W * (d.num_q_heads / d.num_kv_heads);
+    fused_qt = (int32_t)ceil_div(rows_g, bsp::prefix_rows_per_tile(d.dtype, d.head_dim, rows_g));
+    const int64_t slots =
+        std::max<int64_t>(1, bsp::kFillBlocks / ((int64_t)d.num_kv_heads * fused_qt));
+    const int mb = bsp::pick_mb(d.head_dim, rows_g);
+    const int64_t key_bytes = 2 * (int64_t)d.head_dim * elem_bytes(d.dtype);
+    const int64_t part_keys =
+        (int64_t)bsp::split_part_floats(d.head_dim, mb) * 256 * 4 / key_bytes;
+    std::vector<int32_t> by_len(B);
+    for (int b = 0; b < B; ++b) by_len[b] = b;
+    std::stable_sort(by_len.begin(), by_len.end(),
+                     [&](int32_t x, int32_t y) { return req[x].valid > req[y].valid; });
+    // chunks of each request under a candidate chunk size (0: whole): the
+    // requests are taken longest first, and each one is split if its chunks
+    // still fit the plan's partial-state slots that are left
+    auto chunking = [&](int64_t ck, std::vector<int32_t>& parts_of) {
+      parts_of.assign(B, 1);
+      int64_t used = 0;
+      for (int32_t b : by_len) {
+        const int64_t n = ck > 0 && req[b].valid > ck ? ceil_div(req[b].valid, ck) : 1;
+        if (n > 1 && used + n <= pl->max_slots &&
+            (int64_t)B + used + n <= pl->max_fitems) {
+          parts_of[b] = (int32_t)n;
+          used += n;
+        }
       }
-      q.split = split;
-      q.pad = 0;
+    };
+    auto model = [&](int64_t ck, const std::vector<int32_t>& parts_of) {
+      std::vector<int64_t> cost;
+      for (int b = 0; b < B; ++b) {
+        const int64_t P = req[b].valid;
+        if (parts_of[b] == 1) {
+          cost.push_back(P + kItemOverheadKeys);
+          continue;
+        }
+        for (int j = 0; j < parts_of[b]; ++j) {
+          const int64_t len = std::min<int64_t>(P, (j + 1) * ck) - j * ck;
+          cost.push_back(len + kItemOverheadKeys + part_keys +
+                         (j == 0 ? (parts_of[b] - 1) * part_keys : 0));
+        }
+      }
+      std::sort(cost.begin(), cost.end(), std::greater<int64_t>());
+      std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> load;
+      for (int64_t i = 0; i < std::min<int64_t>(slots, (int64_t)cost.size()); ++i) load.push(0);
+      int64_t span = 0;
+      for (int64_t c : cost) {
+        const int64_t t = load.top() + c;
+        load.pop();
+        load.push(t);
+        span = std::max(span, t);
+      }
+      return span;
+    };
+    int64_t ck = 0;
+    std::vector<int32_t> parts_of(B, 1);
+    if (pl->split_force > 0) {
+      ck = pl->split_force;
+      chunking(ck, parts_of);
+    } else if (pl->split_force < 0 && pl->max_slots > 0 && B > 0) {
+      const int64_t p_max = req[by_len[0]].valid;
+      const int64_t base = model(0, parts_of);
+      int64_t best = base;
+      std::vector<int32_t> cand;
+      for (int n = 2; n <= 4; ++n) {
+        const int64_t c = ceil_div(ceil_div(p_max, n), 64) * 64;
+        if (c <= 0 || c >= p_max) continue;
+        chunking(c, cand);
+        const int64_t span = model(c, cand);
+        if (span < best && span <= (int64_t)((1.0 - kSplitMinGain) * base)) {
+          best = span;
+          ck = c;
+          parts_of = cand;
+        }
+      }
     }
-    std::memcpy(st + pl->pairs_off, pairs.data(), sizeof(bsp::PairInfo) * n_pairs);
-    std::memset(st + pl->pair_count_off, 0, sizeof(int32_t) * (size_t)n_pairs * d.num_kv_heads);
+    for (int b = 0; b < B; ++b) {
+      const int32_t n = parts_of[b];
+      for (int32_t j = 0; j < n; ++j) {
+        bsp::FusedItem it;
+        std::memset(&it, 0, sizeof(it));
+        it.ri = req[b];
+        it.b = b;
+        it.k_lo = n > 1 ? (int32_t)(j * ck) : 0;
+        it.k_hi = n > 1 ? (int32_t)std::min<int64_t>(req[b].valid, (j + 1) * ck) : req[b].valid;
+        it.part = j;
+        it.parts = n;
+        it.slot = n > 1 ? n_slots : -1;
+        fitems.push_back(it);
+      }
+      if (n > 1) n_slots += n;
+    }
+    std::stable_sort(fitems.begin(), fitems.end(),
+                     [](const bsp::FusedItem& x, const bsp::FusedItem& y) {
+                       return x.k_hi - x.k_lo > y.k_hi - y.k_lo;
+                     });
+    std::memcpy(st + pl->fitems_off, fitems.data(), sizeof(bsp::FusedItem) * fitems.size());
+    if (n_slots > 0)
+      std::memset(st + pl->split_count_off, 0,
+                  sizeof(int32_t) * (size_t)B * d.num_kv_heads * fused_qt);
   }
 
   if (!pl->host_only) {
     size_t end = pages_offset(B) + sizeof(int32_t) * pages.size();
-    if (n_pairs > 0) end = pl->pair_count_off + sizeof(int32_t) * (size_t)n_pairs * d.num_kv_heads;
+    if (!fitems.empty()) end = pl->fitems_off + sizeof(bsp::FusedItem) * fitems.size();
+    if (n_slots > 0)
+      end = pl->split_count_off + sizeof(int32_t) * (size_t)B * d.num_kv_heads * fused_qt;
     const size_t begin = workspace_d == pl->zeroed_ws ? req_offset() : 0;
     hipError_t e = hipMemcpyAsync(static_cast<char*>(workspace_d) + begin, st + begin,
                                   end - begin, hipMemcpyHostToDevice, stream);
@@ -541,10 +609,10 @@ bsp_status_t bsp_plan(bsp_plan_t pl, int32_t B, int32_t W, int32_t q_len,
   pl->n_split = n_split;
   pl->split_keys = split_keys;
   pl->prefix_rpt = prefix_rpt;
-  pl->order_on = order_on;
   pl->rows_per_req = W * q_len * (d.num_q_heads / d.num_kv_heads);
-  pl->n_pairs = n_pairs;
-  pl->h_pairs = std::move(pairs);
+  pl->n_fitems = (int32_t)fitems.size();
+  pl->n_slots = n_slots;
+  pl->h_fitems = std::move(fitems);
   pl->prefill = false;
   pl->rows_total = B * W * q_len;
   pl->n_items = 0;
@@ -673,9 +741,9 @@ bsp_status_t bsp_plan_prefill(bsp_plan_t pl, int32_t C, const int32_t* q_len_h,
   pl->tail_pad = 0;
   pl->n_split = 1;
   pl->rows_per_req = 0;
-  pl->n_pairs = 0;
-  pl->h_pairs.clear();
-  pl->order_on = false;
+  pl->n_fitems = 0;
+  pl->n_slots = 0;
+  pl->h_fitems.clear();
   pl->prefill = true;
   pl->rows_total = (int32_t)rows;
   pl->n_items = (int32_t)items.size();
@@ -830,7 +898,7 @@ bsp_status_t decode_params(bsp_plan_s* pl, const void* q, const void* k_new, con
   p.k_pool = k_pool;
   p.v_pool = v_pool;
   p.req = dev_req(pl);
-  p.req_order = pl->order_on ? dev_req_order(pl) : nullptr;
+  p.fitems = reinterpret_cast<const bsp::FusedItem*>(static_cast<char*>(pl->ws_d) + pl->fitems_off);
   p.pages = dev_pages(pl);
   p.hdr = dev_header(pl);
   p.B = pl->B;
@@ -845,7 +913,9 @@ bsp_status_t decode_params(bsp_plan_s* pl, const void* q, const void* k_new, con
   p.split_keys = 0;
   const int rows_per_tile = bsp::prefix_rows_per_tile(d.dtype, d.head_dim, pl->rows_per_req);
   p.n_qtiles = (int32_t)ceil_div(pl->rows_per_req, rows_per_tile);
-  p.xcd_remap = p.n_qtiles > 1 && (int64_t)p.B * p.hkv % 8 == 0 ? 1 : 0;
+  // the grid is (item, KV head, query tile): the remap is a bijection when
+  // items x KV heads is a multiple of 8
+  p.xcd_remap = p.n_qtiles > 1 && (int64_t)pl->n_fitems * p.hkv % 8 == 0 ? 1 : 0;
   p.causal = 0;
   p.rows_total = pl->B * pl->W;
   p.scale = d.sm_scale;
@@ -862,17 +932,13 @@ bsp_status_t decode_params(bsp_plan_s* pl, const void* q, const void* k_new, con
   f.max_seq_len = pl->max_seq_len;
   f.o_out = o_out;
   f.lse_out = lse_out;
-  f.pairs = nullptr;
-  f.pair_count = nullptr;
-  f.pair_part = nullptr;
-  f.n_pairs = 0;
-  f.part_floats = pl->pair_part_floats;
-  if (pl->n_pairs > 0 && pl->rows_per_req <= 64 * bsp::kPairMaxMB) {
+  f.split_count = nullptr;
+  f.split_part = nullptr;
+  f.part_floats = pl->part_floats;
+  if (pl->n_slots > 0) {
     char* ws = static_cast<char*>(pl->ws_d);
-    f.pairs = reinterpret_cast<const bsp::PairInfo*>(ws + pl->pairs_off);
-    f.pair_count = reinterpret_cast<int32_t*>(ws + pl->pair_count_off);
-    f.pair_part = reinterpret_cast<float*>(ws + pl->pair_part_off);
-    f.n_pairs = pl->n_pairs;
+    f.split_count = reinterpret_cast<int32_t*>(ws + pl->split_count_off);
+    f.split_part = reinterpret_cast<float*>(ws + pl->split_part_off);
   }
   return BSP_OK;
 }
@@ -933,9 +999,10 @@ bsp_status_t bsp_decode_step(bsp_plan_t pl, const void* q, const void* k_new, co
                                         block_tables_d, cache_indirection_d, o_out, lse_out, p, f);
   if (st != BSP_OK) return st;
   const bsp_layer_desc_t& d = pl->desc;
-  return after_launch(
-      pl, bsp::launch_decode_step(p, f, d.dtype, d.head_dim, pl->rows_per_req, pl->tail_pad, stream),
-      "decode step launch", stream);
+  return after_launch(pl,
+                      bsp::launch_decode_step(p, f, d.dtype, d.head_dim, pl->rows_per_req,
+                                              pl->n_fitems, pl->tail_pad, stream),
+                      "decode step launch", stream);
 }
 
 bsp_status_t bsp_prefill_attn(bsp_plan_t pl, const void* q, const void* k_pool, const void* v_pool,
@@ -981,9 +1048,10 @@ bsp_status_t bsp_mixed_step(bsp_plan_t gen, bsp_plan_t ctx, const void* q, const
                                              ctx->n_items, stream),
                     "prefill launch", stream);
   if (st != BSP_OK) return st;
-  return after_launch(
-      gen, bsp::launch_decode_step(dp, df, d.dtype, d.head_dim, gen->rows_per_req, gen->tail_pad, stream),
-      "decode step launch", stream);
+  return after_launch(gen,
+                      bsp::launch_decode_step(dp, df, d.dtype, d.head_dim, gen->rows_per_req,
+                                              gen->n_fitems, gen->tail_pad, stream),
+                      "decode step launch", stream);
 }
 
 static bsp::TailParams tail_params(const bsp_plan_s* pl, const void* q, const void* k_pool,
@@ -1092,9 +1160,8 @@ bsp_status_t bsp_check(bsp_plan_t pl, hipStream_t stream) {
   e = hipMemcpy(pl->ws_d, &zero, sizeof(zero), hipMemcpyHostToDevice);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpy (clear error word)");
   return fail(BSP_ERR_DEVICE_INDEX,
-              "kernels skipped %d out-of-range index reads/writes or waits (bits 0x%x: 1 prompt "
-              "page, 2 cache_indirection parent, 4 tail page, 8 write slot, 16 pair wait); "
-              "first value %d",
+              "kernels skipped %d out-of-range index reads/writes (bits 0x%x: 1 prompt page, "
+              "2 cache_indirection parent, 4 tail page, 8 write slot); first value %d",
               h.fault_count, h.error_bits, h.first_value);
 }
 
@@ -1115,15 +1182,17 @@ bsp_status_t bsp_debug_plan_tables(bsp_plan_t pl, int32_t* indptr_h, int32_t* pa
   return ok();
 }
 
-bsp_status_t bsp_debug_plan_pairs(bsp_plan_t pl, int32_t* n_pairs_h, int32_t* pairs_h) {
-  if (pl == nullptr || n_pairs_h == nullptr) return fail(BSP_ERR_ARG, "null pointer");
+bsp_status_t bsp_debug_plan_items(bsp_plan_t pl, int32_t* n_items_h, int32_t* items_h) {
+  if (pl == nullptr || n_items_h == nullptr) return fail(BSP_ERR_ARG, "null pointer");
   if (!pl->planned) return fail(BSP_ERR_STALE_PLAN, "plan has no valid step");
-  *n_pairs_h = pl->n_pairs;
-  if (pairs_h != nullptr)
-    for (int i = 0; i < pl->n_pairs; ++i) {
-      pairs_h[3 * i] = pl->h_pairs[i].a;
-      pairs_h[3 * i + 1] = pl->h_pairs[i].b;
-      pairs_h[3 * i + 2] = pl->h_pairs[i].split;
+  *n_items_h = pl->n_fitems;
+  if (items_h != nullptr)
+    for (int i = 0; i < pl->n_fitems; ++i) {
+      const bsp::FusedItem& it = pl->h_fitems[i];
+      items_h[4 * i] = it.b;
+      items_h[4 * i + 1] = it.k_lo;
+      items_h[4 * i + 2] = it.k_hi;
+      items_h[4 * i + 3] = it.parts;
     }
   return ok();
 }

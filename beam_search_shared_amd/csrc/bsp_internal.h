@@ -24,7 +24,6 @@ enum ErrorBits : int32_t {
   kErrTailParent = 2,   // a cache_indirection entry outside [0, W)
   kErrTailPage = 4,     // a tail block-table entry outside [0, num_pages)
   kErrWriteSlot = 8,    // a KV-write slot outside [0, num_pages * page_size)
-  kErrPairWait = 16,    // a balanced pair's partial state did not arrive within the wait
 };
 
 struct DevHeader {
@@ -35,27 +34,14 @@ struct DevHeader {
 };
 static_assert(sizeof(DevHeader) == kHeaderBytes, "header size");
 
-// Balanced pairs of the fused step: the request with the longest prompt is
-// paired with the shortest, the second longest with the second shortest, and
-// so on. For each KV head, workgroup Y first attends the long request `a` over
-// keys [split, P_a) and leaves that partial state (O, running max and sum) in
-// the pair's slot, raising the pair's flag; then it attends the short request
-// `b` in full. Workgroup X attends `a` over [0, split), waits for the flag,
-// merges Y's partial state into its own and completes `a` (tail, output,
-// token write). b < 0: `a` alone (odd count). split == P_a: no split.
-struct PairInfo {
-  int32_t a, b, split, pad;
-};
-static_assert(sizeof(PairInfo) == 16, "PairInfo size");
-
-// Bounded wait for a pair's flag, in sleeps of ~128 clocks (~0.1 s in all).
-constexpr int kPairSpin = 1 << 20;
-// Per-thread floats of one partial state in a pair slot: O accumulators
-// (D/16 blocks x MB query blocks x 4) then the running max and sum per query
-// block; stored element-major over the 256 threads of a workgroup.
-constexpr int pair_part_floats(int head_dim, int mb) { return (head_dim / 16) * mb * 4 + 2 * mb; }
-// Pairing applies to query tiles of at most this many 16-row blocks per wave.
-constexpr int kPairMaxMB = 2;
+// Per-thread floats of one partial state of the fused step (a request's prompt
+// split over several workgroups): O accumulators (D/16 blocks x MB query
+// blocks x 4), then the running max and sum per query block; stored
+// element-major over the 256 threads of a workgroup, so that the workgroup
+// that merges reads back exactly the elements each of its threads holds.
+constexpr int split_part_floats(int head_dim, int mb) { return (head_dim / 16) * mb * 4 + 2 * mb; }
+// Device bytes the plan reserves for split partial states at most.
+constexpr size_t kSplitPartBudget = size_t(24) << 20;
 
 struct ReqInfo {
   int32_t page_off;  // first entry of this request in the page table
@@ -71,6 +57,20 @@ struct ReqInfo {
 // chunk, tail = the chunk's rows (the query rows), seq = n_keys = valid = L_b +
 // chunk rows: the page table covers the cached rows and the chunk's own rows.
 static_assert(sizeof(ReqInfo) == 32, "ReqInfo size");
+
+// One work item of the fused step: keys [k_lo, k_hi) of request b's prompt
+// (all of it unless the plan split the prompt). Items are listed longest
+// first, so the workgroups that stream the most keys are dispatched first.
+// A split request's `parts` items each leave a partial state in slots
+// [slot, slot + parts) and count themselves on the request's counter; the
+// last to arrive merges the others and finishes the request (tails, output,
+// current-token write). Unsplit: parts = 1, slot = -1.
+struct FusedItem {
+  ReqInfo ri;        // request b's info, copied so that one load gives a workgroup its work
+  int32_t b, k_lo, k_hi, part;
+  int32_t parts, slot, pad0, pad1;
+};
+static_assert(sizeof(FusedItem) == 64, "FusedItem size");
 
 // ---------------------------------------------------------------------------
 // Kernel parameter blocks (passed by value).
@@ -95,10 +95,8 @@ struct PrefixParams {
   float* o_part;
   float* lse_part;
   const ReqInfo* req;
-  // fused step: the same requests, longest prompt first, each with q_off = its
-  // request index (blocks are dispatched in order, so the longest start first);
-  // null: plan order
-  const ReqInfo* req_order;
+  // fused step: its work items, longest first (blocks are dispatched in order)
+  const FusedItem* fitems;
   const int32_t* pages;
   DevHeader* hdr;
   int32_t B, W, q_len, hq, hkv, group;
@@ -128,11 +126,12 @@ struct FusedParams {
   int32_t max_blocks, max_seq_len;
   void* o_out;                  // dtype [B*W][Hq][D]
   float* lse_out;               // [B*W][Hq] or null
-  // balanced pairs (null: one workgroup per request and KV head)
-  const PairInfo* pairs;
-  int32_t* pair_count;          // flags [n_pairs][Hkv], zero between launches
-  float* pair_part;             // [n_pairs][Hkv][part_floats][256]
-  int32_t n_pairs, part_floats;
+  // split requests (null when the plan split none): arrival counters
+  // [B][Hkv][n_qtiles], zero between launches (the last arrival resets its
+  // counter), and partial states [slot][Hkv][n_qtiles][part_floats][256]
+  int32_t* split_count;
+  float* split_part;
+  int32_t part_floats;
 };
 
 struct TailParams {
@@ -161,6 +160,11 @@ struct MergeParams {
   float* lse_out;
 };
 
+// The calling thread's error message (bsp_last_error) and status.
+bsp_status_t set_error(bsp_status_t st, const char* fmt, ...);
+// Make the plan's next bsp_plan copy the whole workspace header again.
+void forget_workspace(bsp_plan_t plan);
+
 // ---------------------------------------------------------------------------
 // Launchers (defined next to their kernels). They return hipSuccess or the
 // launch error; shape checks are done by the host entry points beforehand.
@@ -175,7 +179,8 @@ hipError_t launch_prefix(const PrefixParams& p, int dtype, int head_dim, int row
 hipError_t launch_prefix_two(const PrefixParams& a, const PrefixParams& b, int dtype, int head_dim,
                              hipStream_t s);
 hipError_t launch_decode_step(const PrefixParams& p, const FusedParams& f, int dtype,
-                              int head_dim, int rows_per_req, int tail_pad, hipStream_t s);
+                              int head_dim, int rows_per_req, int n_items, int tail_pad,
+                              hipStream_t s);
 // Query-row blocks of 16 per wave for an M-row item (4 waves per workgroup).
 // At head_dim 256 a 128-row tile needs more than half a SIMD's registers (one
 // workgroup per CU); 64-row tiles at two per CU, the tiles of a request on one
@@ -201,7 +206,7 @@ hipError_t launch_prefill(const PrefixParams& p, const FusedParams& f, int dtype
                           int mb, int n_items, hipStream_t s);
 // A mixed step in one launch (beam-step workgroups beside context workgroups):
 // one query block per wave on both sides, head_dim <= 128, the beam step's
-// tails in the LDS slot table and no balanced pairs.
+// tails in the LDS slot table and no split request.
 bool mixed_step_supported(const PrefixParams& dp, const FusedParams& df, int dtype, int head_dim,
                           int rows_per_req, int tail_pad, int pre_mb);
 hipError_t launch_mixed_step(const PrefixParams& dp, const FusedParams& df, const PrefixParams& pp,

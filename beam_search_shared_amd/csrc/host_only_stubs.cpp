@@ -14,7 +14,7 @@ hipError_t launch_prefix(const PrefixParams&, int, int, int, hipStream_t) {
 hipError_t launch_prefix_two(const PrefixParams&, const PrefixParams&, int, int, hipStream_t) {
   return hipErrorNotSupported;
 }
-hipError_t launch_decode_step(const PrefixParams&, const FusedParams&, int, int, int, int,
+hipError_t launch_decode_step(const PrefixParams&, const FusedParams&, int, int, int, int, int,
                               hipStream_t) {
   return hipErrorNotSupported;
 }
@@ -37,3 +37,4 @@ hipError_t launch_naive(const TailParams&, void*, float*, int, int, hipStream_t)
 }
 
 }  // namespace bsp
+

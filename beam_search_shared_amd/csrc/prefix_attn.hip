@@ -179,9 +179,15 @@ __device__ __forceinline__ int32_t resolve_fused_slot(const PrefixParams& p, con
 // MODE 4: a mixed step in one launch: each workgroup is either a MODE 1 item
 // of the beam step or a MODE 3 item of the context requests (`pre`), with
 // that part's parameters.
-// ORD: the fused step takes its requests from the plan's longest-first copy
-// (a variant of its own, so that the other kernels compile without the lookup).
-template <typename T, int D, int MB, int KT, int NST, int MODE, bool PAIR, bool ORD = false>
+// The beam step (MODES 1, 2 and the beam-step items of 4) takes its work
+// items from the plan's list (FusedItem), longest first. An item covers all of
+// a request's prompt, or one chunk of it when the plan split the prompt; then
+// the workgroup leaves its partial state in its slot and counts itself on the
+// request's counter, and only the last of the request's workgroups (per KV
+// head and query tile) to arrive merges the other chunks' states and
+// finishes the request (tails, output, current-token write). No workgroup
+// ever waits for another.
+template <typename T, int D, int MB, int KT, int NST, int MODE>
 __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int block, bool pre) {
   // FUSED / PREFILL: the workgroup may be a beam-step / context item; `fused`
   // and `is_pre` say which one it is.
@@ -190,8 +196,7 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
   constexpr bool TAILS1 = MODE == 1 || MODE == 4;  // tails through the LDS slot table
   const bool is_pre = MODE == 3 || (MODE == 4 && pre);
   const bool fused = FUSED && !is_pre;
-  static_assert(MODE != 4 || (MB == 1 && !PAIR), "mixed steps take one query block per wave");
-  static_assert(!PAIR || (MODE == 1 && MB <= kPairMaxMB), "pairs run in the fused step, MB <= 2");
+  static_assert(MODE != 4 || MB == 1, "mixed steps take one query block per wave");
   using V8 = typename Mfma<T>::V8;
   constexpr int NDS = D / 32;                       // contraction steps of S^T
   constexpr int NDB = D / 16;                       // 16-row blocks of O^T
@@ -207,55 +212,47 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
   __shared__ int lds_pages[kPageWin];
   __shared__ int lds_tail[TAILS1 ? kTailSlots : 1];
 
-  // ---- work: one (request, KV head, key split, query tile) item; with
-  // balanced pairs (PairInfo), one or two segments of a pair for one KV head.
-  int nseg = 1;
-  int sg_b0 = 0, sg_lo0 = 0, sg_hi0 = 0, sg_b1 = 0, sg_lo1 = 0, sg_hi1 = 0;
-  bool sg_share0 = false, sg_share1 = false;
-  int pair_idx = 0, pair_role = 0;
+  // ---- work: one (request or prompt chunk, KV head, key split, query tile) item
   WorkItem w;
-  // the fused step reads its request from the plan's longest-first copy
-  const bool fused_order = ORD && FUSED && !PAIR && !is_pre && p.req_order != nullptr;
-  ReqInfo ri_ord{};
+  ReqInfo ri;
+  int part = 0, parts = 1, slot = -1;  // split requests of the beam step
   {
     int bid = block;
-    if constexpr (PAIR) {
-      // Every Y workgroup comes before every X workgroup in the grid, so an X
-      // never waits for a Y that could not be dispatched yet.
-      const int npk = f.n_pairs * p.hkv;
-      pair_role = bid < npk ? 1 : 0;
-      if (bid >= npk) bid -= npk;
-      pair_idx = bid / p.hkv;
-      w.g = bid % p.hkv;
-      w.split = 0;
-      w.qt = 0;
-      const PairInfo pr = f.pairs[pair_idx];
-      const int Pa = p.req[pr.a].valid;
-      if (pair_role == 0) {  // X: the long request's first keys, then finishes it
-        sg_b0 = pr.a; sg_lo0 = 0; sg_hi0 = pr.split; sg_share0 = pr.split < Pa;
-        nseg = 1;
-      } else if (pr.b < 0) {
-        nseg = 0;  // a request without partner: X has all of it
-      } else if (pr.split < Pa) {  // Y: the long request's last keys, then the short one
-        sg_b0 = pr.a; sg_lo0 = pr.split; sg_hi0 = Pa; sg_share0 = true;
-        sg_b1 = pr.b; sg_lo1 = 0; sg_hi1 = p.req[pr.b].valid;
-        nseg = 2;
+    if (fused) {
+      // (item, KV head, query tile), items longest first
+      if (p.xcd_remap) {
+        // Workgroups are dealt to the 8 XCDs in turn, so block ids 8 apart
+        // share an XCD and its L2: the query tiles of one item go there.
+        const int lo = bid & 7;
+        const int rest = bid >> 3;
+        w.qt = rest % p.n_qtiles;
+        bid = (rest / p.n_qtiles) * 8 + lo;
       } else {
-        sg_b0 = pr.b; sg_lo0 = 0; sg_hi0 = p.req[pr.b].valid;
-        nseg = 1;
+        w.qt = bid % p.n_qtiles;
+        bid /= p.n_qtiles;
       }
+      w.g = bid % p.hkv;
+      const FusedItem it = p.fitems[bid / p.hkv];
+      ri = it.ri;
+      w.b = it.b;
+      w.k_lo = it.k_lo;
+      w.k_hi = it.k_hi;
+      w.split = 0;
+      part = it.part;
+      parts = it.parts;
+      slot = it.slot;
     } else if (PREFILL && is_pre) {
       w.g = bid % p.hkv;
       const int item = bid / p.hkv;
-      sg_b0 = p.items[2 * item];
+      w.b = p.items[2 * item];
       w.qt = p.items[2 * item + 1];
       w.split = 0;
       // keys up to the tile's last row (row r holds chunk position r / group)
-      const ReqInfo rb = p.req[sg_b0];
-      const int last = min((w.qt + 1) * 64 * MB, rb.tail * p.group) - 1;
-      sg_lo0 = 0;
-      sg_hi0 = min(rb.valid, rb.valid - rb.tail + last / p.group + 1);
-    } else if (!FUSED && p.causal && p.W == 1) {
+      ri = p.req[w.b];
+      const int last = min((w.qt + 1) * 64 * MB, ri.tail * p.group) - 1;
+      w.k_lo = 0;
+      w.k_hi = min(ri.valid, ri.valid - ri.tail + last / p.group + 1);
+    } else if (p.causal && p.W == 1) {
       // Causal rows of one sequence: row r is position r / group and sees keys
       // up to n_keys - q_len + r / group, so a tile streams only the keys up to
       // its last row's limit. Tiles go longest first (query tile slowest,
@@ -264,19 +261,16 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
       bid /= p.hkv;
       w.split = bid % p.n_split;
       bid /= p.n_split;
-      sg_b0 = bid % p.B;
+      w.b = bid % p.B;
       w.qt = p.n_qtiles - 1 - bid / p.B;
-      const ReqInfo rb = p.req[sg_b0];
+      ri = p.req[w.b];
       const int r_last = min((w.qt + 1) * 64 * MB, p.q_len * p.group) - 1;
-      const int lim = min(rb.valid, rb.n_keys - p.q_len + r_last / p.group + 1);
-      sg_lo0 = p.split_keys > 0 ? w.split * p.split_keys : 0;
-      sg_hi0 = p.split_keys > 0 ? min(lim, sg_lo0 + p.split_keys) : lim;
-      if (sg_hi0 < sg_lo0) sg_hi0 = sg_lo0;
+      const int lim = min(ri.valid, ri.n_keys - p.q_len + r_last / p.group + 1);
+      w.k_lo = p.split_keys > 0 ? w.split * p.split_keys : 0;
+      w.k_hi = p.split_keys > 0 ? min(lim, w.k_lo + p.split_keys) : lim;
+      if (w.k_hi < w.k_lo) w.k_hi = w.k_lo;
     } else {
       if (p.xcd_remap) {
-        // Workgroups are dealt to the 8 XCDs in turn, so block ids 8 apart
-        // share an XCD and its L2: the query tiles of one work item go there
-        // and read its keys from one L2 rather than from eight.
         const int lo = bid & 7;
         const int rest = bid >> 3;
         w.qt = rest % p.n_qtiles;
@@ -288,37 +282,20 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
       w.split = bid % p.n_split;
       bid /= p.n_split;
       w.g = bid % p.hkv;
-      sg_b0 = bid / p.hkv;
-      if (fused_order) {  // the fused step: longest prompts in the first blocks
-        ri_ord = p.req_order[sg_b0];
-        sg_b0 = ri_ord.q_off;
-      }
-      const int valid = fused_order ? ri_ord.valid : p.req[sg_b0].valid;
-      sg_lo0 = p.split_keys > 0 ? w.split * p.split_keys : 0;
-      sg_hi0 = p.split_keys > 0 ? min(valid, sg_lo0 + p.split_keys) : valid;
-      if (sg_hi0 < sg_lo0) sg_hi0 = sg_lo0;
+      w.b = bid / p.hkv;
+      ri = p.req[w.b];
+      w.k_lo = p.split_keys > 0 ? w.split * p.split_keys : 0;
+      w.k_hi = p.split_keys > 0 ? min(ri.valid, w.k_lo + p.split_keys) : ri.valid;
+      if (w.k_hi < w.k_lo) w.k_hi = w.k_lo;
     }
   }
+  const bool split = fused && parts > 1;
 
-  // Everything from here to the end of the kernel runs once per segment (one
-  // segment except in the second workgroup of a balanced pair); the body is
-  // not indented for the loop.
-#pragma nounroll
-  for (int si = 0; si < nseg; ++si) {
-  if (si > 0) __syncthreads();  // the previous segment is done with LDS
-  w.b = si == 0 ? sg_b0 : sg_b1;
-  w.k_lo = si == 0 ? sg_lo0 : sg_lo1;
-  w.k_hi = si == 0 ? sg_hi0 : sg_hi1;
-  const bool share = PAIR && (si == 0 ? sg_share0 : sg_share1);
-  // Lane indices are derived again in every segment: hoisted out of the
-  // segment loop, everything computed from them would stay live across it.
-  int tid = threadIdx.x;
-  if constexpr (PAIR) asm volatile("" : "+v"(tid));
+  const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform by construction
   const int l16 = lane & 15;
   const int l4 = lane >> 4;
-  const ReqInfo ri = fused_order ? ri_ord : p.req[w.b];
 
   const int M = is_pre ? ri.tail * p.group : p.W * p.q_len * p.group;
   // Rows per wave: 16 per query block; in the fused step with one block per
@@ -337,14 +314,13 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
   const int kb_first = (w.qt * rt) / p.group;   // beams with a row in this tile
   const int kb_last = min(p.W - 1, ((w.qt + 1) * rt - 1) / p.group);
   const int nbt = kb_last - kb_first + 1;
-  // Y's share of a pair ends with its partial state: no tail, output or token
-  const bool finishes = !(PAIR && share && pair_role == 1);
   // MODE 1 tail slots of this tile's beams (slot-table rows u = (beam -
   // kb_first) * n_tail + t), TR per thread at a time: all parent lookups, then
   // all page lookups, then the table entries (the host checked that the table
-  // holds them).
+  // holds them). A workgroup of a split request builds the table only once it
+  // knows that it finishes the request.
   constexpr int TR = 4;
-  const int n_sl = TAILS1 && fused && finishes ? nbt * ri.tail : 0;
+  const int n_sl = TAILS1 && fused ? nbt * ri.tail : 0;
   auto sl_parents = [&](int base, int32_t (&src)[TR]) {
 #pragma unroll
     for (int i = 0; i < TR; ++i) {
@@ -396,12 +372,15 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
   // overlap gains: measured at MB = 2, not free at MB = 3.)
   constexpr bool DEFER = MODE == 1 && MB == 1;
   int32_t t_src[TR], t_page[TR];
-  if constexpr (TAILS1 && !DEFER) {
-    for (int base = 0; base < n_sl; base += 256 * TR) {
+  auto sl_build = [&](int from) {
+    for (int base = from; base < n_sl; base += 256 * TR) {
       sl_parents(base, t_src);
       sl_pages(base, t_src, t_page);
       sl_commit(base, t_src, t_page);
     }
+  };
+  if constexpr (TAILS1 && !DEFER) {
+    if (!split) sl_build(0);
   }
 
   // ---- query rows of this lane (B operand of S^T), causal limits
@@ -436,7 +415,9 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
     }
   }
 
-  if constexpr (DEFER) sl_parents(0, t_src);
+  if constexpr (DEFER) {
+    if (!split) sl_parents(0, t_src);
+  }
 
   f32x4 oacc[NDB][MB];
   float mrow[MB], lrow[MB];
@@ -595,7 +576,7 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
     // lookups then stay in flight beside the tiles; they are used after the
     // prompt, when everything has landed.
     wait_vmcnt<0>();
-    sl_pages(0, t_src, t_page);
+    if (!split) sl_pages(0, t_src, t_page);
   }
 
   for (int wi = 0; wi < n_win; ++wi) {
@@ -679,87 +660,80 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
     if (ROT && wave_active && ntp > 0) o_tile(lds_kv[(ntp - 1) % NST][1], pb);
   }
 
-  // ---- balanced pairs: Y leaves its partial state of the long request in
-  // the pair's slot and raises the flag; X waits for the flag (Y streamed
-  // fewer keys and started no later), merges, and completes the request.
-  // The slot and the flag are accessed only with agent-coherent loads and
-  // stores, and the flag is raised once those stores have completed, so no
-  // cache-wide write-back or invalidation is needed on either side.
-  if constexpr (PAIR) {
-    if (share) {
-      const int64_t slot = (int64_t)pair_idx * p.hkv + w.g;
-      float* part = f.pair_part + slot * f.part_floats * 256;
-      int32_t* flag = f.pair_count + slot;
-      auto put = [](float* q, float v) {
-        __hip_atomic_store(q, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      };
-      auto get = [](const float* q) {
-        return __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      };
-      if (pair_role == 1) {
+  // ---- a split request: this workgroup leaves its chunk's partial state in
+  // its slot and counts its arrival on the request's counter (per KV head and
+  // query tile). The last to arrive merges the other chunks' states into its
+  // own (the exact log-sum-exp rule) and finishes the request; the others are
+  // done. No workgroup waits for another. The states and the counter are
+  // accessed only with agent-coherent loads, stores and one atomic add, and a
+  // state is counted only after its stores have completed, so no cache-wide
+  // write-back or invalidation is needed. The last arrival also resets the
+  // counter for the next launch.
+  if (split) {
+    const int64_t per = (int64_t)f.part_floats * 256;
+    const int64_t nsub = (int64_t)p.hkv * p.n_qtiles;
+    const int64_t sub = (int64_t)w.g * p.n_qtiles + w.qt;
+    auto state = [&](int k) { return f.split_part + ((int64_t)(slot + k) * nsub + sub) * per; };
+    auto put = [](float* q, float v) {
+      __hip_atomic_store(q, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    auto get = [](const float* q) {
+      return __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    {
+      float* st = state(part);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int qb = 0; qb < MB; ++qb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) put(st + ((db * MB + qb) * 4 + e) * 256 + tid, oacc[db][qb][e]);
+#pragma unroll
+      for (int qb = 0; qb < MB; ++qb) {
+        put(st + (NDB * MB * 4 + qb) * 256 + tid, mrow[qb]);
+        put(st + (NDB * MB * 4 + MB + qb) * 256 + tid, lrow[qb]);
+      }
+    }
+    // this thread's stores are complete (the clobber keeps them above it)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // and so are every other thread's; lds_pages is no longer read
+    if (tid == 0) {
+      int32_t* ctr = f.split_count + ((int64_t)w.b * p.hkv + w.g) * p.n_qtiles + w.qt;
+      const int arrived = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int last = arrived == parts - 1 ? 1 : 0;
+      if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      lds_pages[0] = last;
+    }
+    __syncthreads();  // the state loads below are issued after the count was taken
+    if (lds_pages[0] == 0) return;
+    for (int k = 0; k < parts; ++k) {
+      if (k == part) continue;
+      const float* st = state(k);
+#pragma unroll
+      for (int qb = 0; qb < MB; ++qb) {
+        const float m2 = get(st + (NDB * MB * 4 + qb) * 256 + tid);
+        const float l2 = get(st + (NDB * MB * 4 + MB + qb) * 256 + tid);
+        const float m_new = fmaxf(mrow[qb], m2);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float a1 = fast_exp2((mrow[qb] - m_use) * c2);
+        const float a2 = fast_exp2((m2 - m_use) * c2);
+        mrow[qb] = m_new;
+        lrow[qb] = lrow[qb] * a1 + l2 * a2;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
-          for (int qb = 0; qb < MB; ++qb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) put(part + ((db * MB + qb) * 4 + e) * 256 + tid, oacc[db][qb][e]);
-#pragma unroll
-        for (int qb = 0; qb < MB; ++qb) {
-          put(part + (NDB * MB * 4 + qb) * 256 + tid, mrow[qb]);
-          put(part + (NDB * MB * 4 + MB + qb) * 256 + tid, lrow[qb]);
-        }
-        // this thread's stores are complete (the clobber keeps them above)
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();  // and so are every other thread's
-        if (tid == 0) __hip_atomic_store(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        continue;  // on to the short request
-      }
-      // The page table of the last window is no longer read: its first entry
-      // carries whether the partial state arrived within the bounded wait.
-      if (tid == 0) {
-        int got = 0;
-        for (int it = 0; it < kPairSpin; ++it) {
-          if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
-            got = 1;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(2);
-        }
-        if (!got)
-          record_fault(&p.hdr->error_bits, &p.hdr->fault_count, &p.hdr->first_value,
-                       kErrPairWait, (int32_t)slot);
-        else  // ready for the next launch
-          __hip_atomic_store(flag, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        lds_pages[0] = got;
-      }
-      __syncthreads();  // the slot loads below are issued after the flag was seen
-      if (lds_pages[0] != 0) {
-#pragma unroll
-        for (int qb = 0; qb < MB; ++qb) {
-          const float m2 = get(part + (NDB * MB * 4 + qb) * 256 + tid);
-          const float l2 = get(part + (NDB * MB * 4 + MB + qb) * 256 + tid);
-          const float m_new = fmaxf(mrow[qb], m2);
-          const float m_use = m_new == -INFINITY ? 0.f : m_new;
-          const float a1 = fast_exp2((mrow[qb] - m_use) * c2);
-          const float a2 = fast_exp2((m2 - m_use) * c2);
-          mrow[qb] = m_new;
-          lrow[qb] = lrow[qb] * a1 + l2 * a2;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              oacc[db][qb][e] = oacc[db][qb][e] * a1 + get(part + ((db * MB + qb) * 4 + e) * 256 + tid) * a2;
-        }
+          for (int e = 0; e < 4; ++e)
+            oacc[db][qb][e] = oacc[db][qb][e] * a1 + get(st + ((db * MB + qb) * 4 + e) * 256 + tid) * a2;
       }
     }
   }
 
-  if constexpr (DEFER) {  // the slot table, now that the prompt is done
-    sl_commit(0, t_src, t_page);
-    for (int base = 256 * TR; base < n_sl; base += 256 * TR) {
-      sl_parents(base, t_src);
-      sl_pages(base, t_src, t_page);
-      sl_commit(base, t_src, t_page);
+  if constexpr (TAILS1) {  // the slot table, now that the prompt is done
+    if (split) {
+      sl_build(0);
+    } else if constexpr (DEFER) {
+      sl_commit(0, t_src, t_page);
+      sl_build(256 * TR);
     }
   }
 
@@ -771,7 +745,7 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
   // round trips, measured slower.)
   const int kw_lo = (w.qt * rt + p.group - 1) / p.group;
   const int kw_hi = min(p.W, ((w.qt + 1) * rt + p.group - 1) / p.group);
-  const int n_tw = fused && n_tail > 0 && finishes ? (kw_hi - kw_lo) * CPR : 0;
+  const int n_tw = fused && n_tail > 0 ? (kw_hi - kw_lo) * CPR : 0;
   auto tw_load = [&](int base, auto& page, auto& kd, auto& vd) {
     constexpr int N = (int)(sizeof(page) / sizeof(int32_t));
 #pragma unroll
@@ -1075,10 +1049,9 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
   }
 
   // ---- the current tokens (see above); the unrolled batch holds all of a
-  // wide beam's tasks, fewer in the paired kernel, where the next segment's
-  // state is live across the loads
+  // wide beam's tasks
   if (n_tw > 0) {
-    constexpr int TW = PAIR ? 4 : 16;
+    constexpr int TW = 16;
     for (int base = 0; base < n_tw; base += 256 * TW) {
       int32_t page[TW];
       u32x4 kd[TW], vd[TW];
@@ -1086,13 +1059,12 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
       tw_store(base, page, kd, vd);
     }
   }
-  }  // segments
 }
 
-template <typename T, int D, int MB, int KT, int NST, int MODE, bool PAIR, bool ORD = false>
+template <typename T, int D, int MB, int KT, int NST, int MODE>
 __global__ __launch_bounds__(256, (prefix_min_blocks<D, MB>())) void prefix_mfma_kernel(PrefixParams p,
                                                                                           FusedParams f) {
-  prefix_body<T, D, MB, KT, NST, MODE, PAIR, ORD>(p, f, blockIdx.x, false);
+  prefix_body<T, D, MB, KT, NST, MODE>(p, f, blockIdx.x, false);
 }
 
 // A mixed step in one launch: n_dec beam-step workgroups (dp, df) and n_pre
@@ -1120,7 +1092,7 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, 1>())) void mixed_step_k
     else done_p += cnt;
   }
   // one copy of the body; the parameters are picked per workgroup
-  prefix_body<T, D, 1, KT, NST, 4, false>(pre ? pp : dp, pre ? pf : df, idx, pre);
+  prefix_body<T, D, 1, KT, NST, 4>(pre ? pp : dp, pre ? pf : df, idx, pre);
 }
 
 // Two plans' shared-key attention in one launch (MODE 0, one 16-row query
@@ -1132,7 +1104,7 @@ __global__ __launch_bounds__(256, (prefix_min_blocks<D, 1>())) void prefix_two_k
     PrefixParams a, PrefixParams b, int n_a) {
   const FusedParams none{};
   const bool second = (int)blockIdx.x >= n_a;
-  prefix_body<T, D, 1, KT, NST, 0, false>(second ? b : a, none,
+  prefix_body<T, D, 1, KT, NST, 0>(second ? b : a, none,
                                           second ? (int)blockIdx.x - n_a : (int)blockIdx.x, false);
 }
 
@@ -1233,55 +1205,33 @@ __global__ __launch_bounds__(256) void prefix_simt_kernel(PrefixParams p) {
 }
 
 // Tile size and pipeline depth per head_dim: 64 KB of K/V stages per workgroup.
-template <typename T, int MODE, bool PAIR>
+template <typename T, int MODE>
 static void launch_mfma(const PrefixParams& p, const FusedParams& f, int head_dim, int mb,
                         unsigned blocks, hipStream_t s) {
 #define BSP_PFX(DD, MBB, KTT, NS) \
-  prefix_mfma_kernel<T, DD, MBB, KTT, NS, MODE, PAIR><<<blocks, 256, 0, s>>>(p, f)
-  // the fused step in the plan's longest-first order (only where the plan turns
-  // it on: two query blocks per wave, head_dim 64 or 128)
-  if constexpr (MODE == 1 && !PAIR) {
-    if (p.req_order != nullptr && mb == 2 && head_dim == 128) {
-      prefix_mfma_kernel<T, 128, 2, 64, 2, 1, false, true><<<blocks, 256, 0, s>>>(p, f);
-      return;
-    }
-    if (p.req_order != nullptr && mb == 2 && head_dim == 64) {
-      prefix_mfma_kernel<T, 64, 2, 64, 4, 1, false, true><<<blocks, 256, 0, s>>>(p, f);
-      return;
-    }
-  }
-  if constexpr (PAIR) {  // MB <= 2, head_dim <= 128
-    if (head_dim == 64) {
-      if (mb == 1) BSP_PFX(64, 1, 64, 4);
-      else BSP_PFX(64, 2, 64, 4);
-    } else {
-      if (mb == 1) BSP_PFX(128, 1, 32, 4);
+  prefix_mfma_kernel<T, DD, MBB, KTT, NS, MODE><<<blocks, 256, 0, s>>>(p, f)
+  if (head_dim == 64) {
+    if (mb == 1) BSP_PFX(64, 1, 64, 4);
+    else if (mb == 2) BSP_PFX(64, 2, 64, 4);
+    else BSP_PFX(64, 3, 64, 4);
+  } else if (head_dim == 128) {
+    // The fused step at one or two query blocks per wave, and the partial-state
+    // kernel at one, stream 64-key tiles through a two-stage ring (the same LDS
+    // as four stages of 32 keys, half the barriers, waits and row-max
+    // reductions per key): 3-4% faster at one block (fused), ~1-2% at two and
+    // ~2.5% for the partial-state kernel. At three blocks the 64-key tile
+    // spills registers.
+    if (mb == 1) {
+      if constexpr (MODE == 1 || MODE == 0) BSP_PFX(128, 1, 64, 2);
+      else BSP_PFX(128, 1, 32, 4);
+    } else if (mb == 2) {
+      if constexpr (MODE == 1) BSP_PFX(128, 2, 64, 2);
       else BSP_PFX(128, 2, 32, 4);
+    } else {
+      BSP_PFX(128, 3, 32, 4);
     }
-  } else {
-    if (head_dim == 64) {
-      if (mb == 1) BSP_PFX(64, 1, 64, 4);
-      else if (mb == 2) BSP_PFX(64, 2, 64, 4);
-      else BSP_PFX(64, 3, 64, 4);
-    } else if (head_dim == 128) {
-      // The fused step at one or two query blocks per wave, and the partial-state
-      // kernel at one, stream 64-key tiles through a two-stage ring (the same LDS
-      // as four stages of 32 keys, half the barriers, waits and row-max
-      // reductions per key): 3-4% faster at one block (fused), ~1-2% at two and
-      // ~2.5% for the partial-state kernel. At three blocks the 64-key tile
-      // spills registers.
-      if (mb == 1) {
-        if constexpr (MODE == 1 || MODE == 0) BSP_PFX(128, 1, 64, 2);
-        else BSP_PFX(128, 1, 32, 4);
-      } else if (mb == 2) {
-        if constexpr (MODE == 1) BSP_PFX(128, 2, 64, 2);
-        else BSP_PFX(128, 2, 32, 4);
-      } else {
-        BSP_PFX(128, 3, 32, 4);
-      }
-    } else {  // pick_mb: one query block per wave at head_dim 256
-      BSP_PFX(256, 1, 32, 2);
-    }
+  } else {  // pick_mb: one query block per wave at head_dim 256
+    BSP_PFX(256, 1, 32, 2);
   }
 #undef BSP_PFX
 }
@@ -1299,8 +1249,8 @@ hipError_t launch_prefix(const PrefixParams& p, int dtype, int head_dim, int row
     if (mb < 1 || mb > pick_mb(head_dim, 64 * 3) || rows_per_tile % 64 != 0)
       return hipErrorInvalidValue;
     const FusedParams none{};
-    if (dtype == BSP_F16) launch_mfma<_Float16, 0, false>(p, none, head_dim, mb, blocks, s);
-    else launch_mfma<__bf16, 0, false>(p, none, head_dim, mb, blocks, s);
+    if (dtype == BSP_F16) launch_mfma<_Float16, 0>(p, none, head_dim, mb, blocks, s);
+    else launch_mfma<__bf16, 0>(p, none, head_dim, mb, blocks, s);
   }
   return hipGetLastError();
 }
@@ -1334,8 +1284,8 @@ hipError_t launch_prefill(const PrefixParams& p, const FusedParams& f, int dtype
 // wave (as in the fused step: ~5% faster on short chunks), else four stages.
 #define BSP_PRE(TT, DD, MBB, KTT)                                                   \
   prefix_mfma_kernel<TT, DD, MBB, KTT,                                             \
-                     (KTT == 64 && DD == 128) || (DD == 256 && MBB == 1) ? 2 : 4, 3, \
-                     false><<<blocks, 256, 0, s>>>(p, f)
+                     (KTT == 64 && DD == 128) || (DD == 256 && MBB == 1) ? 2 : 4, \
+                     3><<<blocks, 256, 0, s>>>(p, f)
 #define BSP_PRE_T(TT)                                      \
   if (head_dim == 64) {                                    \
     if (mb == 1) BSP_PRE(TT, 64, 1, 64);                   \
@@ -1365,7 +1315,7 @@ bool mixed_step_supported(const PrefixParams& dp, const FusedParams& df, int dty
                           int rows_per_req, int tail_pad, int pre_mb) {
   if (dtype == BSP_F32 || head_dim > 128 || pre_mb != 1) return false;
   if (pick_mb(head_dim, rows_per_req) != 1 || dp.n_qtiles != 1) return false;
-  if (df.pairs != nullptr && df.n_pairs > 0) return false;
+  if (df.split_count != nullptr) return false;
   const int nbt_max = min(dp.W, 63 / dp.group + 2);
   return (int64_t)nbt_max * tail_pad <= kTailSlots;  // the beam step's tails in the LDS table
 }
@@ -1391,26 +1341,19 @@ hipError_t launch_mixed_step(const PrefixParams& dp, const FusedParams& df, cons
 }
 
 hipError_t launch_decode_step(const PrefixParams& p, const FusedParams& f, int dtype,
-                              int head_dim, int rows_per_req, int tail_pad, hipStream_t s) {
-  const unsigned blocks = (unsigned)(p.B * p.hkv * p.n_qtiles);
+                              int head_dim, int rows_per_req, int n_items, int tail_pad,
+                              hipStream_t s) {
+  const unsigned blocks = (unsigned)(n_items * p.hkv * p.n_qtiles);
   if (blocks == 0) return hipSuccess;
   const int mb = pick_mb(head_dim, rows_per_req);
   // beams with a row in one query tile, at most; their tail slots must fit the LDS table
   const int nbt_max = min(p.W, (64 * mb - 1) / p.group + 2);
   if ((int64_t)nbt_max * tail_pad <= kTailSlots) {
-    // balanced pairs when the plan built them and the tile shape allows them
-    if (f.pairs != nullptr && f.n_pairs > 0 && mb <= kPairMaxMB && head_dim <= 128 &&
-        p.n_qtiles == 1 && f.part_floats >= pair_part_floats(head_dim, mb)) {
-      const unsigned pblocks = (unsigned)(f.n_pairs * p.hkv * 2);
-      if (dtype == BSP_F16) launch_mfma<_Float16, 1, true>(p, f, head_dim, mb, pblocks, s);
-      else launch_mfma<__bf16, 1, true>(p, f, head_dim, mb, pblocks, s);
-    } else {
-      if (dtype == BSP_F16) launch_mfma<_Float16, 1, false>(p, f, head_dim, mb, blocks, s);
-      else launch_mfma<__bf16, 1, false>(p, f, head_dim, mb, blocks, s);
-    }
+    if (dtype == BSP_F16) launch_mfma<_Float16, 1>(p, f, head_dim, mb, blocks, s);
+    else launch_mfma<__bf16, 1>(p, f, head_dim, mb, blocks, s);
   } else {
-    if (dtype == BSP_F16) launch_mfma<_Float16, 2, false>(p, f, head_dim, mb, blocks, s);
-    else launch_mfma<__bf16, 2, false>(p, f, head_dim, mb, blocks, s);
+    if (dtype == BSP_F16) launch_mfma<_Float16, 2>(p, f, head_dim, mb, blocks, s);
+    else launch_mfma<__bf16, 2>(p, f, head_dim, mb, blocks, s);
   }
   return hipGetLastError();
 }

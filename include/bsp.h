@@ -266,11 +266,13 @@ bsp_status_t bsp_merge(int32_t rows, int32_t heads, int32_t head_dim, int32_t n_
  *   k_pool, v_pool written at each beam's slot for position S_b - 1
  *   o_out          dtype [B * W][Hq][D]; lse_out float [B * W][Hq] or null
  * bf16/f16 only (BSP_ERR_UNSUPPORTED for f32: use the separate calls).
- * When the plan paired requests (see bsp_debug_plan_pairs), two workgroups
- * share a long request's prompt per KV head and hand one partial state over
- * through the workspace with a bounded wait; a wait that runs out is recorded
- * in the error word (bit 16) for bsp_check. Calls that share one workspace
- * must be ordered on one stream (as for every call of a plan).
+ * Work items go longest first. When the plan split a request's prompt into
+ * chunks (see bsp_debug_plan_items), each chunk's workgroup leaves its partial
+ * state in the workspace and counts itself with one atomic add; the last to
+ * arrive merges the states exactly through their log-sum-exp (PR #21738,
+ * Solution) and finishes the request. No workgroup waits for another. Calls
+ * that share one workspace must be ordered on one stream (as for every call
+ * of a plan).
  */
 bsp_status_t bsp_decode_step(bsp_plan_t plan, const void* q, const void* k_new,
                              const void* v_new, int64_t new_row_stride, void* k_pool,
@@ -361,17 +363,17 @@ bsp_status_t bsp_check(bsp_plan_t plan, hipStream_t stream);
 bsp_status_t bsp_debug_plan_tables(bsp_plan_t plan, int32_t* indptr_h, int32_t* pages_h,
                                    int32_t* n_keys_h, int32_t* valid_h, int32_t* tail_h);
 
-/* Host copy of the current plan's balanced pairs (bsp_decode_step, beam
- * decode with bf16/f16, head_dim <= 128, at most 128 query rows per request
- * and KV head, two or more requests, none for cached-prefix plans). By
- * default bsp_plan pairs when the longest prompt is at least three times the
- * shortest; BSP_PAIRS=1 (always) or 0 (never) in the environment at
- * bsp_plan_create overrides that. *n_pairs_h, and when pairs_h is not null,
- * int32 [n_pairs][3] = (long request a, short request b or -1, split). The
- * step attends a over [0, split) in one workgroup and over [split, P_a) plus
- * all of b in another, per KV head, and merges a's two partial states
- * exactly through their log-sum-exp (PR #21738, Solution). */
-bsp_status_t bsp_debug_plan_pairs(bsp_plan_t plan, int32_t* n_pairs_h, int32_t* pairs_h);
+/* Host copy of the current plan's work items of bsp_decode_step (beam decode,
+ * bf16/f16), in the order the step dispatches them (longest first):
+ * *n_items_h, and when items_h is not null, int32 [n_items][4] = (request,
+ * first key, end key, chunks of that request). A request whose prompt the
+ * plan split has one item per chunk (TensorRT-LLM PR #21738, review thread on
+ * the FA4 split-generation kernels: split the keys, then merge the splits).
+ * By default bsp_plan splits when its model of the step (items dealt longest
+ * first to one round of workgroups) gets at least 5% shorter;
+ * BSP_SPLIT=<keys> in the environment at bsp_plan_create forces chunks of
+ * that many keys (rounded up to 64) and BSP_SPLIT=0 turns splitting off. */
+bsp_status_t bsp_debug_plan_items(bsp_plan_t plan, int32_t* n_items_h, int32_t* items_h);
 
 /* Device: resolve every tail key to its flat pool slot (page * page_size +
  * row), int32 [B][W][tail_len], -1 past each request's tail; the same index

@@ -176,7 +176,7 @@ def test_tail_slots_bit_exact_1200_random_batches():
             pr = (0, int(rng.integers(1, 3 * ps + 2)))
         cfg = BeamConfig("idx1200", batch=int(rng.integers(1, 5)), beam=int(rng.integers(1, 7)),
                          num_q_heads=2, num_kv_heads=1, head_dim=64, dtype="bf16", page_size=ps,
-                         prefix_range=pr, tail_range=(0, int(rng.integers(0, 2 * ps + 3))),
+                         prefix_range=pr, tail_range=(0, int(rng.integers(1, 2 * ps + 3))),
                          shuffle_pages=bool(rng.integers(0, 2)))
         inp = synth.make_beam_step(cfg, trial, page_stride=int(rng.integers(1, 3)), garbage="unit")
         n_full_last += int(((inp.prefix_len % ps) == 0).sum())
@@ -636,38 +636,42 @@ def test_full_size_wide_beam_fused_sampled():
         assert np.abs(lse[b, k] - fl[0]).max() <= tl
 
 
-# ------------------------------------ balanced pairs in the fused step
+# ------------------------------------ split prompts in the fused step
 
-PAIR_CASES = {
-    "odd_spread_bf16": dict(cfg="qwen3_0p6b", batch=7, prefix_range=(0, 1200)),
-    "two_bf16": dict(cfg="qwen3_0p6b", batch=2, prefix_range=(32, 1500)),
-    "equal_bf16": dict(cfg="qwen3_0p6b", batch=4, prefix_range=(512, 512)),
-    "no_tails_bf16": dict(cfg="qwen3_0p6b", batch=4, prefix_range=(0, 900), tail_range=(0, 0)),
-    "mb2_d128_f16": dict(cfg="qwen3_4b", batch=5, prefix_range=(64, 3000)),
-    "mb2_d64_f16": dict(cfg="qwen3_4b", batch=4, head_dim=64, prefix_range=(100, 2400)),
-    "nsample_bf16": dict(cfg="nsample", batch=5, prefix_range=(30, 1000)),
+SPLIT_CASES = {
+    "odd_spread_bf16": (dict(cfg="qwen3_0p6b", batch=7, prefix_range=(0, 1200)), 128),
+    "two_bf16": (dict(cfg="qwen3_0p6b", batch=2, prefix_range=(32, 1500)), 192),
+    "equal_bf16": (dict(cfg="qwen3_0p6b", batch=4, prefix_range=(512, 512)), 256),
+    "no_tails_bf16": (dict(cfg="qwen3_0p6b", batch=4, prefix_range=(0, 900), tail_range=(0, 0)), 64),
+    "mb2_d128_f16": (dict(cfg="qwen3_4b", batch=5, prefix_range=(64, 3000)), 512),
+    "mb2_d64_f16": (dict(cfg="qwen3_4b", batch=4, head_dim=64, prefix_range=(100, 2400)), 320),
+    "mb3_wide_bf16": (dict(cfg="wide_beam", batch=3, prefix_range=(100, 1000)), 256),
+    "d256_f16": (dict(cfg="qwen3_4b", batch=3, head_dim=256, prefix_range=(100, 900)), 128),
+    "nsample_bf16": (dict(cfg="nsample", batch=5, prefix_range=(30, 1000)), 128),
+    "query_tiles_bf16": (dict(cfg=BeamConfig("qt", 2, 90, 10, 2, 64, "bf16", 16, (40, 400), (1, 6), True)), 64),
+    "long_tails_bf16": (dict(cfg=BeamConfig("lt", 1, 192, 2, 2, 64, "bf16", 16, (100, 300), (17, 20), True)), 64),
+    "page_size_1_bf16": (dict(cfg=BeamConfig("p1", 2, 6, 4, 2, 128, "bf16", 1, (40, 400), (1, 5), True)), 64),
 }
 
 
-@pytest.mark.parametrize("case", list(PAIR_CASES))
-def test_decode_step_balanced_pairs(case, monkeypatch):
-    """The step with balanced pairs (the long request of a pair split between two
-    workgroups, its partial states merged) matches the oracle on two launches
-    in a row (each launch leaves the pair flags cleared for the next), and so
-    does the same step with pairing switched off."""
-    kw = dict(PAIR_CASES[case])
+@pytest.mark.parametrize("case", list(SPLIT_CASES))
+def test_decode_step_split_prompts(case, monkeypatch):
+    """Prompts split into chunks (BSP_SPLIT forces the chunk): each chunk's
+    workgroup leaves its partial state and the last to arrive merges them and
+    finishes the request. Two launches in a row match the oracle (the last
+    arrival resets each counter for the next launch), the token write is
+    bit-exact, and the same step unsplit matches too."""
+    kw, chunk = dict(SPLIT_CASES[case][0]), SPLIT_CASES[case][1]
     cfg = kw.pop("cfg")
-    monkeypatch.setenv("BSP_PAIRS", "1")
+    monkeypatch.setenv("BSP_SPLIT", str(chunk))
     inp = synth.make_beam_step(cfg, 5, **kw)
     P = inp.prefix_len
-    say(f"pairs {case} P={P.tolist()} T={inp.tail_len.tolist()}")
+    say(f"split {case} chunk={chunk} P={P.tolist()} T={inp.tail_len.tolist()}")
     s = S.upload_beam_step(inp, DEV)
     S.plan_beam_step(s)
-    pairs = B.bsp_debug_plan_pairs(s.plan)
-    assert len(pairs) == (inp.batch + 1) // 2
-    lo, hi = kw.get("prefix_range", (0, 0))
-    if hi - lo >= 500:
-        assert any(split < P[a] for a, b, split in pairs), pairs
+    items = B.bsp_debug_plan_items(s.plan)
+    assert (items[:, 3] > 1).any(), items
+    say(f"  items={len(items)} split={(items[:, 3] > 1).sum()}")
     ref = _applied(synth.make_beam_step(cfg, 5, **kw))
     fo, fl = oracle.beam_decode_attention(ref)
     for rep in range(2):
@@ -679,40 +683,68 @@ def test_decode_step_balanced_pairs(case, monkeypatch):
     assert torch.equal(s.k_pool.cpu(), S.to_device(ref.k_pool, inp.dtype, "cpu")), case
     assert torch.equal(s.v_pool.cpu(), S.to_device(ref.v_pool, inp.dtype, "cpu")), case
 
-    monkeypatch.setenv("BSP_PAIRS", "0")
+    monkeypatch.setenv("BSP_SPLIT", "0")
     s2 = S.upload_beam_step(synth.make_beam_step(cfg, 5, **kw), DEV)
     S.plan_beam_step(s2)
-    assert len(B.bsp_debug_plan_pairs(s2.plan)) == 0
+    assert (B.bsp_debug_plan_items(s2.plan)[:, 3] == 1).all()
     S.run_decode_step(s2)
     B.bsp_check(s2.plan)
     torch.cuda.synchronize()
-    assert_close(s2.out, s2.lse_out, fo, fl, inp.dtype, f"{case} unpaired")
+    assert_close(s2.out, s2.lse_out, fo, fl, inp.dtype, f"{case} unsplit")
 
 
-@pytest.mark.parametrize("cfg,pairs_env", [("qwen3_0p6b", None), ("qwen3_0p6b", "1"),
-                                           ("qwen3_4b", None), ("qwen3_4b", "1")])
-def test_full_size_fused_sampled(cfg, pairs_env, monkeypatch):
-    """The bench's full shapes (64 requests x 30 beams) through the fused step,
-    as planned (no pairs for these prompt spreads) and with balanced pairs
-    forced; sampled beams against the oracle."""
-    if pairs_env is not None:
-        monkeypatch.setenv("BSP_PAIRS", pairs_env)
+def test_decode_step_split_replanned_between_launches(monkeypatch):
+    """One plan and workspace, re-planned between launches for batches of
+    different sizes (so the split, the items and the counters' layout change):
+    every step matches the oracle."""
+    kw = dict(batch=5, prefix_range=(100, 1400))
+    ref = _applied(synth.make_beam_step("qwen3_0p6b", 9, **kw))
+    fo, fl = oracle.beam_decode_attention(ref)
+    monkeypatch.setenv("BSP_SPLIT", "128")
+    inp = synth.make_beam_step("qwen3_0p6b", 9, **kw)
+    s = S.upload_beam_step(inp, DEV)
+    W = inp.beam
+    for nb in (5, 3, 5, 2):
+        B.bsp_plan(s.plan, nb, W, 1, inp.prefix_len[:nb], inp.seq_len[:nb],
+                   np.ascontiguousarray(inp.block_tables[:nb]), s.workspace)
+        assert (B.bsp_debug_plan_items(s.plan)[:, 3] > 1).any()
+        S.run_decode_step(s)
+        B.bsp_check(s.plan)
+        torch.cuda.synchronize()
+        rows = nb * W
+        assert_close(s.out[:rows], s.lse_out[:rows], fo[:nb], fl[:nb], "bf16",
+                     f"re-planned batch of {nb}")
+
+
+@pytest.mark.parametrize("cfg,split_env", [("qwen3_0p6b", None), ("qwen3_0p6b", "256"),
+                                           ("qwen3_4b", None), ("qwen3_4b", "512"),
+                                           ("wide_beam", "1024")])
+def test_full_size_fused_sampled(cfg, split_env, monkeypatch):
+    """The bench's full shapes through the fused step, as planned (no split at
+    these prompt spreads) and with every prompt split that the plan's partial-
+    state reserve allows; sampled beams against the oracle."""
+    if split_env is not None:
+        monkeypatch.setenv("BSP_SPLIT", split_env)
+    else:
+        monkeypatch.delenv("BSP_SPLIT", raising=False)
     inp = synth.make_beam_step(cfg, 0, garbage="unit")
     s = S.upload_beam_step(inp, DEV)
     S.plan_beam_step(s)
-    pairs = B.bsp_debug_plan_pairs(s.plan)
-    say(f"full-size fused {cfg}: pairs={len(pairs)}")
-    assert len(pairs) == (32 if pairs_env == "1" else 0)
+    items = B.bsp_debug_plan_items(s.plan)
+    n_split = int((items[:, 3] > 1).sum())
+    say(f"full-size fused {cfg}: items={len(items)} split items={n_split}")
+    assert (n_split > 0) == (split_env is not None)
     S.run_decode_step(s)
     B.bsp_check(s.plan)
     torch.cuda.synchronize()
     ref = _applied(inp)
     rng = np.random.default_rng(3)
     W, Hq, D = inp.beam, inp.num_q_heads, inp.head_dim
-    # the longest and the shortest prompt (the first pair), plus random ones
+    split_reqs = sorted({int(b) for b, lo, hi, n in items if n > 1})
     a, b = int(np.argmax(inp.prefix_len)), int(np.argmin(inp.prefix_len))
     picks = [(a, 0), (a, W - 1), (b, 1)]
-    picks += [(int(x), int(k)) for x, k in zip(rng.integers(0, inp.batch, 10), rng.integers(0, W, 10))]
+    picks += [(r, int(rng.integers(0, W))) for r in split_reqs[:4]]
+    picks += [(int(x), int(k)) for x, k in zip(rng.integers(0, inp.batch, 8), rng.integers(0, W, 8))]
     out = s.out.float().cpu().numpy().reshape(inp.batch, W, Hq, D)
     lse = s.lse_out.cpu().numpy().reshape(inp.batch, W, Hq)
     to, tl = TOL[inp.dtype]

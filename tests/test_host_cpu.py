@@ -230,86 +230,124 @@ def test_check_mode_requires_shared_prompt_blocks(monkeypatch):
     assert name == "BSP_ERR_ARG" and "share prompt block" in msg
 
 
-# ------------------------------------------------ balanced pairs (host plan)
+# ------------------------------------- fused-step work items and splits (host plan)
 
-def _pair_plan(B_, W, G, D, dtype, prefix, key_bucket=0):
+def _item_plan(B_, W, G, D, dtype, prefix, key_bucket=0, hkv=8):
     ps = 32
     nb = -(-(max(prefix) + 8) // ps)
-    desc = B.make_desc(2 * G, 2, D, ps, 4096, dtype, key_bucket=key_bucket,
+    desc = B.make_desc(hkv * G, hkv, D, ps, 1 << 20, dtype, key_bucket=key_bucket,
                        max_cache_rows=nb * ps if key_bucket else 0)
     plan = B.Plan(desc, B_, W, nb, nb * ps, 1, host_only=True)
     P = np.asarray(prefix, np.int32)
-    bt = np.arange(B_ * W * nb, dtype=np.int32).reshape(B_, W, nb) % 4096
+    bt = np.arange(B_ * W * nb, dtype=np.int32).reshape(B_, W, nb) % (1 << 20)
     bt[:, :, :] = bt[:, :1, :]  # every beam shares its request's blocks
     S = P if key_bucket else P + 3
     B.bsp_plan(plan, B_, W, 1, P, S.astype(np.int32), bt)
-    return B.bsp_debug_plan_pairs(plan)
+    return B.bsp_debug_plan_items(plan)
 
 
-def test_pairs_cover_every_request_once_and_balance_keys(monkeypatch):
-    """Longest prompt with shortest: each request in exactly one pair, the long
-    one split at a multiple of 64 so that both workgroups stream about as many
-    keys (X: a's first keys; Y: a's last keys and all of b)."""
-    monkeypatch.setenv("BSP_PAIRS", "1")
+def _check_items(items, P, chunk=None):
+    """Each request's items are contiguous, disjoint chunks covering [0, P_b)
+    (one item [0, P_b) when unsplit), listed longest first."""
+    lens = items[:, 2] - items[:, 1]
+    assert np.all(np.diff(lens) <= 0), "items must be listed longest first"
+    for b, Pb in enumerate(P):
+        mine = items[items[:, 0] == b]
+        mine = mine[np.argsort(mine[:, 1])]
+        n = len(mine)
+        assert n >= 1 and np.all(mine[:, 3] == n)
+        assert mine[0, 1] == 0 and mine[-1, 2] == Pb
+        assert np.all(mine[1:, 1] == mine[:-1, 2])
+        if n > 1:
+            assert np.all(mine[:, 2] > mine[:, 1])
+            if chunk is not None:
+                assert np.all(mine[:, 1] % chunk == 0)
+                assert np.all(mine[:-1, 2] - mine[:-1, 1] == chunk)
+
+
+def test_items_cover_every_request_once(monkeypatch):
+    """Random batches, unsplit, forced chunks and the automatic choice."""
     rng = np.random.default_rng(7)
     for trial in range(300):
-        Bn = int(rng.integers(2, 12))
-        P = rng.integers(0, 2500, size=Bn)
-        pairs = _pair_plan(Bn, 30, 2, 128, "bf16", P)
-        assert len(pairs) == (Bn + 1) // 2
-        seen = [int(r) for r in pairs[:, 0]] + [int(r) for r in pairs[:, 1] if r >= 0]
-        assert sorted(seen) == list(range(Bn))
-        assert (pairs[:, 1] < 0).sum() == Bn % 2
-        a_len = P[pairs[:, 0]]
-        assert np.all(np.diff(a_len) <= 0)  # pairs in order of the long prompt
-        for a, b, split in pairs:
-            Pa, Pb = int(P[a]), int(P[b]) if b >= 0 else 0
-            assert b < 0 or Pa >= Pb
-            if b < 0:
-                assert split == Pa
-            elif split < Pa:
-                assert split % 64 == 0 and split >= 64
-                assert abs(split - (Pa - split + Pb)) <= 64
-            else:
-                assert split == Pa and Pa - Pb <= 128
+        Bn = int(rng.integers(1, 40))
+        P = rng.integers(0, 3000, size=Bn)
+        mode = trial % 3
+        if mode == 0:
+            monkeypatch.setenv("BSP_SPLIT", "0")
+        elif mode == 1:
+            monkeypatch.setenv("BSP_SPLIT", str(int(rng.integers(1, 1200))))
+        else:
+            monkeypatch.delenv("BSP_SPLIT", raising=False)
+        G = int(rng.choice([1, 2, 4]))
+        items = _item_plan(Bn, int(rng.integers(1, 40)), G, 128, "bf16", P)
+        chunk = None
+        if mode == 1:
+            chunk = -(-int(__import__("os").environ["BSP_SPLIT"]) // 64) * 64
+        _check_items(items, P, chunk)
+        if mode == 0:
+            assert np.all(items[:, 3] == 1) and len(items) == Bn
 
 
-@pytest.mark.parametrize("what", ["f32", "d256", "rows", "cached", "one", "env"])
-def test_pairs_only_where_the_step_supports_them(what, monkeypatch):
-    P = [2000, 100, 900, 1500]
-    kw = dict(B_=4, W=30, G=2, D=128, dtype="bf16", prefix=P)
-    assert len(_pair_plan(**kw)) == 2
+def test_forced_split_respects_the_partial_state_budget(monkeypatch):
+    """A forced split of every prompt goes through the requests longest first and
+    splits each one whose chunks still fit the plan's partial-state slots; the
+    rest stay whole, and the slots in use never exceed the reserve."""
+    monkeypatch.setenv("BSP_SPLIT", "64")
+    P = np.arange(64, dtype=np.int32) * 40 + 100
+    items = _item_plan(64, 96, 2, 128, "bf16", P)  # three 16-row blocks per wave
+    _check_items(items, P, 64)
+    split = sorted({int(b) for b, lo, hi, n in items if n > 1})
+    assert split and len(split) < 64
+    used = sum(-(-int(P[b]) // 64) for b in split)
+    slot_bytes = 4 * 256 * (8 * 3 * 4 + 6) * 8   # floats of a 48-row state x 256 threads x 8 heads
+    assert used <= (24 << 20) // slot_bytes
+    whole = [b for b in range(64) if b not in split]
+    # the longest whole request did not fit what was left after the longer ones
+    longer = [b for b in split if P[b] > P[max(whole, key=lambda x: P[x])]]
+    left = (24 << 20) // slot_bytes - sum(-(-int(P[b]) // 64) for b in longer)
+    assert -(-int(P[max(whole, key=lambda x: P[x])]) // 64) > left
+
+
+@pytest.mark.parametrize("what", ["f32", "cached"])
+def test_no_items_where_the_fused_step_does_not_run(what, monkeypatch):
+    monkeypatch.setenv("BSP_SPLIT", "64")
+    kw = dict(B_=4, W=30, G=2, D=128, dtype="bf16", prefix=[2000, 100, 900, 1500])
+    assert len(_item_plan(**kw)) > 4
     if what == "f32":
         kw["dtype"] = "f32"
-    elif what == "d256":
-        kw["D"] = 256
-    elif what == "rows":
-        kw["W"] = 65  # 130 query rows per request and KV head
-    elif what == "cached":
-        kw.update(key_bucket=64, W=1)
-    elif what == "one":
-        kw.update(B_=1, prefix=[2000])
     else:
-        monkeypatch.setenv("BSP_PAIRS", "0")
-    assert len(_pair_plan(**kw)) == 0
+        kw.update(key_bucket=64, W=1)
+    assert len(_item_plan(**kw)) == 0
 
 
-@pytest.mark.parametrize("prefix,paired", [([500, 450, 600, 420], False),
-                                           ([1600, 2400, 2000, 1900], False),
-                                           ([200, 800, 500, 700], True),
-                                           ([300, 899, 600, 500, 700], False),
-                                           ([300, 900, 600, 500, 700], True),
-                                           ([150, 800, 500, 700], True),
-                                           ([0, 100, 50], True),
-                                           ([0, 0, 0], False)])
-def test_pairs_chosen_for_wide_prompt_spread(prefix, paired, monkeypatch):
-    """Without BSP_PAIRS the planner pairs only when the longest prompt is at
-    least three times the shortest (and some prompt is non-empty)."""
-    monkeypatch.delenv("BSP_PAIRS", raising=False)
-    pairs = _pair_plan(len(prefix), 30, 2, 128, "bf16", prefix)
-    assert (len(pairs) > 0) == paired
-    monkeypatch.setenv("BSP_PAIRS", "1")
-    assert len(_pair_plan(len(prefix), 30, 2, 128, "bf16", prefix)) == (len(prefix) + 1) // 2
+@pytest.mark.parametrize("name,prefix,split", [
+    ("qwen3_0p6b spread 400-600", ("u", 64, 400, 600), False),
+    ("qwen3_4b spread 1600-2400", ("u", 64, 1600, 2400), False),
+    ("wide beam spread 2800-3200", ("u", 128, 2800, 3200), False),
+    ("spread 200-800", ("u", 64, 200, 800), False),
+    ("spread 100-1500", ("u", 64, 100, 1500), True),
+    ("four long prompts among short ones", ("few",), True),
+    ("empty prompts", ("z",), False),
+])
+def test_split_chosen_only_where_the_model_gains(name, prefix, split, monkeypatch):
+    """Without BSP_SPLIT the plan splits only when its model of the step gets
+    at least 5% shorter: not on the bench spreads, yes when a few prompts are
+    much longer than the rest."""
+    monkeypatch.delenv("BSP_SPLIT", raising=False)
+    rng = np.random.default_rng(3)
+    if prefix[0] == "u":
+        P = rng.integers(prefix[2], prefix[3] + 1, prefix[1])
+    elif prefix[0] == "few":
+        P = np.full(64, 300)
+        P[:4] = 3000
+    else:
+        P = np.zeros(16, np.int64)
+    W, G = (96, 2) if prefix[0] == "u" and prefix[1] == 128 else (30, 2)
+    items = _item_plan(len(P), W, G, 128, "bf16", P)
+    _check_items(items, P)
+    assert bool((items[:, 3] > 1).any()) == split, name
+    monkeypatch.setenv("BSP_SPLIT", "0")
+    assert not (_item_plan(len(P), W, G, 128, "bf16", P)[:, 3] > 1).any()
 
 
 # ------------------------------------------------ prefill plans (mixed steps)
