@@ -32,6 +32,7 @@
 
 #include "bsp_internal.h"
 #include "device_common.h"
+#include "tile_index.h"
 
 namespace bsp {
 
@@ -75,17 +76,6 @@ constexpr int kPageWin = 1024;
 constexpr int kTailSlots = 3072;
 // Lazy rescaling threshold of the online softmax, in base-2 exponent units.
 constexpr float kLazyLog2 = 8.f;
-
-// XOR swizzle of the 16-byte chunks of an LDS key row (a function of the low 4
-// row bits): chunk c of row r is stored at chunk c ^ swz(r). It keeps both the
-// K-operand reads (16 consecutive rows, one chunk each) and the V transpose
-// reads (4 rows x 2 chunks per 16 lanes) on distinct LDS banks, and it lets
-// 1 KB direct-to-LDS loads fill rows without padding.
-template <int D>
-__device__ __forceinline__ int lds_swz(int r) {
-  const int a = ((r & 1) << 1) ^ ((r & 2) << 1) ^ ((r >> 3) & 1);
-  return a ^ ((r & 4) ? (D == 64 ? 3 : 9) : 0);
-}
 
 // Wait until at most N vector-memory operations of this wave are in flight
 // (vmcnt only; LDS and export counters unconstrained).
@@ -198,6 +188,7 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
   const bool fused = FUSED && !is_pre;
   static_assert(MODE != 4 || MB == 1, "mixed steps take one query block per wave");
   using V8 = typename Mfma<T>::V8;
+  using TG = TileGeom<(int)sizeof(T), D, KT, NST>;  // LDS and global offsets (tile_index.h)
   constexpr int NDS = D / 32;                       // contraction steps of S^T
   constexpr int NDB = D / 16;                       // 16-row blocks of O^T
   constexpr int NKB = KT / 16;                      // 16-key blocks of S^T per tile
@@ -209,6 +200,7 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
   static_assert(NI >= 1 && TILE * sizeof(T) % 4096 == 0, "tile must split into 1 KB loads");
   static_assert(NST >= 2 && NST <= 4 && 2 * LPT < 64, "pipeline depth");
   __shared__ __attribute__((aligned(1024))) T lds_kv[NST][2][TILE];
+  T* const lds_ring = &lds_kv[0][0][0];  // the ring as one array (TileGeom offsets)
   __shared__ int lds_pages[kPageWin];
   __shared__ int lds_tail[TAILS1 ? kTailSlots : 1];
 
@@ -360,7 +352,7 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
                      kErrTailPage, page[i]);
         e = -1;
       } else {
-        e = ((page[i] * p.hkv + w.g) << shift) + (j & pmask);
+        e = (int32_t)(pool_row(page[i], p.hkv, w.g, shift, j & pmask, 1));
       }
       lds_tail[task] = e;
     }
@@ -449,7 +441,7 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const int r = kb * 16 + l16;
-        const V8 a = *reinterpret_cast<const V8*>(&lk[r * D + (((ds * 4 + l4) ^ lds_swz<D>(r)) << 3)]);
+        const V8 a = *reinterpret_cast<const V8*>(&lk[TG::k_read(r, ds * 4 + l4)]);
 #pragma unroll
         for (int qb = 0; qb < MB; ++qb) sacc[kb][qb] = Mfma<T>::mma(a, qv[qb][ds], sacc[kb][qb]);
       }
@@ -521,14 +513,14 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
 #pragma unroll
     for (int s2 = 0; s2 < NS2; ++s2) {
       const int ra = 32 * s2 + 4 * l4 + (l16 >> 2);   // row read by this lane (+16 for the upper half)
-      const int swa = lds_swz<D>(ra);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const int col = db * 16 + 4 * (l16 & 3);
-        const int off = (((col >> 3) ^ swa) << 3) + (col & 7);
-        // The operand is assembled from whole 32-bit words of the two reads.
-        const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr(&lv[ra * D + off]));
-        const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr(&lv[(ra + 16) * D + off]));
+        // The operand is assembled from whole 32-bit words of the two reads
+        // (rows ra and ra + 16 share the swizzle: it depends on the low 4 bits).
+        const int off = TG::v_read(ra, col);
+        const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr(&lv[off]));
+        const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr(&lv[off + 16 * D]));
         const V8 a = __builtin_bit_cast(V8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 #pragma unroll
         for (int qb = 0; qb < MB; ++qb) oacc[db][qb] = Mfma<T>::mma(a, pb[s2][qb], oacc[db][qb]);
@@ -600,32 +592,30 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
       if ((t0 & pmask) + KT <= pmask + 1) {
         // The tile lies in one page: one scalar base per pool, and each lane
         // adds its fixed offset (rows past the key range re-read row t0).
-        const int page = __builtin_amdgcn_readfirstlane(lds_pages[(t0 >> shift) - pg0]);
-        const int64_t base = ((((int64_t)page * p.hkv + w.g) << shift) + (t0 & pmask)) * D;
+        const int page = __builtin_amdgcn_readfirstlane(lds_pages[window_slot(t0, shift, pg0)]);
+        const int64_t base = pool_row(page, p.hkv, w.g, shift, t0 & pmask, D);
         const T* kb = kpool + base;
         const T* vb = vpool + base;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-          const int chunk = (wave * NI + i) * 64 + lane;
-          const int r = chunk / CPR;
-          const int c = (chunk % CPR) ^ lds_swz<D>(r);
+          const int r = TG::load_row(wave, i, lane);
+          const int c = TG::load_chunk(wave, i, lane);
           const unsigned voff = (unsigned)(((t0 + r < seg_hi ? r : 0) * D + c * 8) * (int)sizeof(T));
-          lds_dma16_s(kb, voff, &lds_kv[stage][0][(wave * NI + i) * (1024 / (int)sizeof(T))]);
-          lds_dma16_s(vb, voff, &lds_kv[stage][1][(wave * NI + i) * (1024 / (int)sizeof(T))]);
+          lds_dma16_s(kb, voff, &lds_ring[TG::ring_dst(stage, 0, wave, i)]);
+          lds_dma16_s(vb, voff, &lds_ring[TG::ring_dst(stage, 1, wave, i)]);
         }
         return;
       }
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const int chunk = (wave * NI + i) * 64 + lane;
-        const int r = chunk / CPR;
-        const int c = (chunk % CPR) ^ lds_swz<D>(r);
+        const int r = TG::load_row(wave, i, lane);
+        const int c = TG::load_chunk(wave, i, lane);
         int j = t0 + r;
         if (j >= seg_hi) j = t0;
-        const int page = lds_pages[(j >> shift) - pg0];
-        const int64_t off = ((((int64_t)page * p.hkv + w.g) << shift) + (j & pmask)) * D + c * 8;
-        lds_dma16(kpool + off, &lds_kv[stage][0][(wave * NI + i) * (1024 / (int)sizeof(T))]);
-        lds_dma16(vpool + off, &lds_kv[stage][1][(wave * NI + i) * (1024 / (int)sizeof(T))]);
+        const int page = lds_pages[window_slot(j, shift, pg0)];
+        const int64_t off = pool_row(page, p.hkv, w.g, shift, j & pmask, D) + c * 8;
+        lds_dma16(kpool + off, &lds_ring[TG::ring_dst(stage, 0, wave, i)]);
+        lds_dma16(vpool + off, &lds_ring[TG::ring_dst(stage, 1, wave, i)]);
       }
     };
 
@@ -662,8 +652,8 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
 
   // ---- a split request: this workgroup leaves its chunk's partial state in
   // its slot and counts its arrival on the request's counter (per KV head and
-  // query tile). The last to arrive merges the other chunks' states into its
-  // own (the exact log-sum-exp rule) and finishes the request; the others are
+  // query tile). The last to arrive merges all chunks' states (the exact
+  // log-sum-exp rule, in chunk order) and finishes the request; the others are
   // done. No workgroup waits for another. The states and the counter are
   // accessed only with agent-coherent loads, stores and one atomic add, and a
   // state is counted only after its stores have completed, so no cache-wide
@@ -706,9 +696,22 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
     }
     __syncthreads();  // the state loads below are issued after the count was taken
     if (lds_pages[0] == 0) return;
+    // The states are merged in chunk order, this workgroup's own read back like
+    // the others, so the result does not depend on which chunk arrived last.
     for (int k = 0; k < parts; ++k) {
-      if (k == part) continue;
       const float* st = state(k);
+      if (k == 0) {
+#pragma unroll
+        for (int qb = 0; qb < MB; ++qb) {
+          mrow[qb] = get(st + (NDB * MB * 4 + qb) * 256 + tid);
+          lrow[qb] = get(st + (NDB * MB * 4 + MB + qb) * 256 + tid);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) oacc[db][qb][e] = get(st + ((db * MB + qb) * 4 + e) * 256 + tid);
+        }
+        continue;
+      }
 #pragma unroll
       for (int qb = 0; qb < MB; ++qb) {
         const float m2 = get(st + (NDB * MB * 4 + qb) * 256 + tid);
@@ -773,8 +776,7 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
                        kErrTailPage, page[i]);
         continue;
       }
-      const int64_t dst =
-          ((((int64_t)page[i] * p.hkv + w.g) << shift) + ((ri.seq - 1) & pmask)) * D + (task % CPR) * 8;
+      const int64_t dst = pool_row(page[i], p.hkv, w.g, shift, (ri.seq - 1) & pmask, D) + (task % CPR) * 8;
       *reinterpret_cast<u32x4*>(static_cast<T*>(f.k_pool_w) + dst) = kd[i];
       *reinterpret_cast<u32x4*>(static_cast<T*>(f.v_pool_w) + dst) = vd[i];
     }
@@ -787,13 +789,11 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
   if constexpr (TAILS1) {
     __syncthreads();  // every wave is done with the ring; the slot table is visible
     if (n_tail > 0 && wave_active) {
-      constexpr int KW = 16;                                       // keys per sub-tile
-      constexpr int SUB = KW * D;                                  // elements of K (or V)
-      constexpr int NIW = SUB * (int)sizeof(T) / 1024;             // 1 KB loads each
-      constexpr int REGION = (int)(sizeof(lds_kv) / sizeof(T)) / 4;  // elements per wave
-      constexpr int NBUF = REGION >= 4 * SUB ? 2 : 1;
-      static_assert(REGION >= 2 * SUB && NIW >= 1, "sub-tile must fit a wave's share of the ring");
-      T* region = &lds_kv[0][0][0] + wave * REGION;
+      constexpr int KW = TG::KW;                                   // keys per sub-tile
+      constexpr int NIW = TG::NIW;                                 // 1 KB loads each (K, and V)
+      constexpr int NBUF = TG::NBUF;
+      static_assert(TG::REGION >= 2 * TG::SUB && NIW >= 1 && TG::RING * (int)sizeof(T) == (int)sizeof(lds_kv),
+                    "sub-tile must fit a wave's share of the ring");
       const int r_last = row_end - 1;
       const int u_lo = (row0 / p.group - kb_first) * n_tail;
       const int u_hi = (r_last / p.group - kb_first + 1) * n_tail;
@@ -807,12 +807,10 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
       // a finite row for sub-tile rows that carry no key (padding, invalid slots)
       const int64_t pad_row = ((int64_t)w.b * p.W + kb_first) * f.new_stride + (int64_t)w.g * D;
       auto issue_sub = [&](int sidx, int buf) {
-        T* dk = region + buf * 2 * SUB;
 #pragma unroll
         for (int i = 0; i < NIW; ++i) {
-          const int chunk = i * 64 + lane;
-          const int r = chunk / CPR;
-          const int c = (chunk % CPR) ^ lds_swz<D>(r);
+          const int r = TG::sub_row(i, lane);
+          const int c = TG::sub_chunk(i, lane);
           const int u = u_lo + sidx * KW + r;
           const int32_t e = u < u_hi ? lds_tail[u] : -1;
           const T* ksrc;
@@ -826,8 +824,8 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
             ksrc = static_cast<const T*>(f.k_new) + o + c * 8;
             vsrc = static_cast<const T*>(f.v_new) + o + c * 8;
           }
-          lds_dma16(ksrc, dk + i * (1024 / (int)sizeof(T)));
-          lds_dma16(vsrc, dk + SUB + i * (1024 / (int)sizeof(T)));
+          lds_dma16(ksrc, &lds_ring[TG::region_dst(wave, buf, 0, i)]);
+          lds_dma16(vsrc, &lds_ring[TG::region_dst(wave, buf, 1, i)]);
         }
       };
       issue_sub(0, 0);
@@ -836,8 +834,8 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
         const int buf = NBUF == 2 ? (sidx & 1) : 0;
         if (NBUF == 2 && sidx + 1 < n_sub) wait_vmcnt<2 * NIW>();
         else wait_vmcnt<0>();
-        const T* lk = region + buf * 2 * SUB;
-        const T* lv = lk + SUB;
+        const T* lk = &lds_ring[TG::region_dst(wave, buf, 0, 0)];
+        const T* lv = &lds_ring[TG::region_dst(wave, buf, 1, 0)];
         const int u0 = u_lo + sidx * KW;
         // ---- S^T = K Q^T for the query blocks whose beams own keys here
         f32x4 sacc[MB];
@@ -852,7 +850,7 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
         }
 #pragma unroll
         for (int ds = 0; ds < NDS; ++ds) {
-          const V8 a = *reinterpret_cast<const V8*>(&lk[l16 * D + (((ds * 4 + l4) ^ lds_swz<D>(l16)) << 3)]);
+          const V8 a = *reinterpret_cast<const V8*>(&lk[TG::k_read(l16, ds * 4 + l4)]);
 #pragma unroll
           for (int qb = 0; qb < MB; ++qb)
             if (act[qb]) sacc[qb] = Mfma<T>::mma(a, qv[qb][ds], sacc[qb]);
@@ -895,12 +893,10 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
         }
         // ---- O^T += V^T P^T over the 16 keys (V^T operand by transpose reads)
         const int ra = 4 * l4 + (l16 >> 2);
-        const int swa = lds_swz<D>(ra);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const int col = db * 16 + 4 * (l16 & 3);
-          const int off = (((col >> 3) ^ swa) << 3) + (col & 7);
-          const u32x2 a = __builtin_bit_cast(u32x2, lds_read_tr(&lv[ra * D + off]));
+          const u32x2 a = __builtin_bit_cast(u32x2, lds_read_tr(&lv[TG::v_read(ra, col)]));
 #pragma unroll
           for (int qb = 0; qb < MB; ++qb)
             if (act[qb]) oacc[db][qb] = Mfma<T>::mma16(a, pb[qb], oacc[db][qb]);
