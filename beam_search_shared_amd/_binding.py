@@ -74,6 +74,7 @@ _SIGS = {
     "bsp_plan_workspace_bytes": (ctypes.c_size_t, [_P]),
     "bsp_plan_destroy": (None, [_P]),
     "bsp_plan": (_I32, [_P, _I32, _I32, _I32, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "bsp_plan_static": (_I32, [_P, _I32, _I32, _I32, _P, _P, _P, _P]),
     "bsp_plan_num_splits": (_I32, [_P]),
     "bsp_plan_split_keys": (_I32, [_P]),
     "bsp_plan_tail_len": (_I32, [_P]),
@@ -219,6 +220,16 @@ def bsp_plan(plan: Plan, B: int, W: int, q_len: int, prefix_len, seq_len, block_
     st = None if plan.host_only else _stream(stream)
     _check(load_library().bsp_plan(plan.handle, B, W, q_len, _ptr(pl), _ptr(sl), _ptr(bt),
                                    _ptr(workspace), nbytes, st))
+
+
+def bsp_plan_static(plan: Plan, B: int, W: int, q_len: int, prefix_len, seq_len, block_tables,
+                    stream=None) -> None:
+    pl = _host_i32(prefix_len)
+    sl = _host_i32(seq_len)
+    bt = _host_i32(block_tables)
+    plan._keep = [pl, sl, bt]
+    _check(load_library().bsp_plan_static(plan.handle, B, W, q_len, _ptr(pl), _ptr(sl), _ptr(bt),
+                                          _stream(stream)))
 
 
 def bsp_write_kv(plan: Plan, k_new, v_new, src_row_stride: int, slots, n: int, k_pool, v_pool,

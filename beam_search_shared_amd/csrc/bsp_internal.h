@@ -160,6 +160,8 @@ struct MergeParams {
   float* lse_out;
 };
 
+// Bytes of the library's static device scratch (bsp_plan_static).
+constexpr size_t kStaticWorkspaceBytes = size_t(32) << 20;
 // The calling thread's error message (bsp_last_error) and status.
 bsp_status_t set_error(bsp_status_t st, const char* fmt, ...);
 // Make the plan's next bsp_plan copy the whole workspace header again.
@@ -174,6 +176,7 @@ hipError_t launch_write_kv(const WriteKvParams& p, int dtype, hipStream_t s);
 // on the matrix cores, prefix_rows_per_tile() or fewer).
 hipError_t launch_prefix(const PrefixParams& p, int dtype, int head_dim, int rows_per_tile,
                          hipStream_t s);
+
 // Two plans' bsp_prefix_attn work in one launch; both take 64 query rows per
 // work item (bf16/f16 only).
 hipError_t launch_prefix_two(const PrefixParams& a, const PrefixParams& b, int dtype, int head_dim,

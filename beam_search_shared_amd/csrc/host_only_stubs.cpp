@@ -38,3 +38,8 @@ hipError_t launch_naive(const TailParams&, void*, float*, int, int, hipStream_t)
 
 }  // namespace bsp
 
+// The static scratch is GPU code: the host-only build has none.
+extern "C" bsp_status_t bsp_plan_static(bsp_plan_t, int32_t, int32_t, int32_t, const int32_t*,
+                                        const int32_t*, const int32_t*, hipStream_t) {
+  return bsp::set_error(BSP_ERR_UNSUPPORTED, "host-only build: no static scratch");
+}

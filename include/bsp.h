@@ -163,6 +163,25 @@ bsp_status_t bsp_plan(bsp_plan_t plan, int32_t B, int32_t W, int32_t q_len,
                       const int32_t* block_tables_h, void* workspace_d,
                       size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * bsp_plan without a caller workspace, for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that forbid
+ * allocation): the plan's tables go into a static scratch array the library
+ * holds on each device it runs on (32 MiB, kept until the process ends; its
+ * address is looked up once per device on the first call there). Arguments,
+ * checks and the non-blocking copy are those of bsp_plan; every later call of
+ * the plan (bsp_decode_step, bsp_prefix_attn, ...) uses that scratch. The call
+ * allocates nothing. A plan whose bsp_plan_workspace_bytes exceeds 32 MiB is
+ * rejected with BSP_ERR_WORKSPACE. All plans planned this way on one device
+ * share its array, which keeps the last call's contents (each call rewrites
+ * everything a step reads, error word and split counters included): calls,
+ * and the steps that read their plans, that overlap on one device race, so
+ * order them on one stream and use one such plan at a time per device.
+ */
+bsp_status_t bsp_plan_static(bsp_plan_t plan, int32_t B, int32_t W, int32_t q_len,
+                             const int32_t* prefix_len_h, const int32_t* seq_len_h,
+                             const int32_t* block_tables_h, hipStream_t stream);
+
 /* Number of partial states bsp_prefix_attn writes for the current plan (1 when
  * kv_split is 0), the keys per split (0: one pass; the chosen chunk when
  * kv_split is -1), and the tail length each beam is padded to. -1 if
