@@ -586,11 +586,18 @@ bsp_status_t bsp_plan(bsp_plan_t pl, int32_t B, int32_t W, int32_t q_len,
                   sizeof(int32_t) * (size_t)B * d.num_kv_heads * fused_qt);
   }
 
+  // One-row cached-prefix decode (bsp_cached_decode): an arrival counter per
+  // (request, KV head), zero at every launch (the last chunk resets it).
+  const bool cached_decode = cached && q_len == 1 && W == 1;
+  if (cached_decode)
+    std::memset(st + pl->split_count_off, 0, sizeof(int32_t) * (size_t)B * d.num_kv_heads);
+
   if (!pl->host_only) {
     size_t end = pages_offset(B) + sizeof(int32_t) * pages.size();
     if (!fitems.empty()) end = pl->fitems_off + sizeof(bsp::FusedItem) * fitems.size();
     if (n_slots > 0)
       end = pl->split_count_off + sizeof(int32_t) * (size_t)B * d.num_kv_heads * fused_qt;
+    if (cached_decode) end = pl->split_count_off + sizeof(int32_t) * (size_t)B * d.num_kv_heads;
     const size_t begin = workspace_d == pl->zeroed_ws ? req_offset() : 0;
     hipError_t e = hipMemcpyAsync(static_cast<char*>(workspace_d) + begin, st + begin,
                                   end - begin, hipMemcpyHostToDevice, stream);
@@ -833,6 +840,50 @@ bsp_status_t bsp_prefix_attn(bsp_plan_t pl, const void* q, const void* k_pool, c
   const bsp_layer_desc_t& d = pl->desc;
   return after_launch(pl, bsp::launch_prefix(p, d.dtype, d.head_dim, pl->prefix_rpt, stream),
                       "prefix launch", stream);
+}
+
+bsp_status_t bsp_cached_decode(bsp_plan_t pl, const void* q, const void* k_new, const void* v_new,
+                               int64_t new_row_stride, const int32_t* slots_d, void* k_pool,
+                               void* v_pool, float* o_part, float* lse_part, void* o_out,
+                               float* lse_out, hipStream_t stream) {
+  bsp::PrefixParams p{};
+  bsp_status_t st = prefix_params(pl, q, k_pool, v_pool, o_part, lse_part, p);
+  if (st != BSP_OK) return st;
+  const bsp_layer_desc_t& d = pl->desc;
+  if (d.key_bucket <= 0 || pl->q_len != 1 || pl->W != 1)
+    return fail(BSP_ERR_UNSUPPORTED,
+                "bsp_cached_decode needs a cached-prefix plan with q_len 1 and one beam");
+  if (d.dtype == BSP_F32)
+    return fail(BSP_ERR_UNSUPPORTED, "bsp_cached_decode runs bf16/f16; use the separate calls for f32");
+  if (pl->prefix_rpt != 64 || pl->rows_per_req > 64 ||
+      !bsp::cached_decode_supported(d.num_q_heads / d.num_kv_heads, d.head_dim))
+    return fail(BSP_ERR_UNSUPPORTED,
+                "bsp_cached_decode takes at most 64 query rows per KV head and query heads per "
+                "KV head x head_dim / 4 at most 256");
+  if ((int64_t)pl->n_split * pl->rows_total * d.num_q_heads * d.head_dim * 4 > (int64_t)UINT32_MAX)
+    return fail(BSP_ERR_UNSUPPORTED,
+                "bsp_cached_decode addresses its partial states with 32-bit offsets: %d chunks x "
+                "%d rows x %d heads x %d floats is too many",
+                pl->n_split, pl->rows_total, d.num_q_heads, d.head_dim);
+  if (!k_new || !v_new || !slots_d || !o_out) return fail(BSP_ERR_ARG, "null pointer");
+  if (new_row_stride < (int64_t)d.num_kv_heads * d.head_dim || new_row_stride % 8 != 0)
+    return fail(BSP_ERR_ARG, "new_row_stride %lld must be >= %d and a multiple of 8",
+                (long long)new_row_stride, d.num_kv_heads * d.head_dim);
+  if (!aligned16(k_new) || !aligned16(v_new) || (reinterpret_cast<uintptr_t>(o_out) & 7u) != 0)
+    return fail(BSP_ERR_ARG, "k_new and v_new must be 16-byte aligned, o_out 8-byte");
+  bsp::FusedParams f{};
+  f.k_new = k_new;
+  f.v_new = v_new;
+  f.new_stride = new_row_stride;
+  f.k_pool_w = k_pool;
+  f.v_pool_w = v_pool;
+  f.o_out = o_out;
+  f.lse_out = lse_out;
+  f.split_count = reinterpret_cast<int32_t*>(static_cast<char*>(pl->ws_d) + pl->split_count_off);
+  f.new_slots = slots_d;
+  f.fuse_decode = 1;
+  return after_launch(pl, bsp::launch_cached_decode(p, f, d.dtype, d.head_dim, stream),
+                      "cached decode launch", stream);
 }
 
 bsp_status_t bsp_prefix_attn_two(bsp_plan_t a, bsp_plan_t b, const void* q, const void* k_pool,

@@ -132,6 +132,12 @@ struct FusedParams {
   int32_t* split_count;
   float* split_part;
   int32_t part_floats;
+  // one-launch cached-prefix decode (bsp_cached_decode, MODE 0 with q_len 1):
+  // the chunks' partial states are counted on split_count per (request, KV
+  // head), and the last chunk to arrive merges them with the new row
+  // (k_new/v_new) into o_out/lse_out and writes the new row at new_slots[b]
+  const int32_t* new_slots;
+  int32_t fuse_decode;
 };
 
 struct TailParams {
@@ -176,7 +182,14 @@ hipError_t launch_write_kv(const WriteKvParams& p, int dtype, hipStream_t s);
 // on the matrix cores, prefix_rows_per_tile() or fewer).
 hipError_t launch_prefix(const PrefixParams& p, int dtype, int head_dim, int rows_per_tile,
                          hipStream_t s);
-
+// The cache chunks of a one-row cached-prefix decode and, in the last chunk of
+// each (request, KV head) to finish, the merge with the new row (bf16/f16,
+// one 64-row query tile per item).
+hipError_t launch_cached_decode(const PrefixParams& p, const FusedParams& f, int dtype,
+                                int head_dim, hipStream_t s);
+// Whether the one-launch decode's merge takes this shape (query heads per KV
+// head x head_dim / 4 at most 256).
+bool cached_decode_supported(int group, int head_dim);
 // Two plans' bsp_prefix_attn work in one launch; both take 64 query rows per
 // work item (bf16/f16 only).
 hipError_t launch_prefix_two(const PrefixParams& a, const PrefixParams& b, int dtype, int head_dim,

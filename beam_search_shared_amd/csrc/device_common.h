@@ -32,6 +32,17 @@ template <> struct Traits<__bf16> {
   static __device__ __forceinline__ __bf16 from_f(float x) { return (__bf16)x; }
 };
 
+// Buffer resource over [base, base + bytes) for raw (stride 0) dword buffer
+// operations: an access past the end reads 0 and writes nothing. Word 3 selects
+// the 32-bit data format that untyped buffer loads and stores use on CDNA.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+// Cache-policy operand of a buffer load or store that is coherent across the
+// whole device (the sc1 bit: the access is made at the device's coherence
+// point, so data written by a workgroup on another XCD is seen).
+constexpr int kCoherentAgent = 16;
+
 // 2^x on the transcendental unit (v_exp_f32); exp2(-inf) = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

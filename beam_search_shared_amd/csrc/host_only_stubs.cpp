@@ -11,6 +11,10 @@ hipError_t launch_write_kv(const WriteKvParams&, int, hipStream_t) { return hipE
 hipError_t launch_prefix(const PrefixParams&, int, int, int, hipStream_t) {
   return hipErrorNotSupported;
 }
+hipError_t launch_cached_decode(const PrefixParams&, const FusedParams&, int, int, hipStream_t) {
+  return hipErrorNotSupported;
+}
+bool cached_decode_supported(int, int) { return false; }
 hipError_t launch_prefix_two(const PrefixParams&, const PrefixParams&, int, int, hipStream_t) {
   return hipErrorNotSupported;
 }

@@ -166,6 +166,8 @@ __device__ __forceinline__ int32_t resolve_fused_slot(const PrefixParams& p, con
 // causally, the chunk's rows up to its own; work items (request, query tile)
 // come from the plan's list and key tiles past a tile's last visible key are
 // never loaded; the output is written in the storage dtype.
+// MODE 5: MODE 0 for a one-row cached-prefix decode, with the chunks' partial
+// states merged with this call's row by the last chunk to finish (one launch).
 // MODE 4: a mixed step in one launch: each workgroup is either a MODE 1 item
 // of the beam step or a MODE 3 item of the context requests (`pre`), with
 // that part's parameters.
@@ -1012,6 +1014,10 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
   }
 
   // ---- epilogue: normalise and write the partial state (or the final output)
+  [[maybe_unused]] const __amdgpu_buffer_rsrc_t o_rsrc =
+      raw_rsrc(p.o_part, (uint32_t)((int64_t)p.n_split * p.rows_total * p.hq * D * 4));
+  [[maybe_unused]] const __amdgpu_buffer_rsrc_t l_rsrc =
+      raw_rsrc(p.lse_part, (uint32_t)((int64_t)p.n_split * p.rows_total * p.hq * 4));
 #pragma unroll
   for (int qb = 0; qb < MB; ++qb) {
     const float lt = sum4x16(lrow[qb]);
@@ -1034,6 +1040,18 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
         *reinterpret_cast<u32x2*>(op + db * 16) = __builtin_bit_cast(u32x2, e4);
       }
       if (l4 == 0 && f.lse_out != nullptr) f.lse_out[ohead] = lse;
+    } else if constexpr (MODE == 5) {
+      // read back by the last chunk to finish, maybe on another XCD: agent-coherent
+      // (sc1) stores, 16 bytes each; offsets fit 32 bits (checked by the host)
+      const int64_t ohead = ((int64_t)w.split * p.rows_total + grow) * p.hq + w.g * p.group + hh;
+      const uint32_t ob = (uint32_t)((ohead * D + l4 * 4) * 4);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(u32x4, oacc[db][qb] * inv), o_rsrc, ob + db * 64, 0, kCoherentAgent);
+      if (l4 == 0)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lse), l_rsrc,
+                                              (uint32_t)(ohead * 4), 0, kCoherentAgent);
     } else {
       const int64_t ohead = ((int64_t)w.split * p.rows_total + grow) * p.hq + w.g * p.group + hh;
       float* op = p.o_part + ohead * D + l4 * 4;
@@ -1041,6 +1059,152 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
       for (int db = 0; db < NDB; ++db)
         *reinterpret_cast<f32x4*>(op + db * 16) = oacc[db][qb] * inv;
       if (l4 == 0) p.lse_part[ohead] = lse;
+    }
+  }
+
+  // ---- MODE 5, the one-launch cached-prefix decode: each cache chunk counts
+  // its arrival per (request, KV head) once its partial state is stored; the
+  // last to arrive merges all chunks' states, in chunk order, with this call's
+  // row (its own key, read from k_new/v_new) into the output, and writes the
+  // new row into its page. No workgroup waits for another.
+  if constexpr (MODE == 5) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // every thread's partial-state stores are complete; the ring is idle
+    if (tid == 0) {
+      int32_t* ctr = f.split_count + (int64_t)w.b * p.hkv + w.g;
+      const int arrived = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int last = arrived == p.n_split - 1 ? 1 : 0;
+      if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      lds_pages[0] = last;
+    }
+    __syncthreads();
+    if (lds_pages[0] == 0) return;
+    // The chunks' states were stored with agent-coherent stores, complete before
+    // their counts; they are read back with agent-coherent (sc1) loads.
+    //
+    // Thread (slice, row, chunk of 4 columns) loads the lse and the 4 output
+    // columns of its slice's chunks (every ns-th one), all in one round trip,
+    // and folds them with its own running maximum; the ns slices are then
+    // joined, with this call's new row, through LDS. A row's CH chunks are CH
+    // adjacent lanes of one wave (CH divides 64), so the new row's score is a
+    // lane reduction.
+    constexpr int CH = D / 4;                 // 4-column chunks of a row
+    const int np = p.group * CH;              // (row, chunk) pairs; the host checked np <= 256
+    const int ns = 256 / np;                  // slices of threads
+    const int pair = tid % np, slice = tid / np;
+    const bool act = slice < ns;
+    const int row = pair / CH, ch = pair % CH;
+    const int h = w.g * p.group + row;
+    const int64_t hs = (int64_t)p.rows_total * p.hq;  // entries of one chunk's lse
+    const int64_t lrow = (int64_t)w.b * p.hq + h;
+    const int64_t nrow = (int64_t)w.b * f.new_stride + (int64_t)w.g * D + ch * 4;
+    const u32x2 q2 = *reinterpret_cast<const u32x2*>(static_cast<const T*>(p.q) + lrow * D + ch * 4);
+    const u32x2 k2 = *reinterpret_cast<const u32x2*>(static_cast<const T*>(f.k_new) + nrow);
+    const u32x2 v2 = *reinterpret_cast<const u32x2*>(static_cast<const T*>(f.v_new) + nrow);
+    constexpr int NB = 32;  // chunks in flight per thread
+    const uint32_t ob = (uint32_t)((lrow * D + ch * 4) * 4), lb = (uint32_t)(lrow * 4);
+    const uint32_t ostep = (uint32_t)(hs * D * 4), lstep = (uint32_t)(hs * 4);
+    f32x4 o[NB];
+    float lv[NB];
+    auto load_batch = [&](int sp0) {
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const uint32_t sp = (uint32_t)(sp0 + k * ns);
+        const bool in = act && (int)sp < p.n_split;
+        lv[k] = in ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                   l_rsrc, lb + sp * lstep, 0, kCoherentAgent))
+                   : -INFINITY;
+        o[k] = in ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  o_rsrc, ob + sp * ostep, 0, kCoherentAgent))
+                  : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    };
+    // running state of this thread's chunks: max m_s, weight sum den_s, weighted sum acc
+    float m_s = -INFINITY, den_s = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    auto add_batch = [&]() {
+      float bm = lv[0];
+#pragma unroll
+      for (int k = 1; k < NB; ++k) bm = fmaxf(bm, lv[k]);
+      const float mn = fmaxf(m_s, bm);
+      if (mn == -INFINITY) return;  // only empty chunks so far
+      const float sc = fast_exp2((m_s - mn) * kLog2e);  // m_s = -inf: 0, and acc is 0
+      acc *= sc;
+      den_s *= sc;
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const float wt = fast_exp2((lv[k] - mn) * kLog2e);  // empty or absent chunk: 0
+        if (wt > 0.f) {
+          den_s += wt;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e] = fmaf(wt, o[k][e], acc[e]);
+        }
+      }
+      m_s = mn;
+    };
+    load_batch(slice);
+    float s_new;  // the new row's score, natural-log units like the chunks' lse
+    {
+      const T* qe = reinterpret_cast<const T*>(&q2);
+      const T* ke = reinterpret_cast<const T*>(&k2);
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dot = fmaf(Traits<T>::to_f(qe[e]), Traits<T>::to_f(ke[e]), dot);
+      dot = row16_sum(dot);
+      if constexpr (CH >= 32) dot += xor16(dot);
+      if constexpr (CH == 64) dot += xor32(dot);
+      s_new = dot * p.scale;
+    }
+    add_batch();
+    for (int sp0 = slice + NB * ns; sp0 < p.n_split; sp0 += NB * ns) {
+      load_batch(sp0);
+      add_batch();
+    }
+    // LDS (the idle ring): the states of slices 1..ns-1
+    f32x4* sh_acc = reinterpret_cast<f32x4*>(lds_ring);
+    float2* sh_md = reinterpret_cast<float2*>(sh_acc + 256);
+    if (act && slice > 0) {
+      sh_acc[(slice - 1) * np + pair] = acc;
+      sh_md[(slice - 1) * np + pair] = float2{m_s, den_s};
+    }
+    __syncthreads();
+    if (act && slice == 0) {
+      float M = fmaxf(s_new, m_s);
+      for (int sl = 1; sl < ns; ++sl) M = fmaxf(M, sh_md[(sl - 1) * np + pair].x);
+      float c = fast_exp2((m_s - M) * kLog2e);
+      acc *= c;
+      float den = den_s * c;
+      for (int sl = 1; sl < ns; ++sl) {
+        const float2 md = sh_md[(sl - 1) * np + pair];
+        c = fast_exp2((md.x - M) * kLog2e);
+        acc += sh_acc[(sl - 1) * np + pair] * c;
+        den = fmaf(md.y, c, den);
+      }
+      const float w_new = fast_exp2((s_new - M) * kLog2e);
+      den += w_new;
+      const T* ve = reinterpret_cast<const T*>(&v2);
+      const float inv = 1.f / den;
+      T e4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) e4[e] = Traits<T>::from_f(fmaf(w_new, Traits<T>::to_f(ve[e]), acc[e]) * inv);
+      *reinterpret_cast<u32x2*>(static_cast<T*>(f.o_out) + lrow * D + ch * 4) = __builtin_bit_cast(u32x2, e4);
+      if (ch == 0 && f.lse_out != nullptr) f.lse_out[lrow] = M + __logf(den);
+    }
+    // this call's row into its page (KV head g's slice)
+    if (tid < CPR) {
+      const int32_t slot = f.new_slots[w.b];
+      if (slot < 0 || (int64_t)slot >= ((int64_t)p.num_pages << shift)) {
+        if (tid == 0)
+          record_fault(&p.hdr->error_bits, &p.hdr->fault_count, &p.hdr->first_value,
+                       kErrWriteSlot, slot);
+      } else {
+        const int64_t src = (int64_t)w.b * f.new_stride + (int64_t)w.g * D + tid * 8;
+        const int64_t dst = pool_row(slot >> shift, p.hkv, w.g, shift, slot & pmask, D) + tid * 8;
+        *reinterpret_cast<u32x4*>(static_cast<T*>(f.k_pool_w) + dst) =
+            *reinterpret_cast<const u32x4*>(static_cast<const T*>(f.k_new) + src);
+        *reinterpret_cast<u32x4*>(static_cast<T*>(f.v_pool_w) + dst) =
+            *reinterpret_cast<const u32x4*>(static_cast<const T*>(f.v_new) + src);
+      }
     }
   }
 
@@ -1248,6 +1412,31 @@ hipError_t launch_prefix(const PrefixParams& p, int dtype, int head_dim, int row
     if (dtype == BSP_F16) launch_mfma<_Float16, 0>(p, none, head_dim, mb, blocks, s);
     else launch_mfma<__bf16, 0>(p, none, head_dim, mb, blocks, s);
   }
+  return hipGetLastError();
+}
+
+bool cached_decode_supported(int group, int head_dim) {
+  // the merge's (row, chunk of 4 columns) pairs fit the 256 threads
+  return group * head_dim / 4 <= 256;
+}
+
+hipError_t launch_cached_decode(const PrefixParams& p, const FusedParams& f, int dtype,
+                                int head_dim, hipStream_t s) {
+  const unsigned blocks = (unsigned)(p.B * p.hkv * p.n_split * p.n_qtiles);
+  if (blocks == 0) return hipSuccess;
+  if (dtype != BSP_F16 && dtype != BSP_BF16) return hipErrorInvalidValue;
+  if (!cached_decode_supported(p.group, head_dim)) return hipErrorInvalidValue;
+#define BSP_CD(TT, DD, KTT, NS) prefix_mfma_kernel<TT, DD, 1, KTT, NS, 5><<<blocks, 256, 0, s>>>(p, f)
+  if (dtype == BSP_F16) {
+    if (head_dim == 64) BSP_CD(_Float16, 64, 64, 4);
+    else if (head_dim == 128) BSP_CD(_Float16, 128, 64, 2);
+    else BSP_CD(_Float16, 256, 32, 2);
+  } else {
+    if (head_dim == 64) BSP_CD(__bf16, 64, 64, 4);
+    else if (head_dim == 128) BSP_CD(__bf16, 128, 64, 2);
+    else BSP_CD(__bf16, 256, 32, 2);
+  }
+#undef BSP_CD
   return hipGetLastError();
 }
 

@@ -16,6 +16,8 @@ and a cached-prefix call (beam 1) is
     bsp_prefix_attn  this call's rows, causal
     bsp_merge        n-way merge of all the partial states
 
+or, for a one-row decode, all four in one launch (``bsp_cached_decode``);
+
 and a mixed step (context requests beside generation requests) is
 
     bsp_write_kv     the context chunks' rows -> their requests' pages
@@ -271,6 +273,16 @@ def run_cached_prefix(c: CachedPrefixDevice, stream=None, two_launches: bool = F
     rows = c.q_len
     B.bsp_merge(rows, c.num_q_heads, D, ns + 1, c.o_part, c.lse_part, rows * c.num_q_heads * D,
                 rows * c.num_q_heads, c.out, c.dtype, c.lse_out, stream)
+
+
+def run_cached_decode(c: CachedPrefixDevice, stream=None) -> None:
+    """A one-row cached-prefix decode call in one launch (bsp_cached_decode): the
+    cache chunks, the merge with this call's row and the row's write into its
+    page."""
+    ns = c.n_split
+    B.bsp_cached_decode(c.plan_cache, c.q, c.new_k, c.new_v, c.num_kv_heads * c.head_dim, c.slots,
+                        c.k_pool, c.v_pool, c.o_part[:ns], c.lse_part[:ns], c.out, c.lse_out,
+                        stream)
 
 
 @dataclass

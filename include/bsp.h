@@ -238,6 +238,37 @@ bsp_status_t bsp_prefix_attn_two(bsp_plan_t a, bsp_plan_t b, const void* q, cons
                                  float* o_part_b, float* lse_part_b, hipStream_t stream);
 
 /*
+ * A whole one-row cached-prefix decode call in one launch (PR #2202,
+ * Background and Implementation: a decode step attends the valid cached rows,
+ * bounded to the bucket, plus its own row; TensorRT-LLM PR #21738, review
+ * thread on the FA4 split-generation kernels: split the keys, then merge the
+ * splits). The plan (key_bucket > 0, W = 1, q_len = 1, at most 64 query rows
+ * per KV head, bf16/f16) splits the valid cached rows into chunks
+ * (bsp_plan_num_splits); each chunk's workgroup writes its partial state to
+ * o_part/lse_part (as bsp_prefix_attn) and counts itself on a counter in the
+ * workspace; the last chunk of each (request, KV head) to finish merges all
+ * chunks, in chunk order, with this call's row -- its key and value read from
+ * k_new/v_new, visible to the row itself -- into o_out (dtype [B][Hq][D]) and
+ * lse_out (float [B][Hq], may be null), and writes the new row into the pools
+ * at slots_d[b] (device int32 [B], page * page_size + row; a slot outside the
+ * pool is skipped and recorded for bsp_check). No workgroup waits for another.
+ *   q             [B, 1, 1, Hq, D]
+ *   k_new, v_new  request b's new row at element b * new_row_stride, [Hkv][D]
+ *   o_part        float [n_split][B][Hq][D]; lse_part float [n_split][B][Hq]
+ * The same result as bsp_write_kv + bsp_prefix_attn (cache) + bsp_prefix_attn
+ * (the new row) + bsp_merge, up to fp32 summation order. The counters live in
+ * the plan's workspace and each last chunk resets its own, so launches of one
+ * plan must be ordered (one stream); overlapping launches of one plan race.
+ * Errors as for bsp_prefix_attn, and BSP_ERR_UNSUPPORTED for other plans, for
+ * (Hq / Hkv) * D / 4 > 256, and for partial states of more than 4 GiB
+ * (n_split * B * Hq * D * 4 bytes: the merge addresses them with 32-bit offsets).
+ */
+bsp_status_t bsp_cached_decode(bsp_plan_t plan, const void* q, const void* k_new, const void* v_new,
+                               int64_t new_row_stride, const int32_t* slots_d, void* k_pool,
+                               void* v_pool, float* o_part, float* lse_part, void* o_out,
+                               float* lse_out, hipStream_t stream);
+
+/*
  * Tail attention: each beam's G query rows against its own tail positions
  * P_b <= j < S_b, gathered through cache_indirection: position j of beam k is
  * read from beam src = cache_indirection[b][k][j], page

@@ -347,6 +347,81 @@ def test_cached_prefix_decode_random_lengths(L):
         assert_close(c.o_part[sp], c.lse_part[sp], po, pl, "f16", f"decode L={L} split {sp}")
 
 
+@pytest.mark.parametrize("L", CACHED_L + RANDOM_L[:8])
+def test_cached_decode_one_launch(L):
+    """The one-row decode in one launch (bsp_cached_decode) against the oracle at
+    the edge and random valid lengths of the 10368-row allocation, twice in a
+    row (the last chunk resets each counter for the next launch): the output
+    within tolerance, the new row written at its slot bit for bit, and the
+    result equal to that of the four-launch call."""
+    R = oracle.bucket_rows(L, 256, 10368)
+    inp = synth.make_cached_prefix(L % 5, valid_rows=L, q_len=1, nan_from_row=R)
+    c = S.upload_cached_prefix(inp, DEV)
+    S.plan_cached_prefix(c)
+    say(f"one-launch cached decode L={L}: {c.n_split} chunks of {c.plan_cache.split_keys} keys")
+    o, lse = oracle.cached_prefix_attention(inp, causal=True)
+    outs = []
+    for rep in range(2):
+        S.run_cached_decode(c)
+        B.bsp_check(c.plan_cache)
+        torch.cuda.synchronize()
+        assert_close(c.out.reshape(1, 24, 128), c.lse_out.reshape(1, 24), o, lse, "f16",
+                     f"one-launch decode L={L} launch {rep}")
+        outs.append((c.out.clone(), c.lse_out.clone()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    page, row = divmod(int(c.slots[0]), c.page_size)
+    assert torch.equal(c.k_pool[page, :, row].cpu(), S.to_device(inp.new_k[0], "f16", "cpu"))
+    assert torch.equal(c.v_pool[page, :, row].cpu(), S.to_device(inp.new_v[0], "f16", "cpu"))
+    S.run_cached_prefix(c)  # the four-launch call
+    B.bsp_check(c.plan_cache)
+    B.bsp_check(c.plan_new)
+    torch.cuda.synchronize()
+    assert (c.out.float() - outs[0][0].float()).abs().max().item() <= 2e-3
+    assert (c.lse_out - outs[0][1]).abs().max().item() <= 1e-5
+
+
+@pytest.mark.parametrize("L,split", [(10368, 64), (5000, 64), (777, 64), (10368, 128)])
+def test_cached_decode_one_launch_many_chunks(L, split):
+    """Forced small chunks, so each merging thread folds its chunks over several
+    batches of loads (more than 32 chunks per slice of threads): against the
+    oracle and the four-launch call."""
+    R = oracle.bucket_rows(L, 256, 10368)
+    inp = synth.make_cached_prefix(11 + L % 7, valid_rows=L, q_len=1, nan_from_row=R)
+    c = S.upload_cached_prefix(inp, DEV, kv_split=split)
+    S.plan_cached_prefix(c)
+    say(f"one-launch cached decode L={L}: {c.n_split} chunks of {c.plan_cache.split_keys} keys")
+    if L >= 5000:
+        assert c.n_split > 64  # more than 32 chunks per slice at 2 slices
+    o, lse = oracle.cached_prefix_attention(inp, causal=True)
+    S.run_cached_decode(c)
+    B.bsp_check(c.plan_cache)
+    torch.cuda.synchronize()
+    assert_close(c.out.reshape(1, 24, 128), c.lse_out.reshape(1, 24), o, lse, "f16",
+                 f"one-launch decode L={L} split {split}")
+    one = (c.out.clone(), c.lse_out.clone())
+    S.run_cached_prefix(c)
+    B.bsp_check(c.plan_cache)
+    B.bsp_check(c.plan_new)
+    torch.cuda.synchronize()
+    assert (c.out.float() - one[0].float()).abs().max().item() <= 2e-3
+    assert (c.lse_out - one[1]).abs().max().item() <= 1e-5
+
+
+def test_cached_decode_one_launch_rejects_other_plans():
+    inp = synth.make_cached_prefix(3, valid_rows=300, q_len=4)
+    c = S.upload_cached_prefix(inp, DEV)
+    S.plan_cached_prefix(c)
+    with pytest.raises(B.BspError) as ei:
+        S.run_cached_decode(c)
+    assert ei.value.name == "BSP_ERR_UNSUPPORTED"
+    beam = S.upload_beam_step(synth.make_beam_step("qwen3_0p6b", 1, batch=2), DEV)
+    S.plan_beam_step(beam)
+    with pytest.raises(B.BspError) as ei:
+        B.bsp_cached_decode(beam.plan, beam.q, beam.k_new, beam.v_new, 1024, beam.slots,
+                            beam.k_pool, beam.v_pool, beam.o_part[0], beam.lse_part[0], beam.out)
+    assert ei.value.name == "BSP_ERR_UNSUPPORTED"
+
+
 @pytest.mark.parametrize("draw", range(16))
 def test_cached_prefix_prefill_random_lengths(draw):
     """A prefill at the full 10368-row allocation with the valid length drawn from
