@@ -94,6 +94,7 @@ _SIGS = {
     "bsp_debug_plan_tables": (_I32, [_P, _P, _P, _P, _P, _P]),
     "bsp_debug_plan_items": (_I32, [_P, _P, _P]),
     "bsp_debug_tail_slots": (_I32, [_P, _P, _P, _P, _P]),
+    "bsp_debug_fused_slots": (_I32, [_P, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P]),
 }
 
 
@@ -353,3 +354,12 @@ def bsp_debug_tail_slots(plan: Plan, block_tables, cache_indirection, slots_out,
     _check(load_library().bsp_debug_tail_slots(plan.handle, _ptr(block_tables),
                                                _ptr(cache_indirection), _ptr(slots_out),
                                                _stream(stream)))
+
+
+def bsp_debug_fused_slots(plan: Plan, q, k_new, v_new, new_row_stride: int, k_pool, v_pool,
+                          block_tables, cache_indirection, o_out, slots_out,
+                          stream=None) -> None:
+    _check(load_library().bsp_debug_fused_slots(plan.handle, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                                new_row_stride, _ptr(k_pool), _ptr(v_pool),
+                                                _ptr(block_tables), _ptr(cache_indirection),
+                                                _ptr(o_out), _ptr(slots_out), _stream(stream)))

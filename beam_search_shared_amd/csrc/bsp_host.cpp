@@ -881,7 +881,6 @@ bsp_status_t bsp_cached_decode(bsp_plan_t pl, const void* q, const void* k_new, 
   f.lse_out = lse_out;
   f.split_count = reinterpret_cast<int32_t*>(static_cast<char*>(pl->ws_d) + pl->split_count_off);
   f.new_slots = slots_d;
-  f.fuse_decode = 1;
   return after_launch(pl, bsp::launch_cached_decode(p, f, d.dtype, d.head_dim, stream),
                       "cached decode launch", stream);
 }
@@ -1054,6 +1053,30 @@ bsp_status_t bsp_decode_step(bsp_plan_t pl, const void* q, const void* k_new, co
                       bsp::launch_decode_step(p, f, d.dtype, d.head_dim, pl->rows_per_req,
                                               pl->n_fitems, pl->tail_pad, stream),
                       "decode step launch", stream);
+}
+
+bsp_status_t bsp_debug_fused_slots(bsp_plan_t pl, const void* q, const void* k_new,
+                                   const void* v_new, int64_t new_row_stride, void* k_pool,
+                                   void* v_pool, const int32_t* block_tables_d,
+                                   const int32_t* cache_indirection_d, void* o_out,
+                                   int32_t* slots_out_d, hipStream_t stream) {
+  bsp::PrefixParams p;
+  bsp::FusedParams f;
+  const bsp_status_t st = decode_params(pl, q, k_new, v_new, new_row_stride, k_pool, v_pool,
+                                        block_tables_d, cache_indirection_d, o_out, nullptr, p, f);
+  if (st != BSP_OK) return st;
+  if (slots_out_d == nullptr) return fail(BSP_ERR_ARG, "null slots_out");
+  const bsp_layer_desc_t& d = pl->desc;
+  if (!bsp::decode_uses_slot_table(d.head_dim, pl->rows_per_req, pl->W,
+                                   d.num_q_heads / d.num_kv_heads, pl->tail_pad))
+    return fail(BSP_ERR_UNSUPPORTED,
+                "this plan's tails are gathered key by key, without the LDS slot table");
+  f.dump_slots = slots_out_d;
+  f.dump_pad = std::max(pl->tail_pad, 1);
+  return after_launch(pl,
+                      bsp::launch_decode_step(p, f, d.dtype, d.head_dim, pl->rows_per_req,
+                                              pl->n_fitems, pl->tail_pad, stream),
+                      "fused slot-table dump launch", stream);
 }
 
 bsp_status_t bsp_prefill_attn(bsp_plan_t pl, const void* q, const void* k_pool, const void* v_pool,

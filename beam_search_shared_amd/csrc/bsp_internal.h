@@ -132,12 +132,16 @@ struct FusedParams {
   int32_t* split_count;
   float* split_part;
   int32_t part_floats;
-  // one-launch cached-prefix decode (bsp_cached_decode, MODE 0 with q_len 1):
-  // the chunks' partial states are counted on split_count per (request, KV
-  // head), and the last chunk to arrive merges them with the new row
-  // (k_new/v_new) into o_out/lse_out and writes the new row at new_slots[b]
+  // one-launch cached-prefix decode (bsp_cached_decode, MODE 5): the chunks'
+  // partial states are counted on split_count per (request, KV head), and the
+  // last chunk to arrive merges them with the new row (k_new/v_new) into
+  // o_out/lse_out and writes the new row at new_slots[b]
   const int32_t* new_slots;
-  int32_t fuse_decode;
+  // debug (bsp_debug_fused_slots): when set, the beam step (MODE 1) writes its
+  // LDS tail-slot table here, entry (b, g, beam, t) at
+  // ((b * Hkv + g) * W + beam) * dump_pad + t, and stops before the tails
+  int32_t* dump_slots;
+  int32_t dump_pad;
 };
 
 struct TailParams {
@@ -197,6 +201,9 @@ hipError_t launch_prefix_two(const PrefixParams& a, const PrefixParams& b, int d
 hipError_t launch_decode_step(const PrefixParams& p, const FusedParams& f, int dtype,
                               int head_dim, int rows_per_req, int n_items, int tail_pad,
                               hipStream_t s);
+// Whether bsp_decode_step resolves the tails through its LDS slot table (MODE 1)
+// for this shape, rather than key by key (MODE 2).
+bool decode_uses_slot_table(int head_dim, int rows_per_req, int W, int group, int tail_pad);
 // Query-row blocks of 16 per wave for an M-row item (4 waves per workgroup).
 // At head_dim 256 a 128-row tile needs more than half a SIMD's registers (one
 // workgroup per CU); 64-row tiles at two per CU, the tiles of a request on one

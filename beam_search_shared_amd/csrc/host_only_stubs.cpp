@@ -15,6 +15,7 @@ hipError_t launch_cached_decode(const PrefixParams&, const FusedParams&, int, in
   return hipErrorNotSupported;
 }
 bool cached_decode_supported(int, int) { return false; }
+bool decode_uses_slot_table(int, int, int, int, int) { return false; }
 hipError_t launch_prefix_two(const PrefixParams&, const PrefixParams&, int, int, hipStream_t) {
   return hipErrorNotSupported;
 }

@@ -790,6 +790,12 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
   // tail key is visible only to its own beam's query rows.
   if constexpr (TAILS1) {
     __syncthreads();  // every wave is done with the ring; the slot table is visible
+    if (f.dump_slots != nullptr) {  // debug: the table itself instead of the tails and output
+      for (int u = tid; u < n_sl; u += 256)
+        f.dump_slots[(((int64_t)w.b * p.hkv + w.g) * p.W + kb_first + u / ri.tail) * f.dump_pad +
+                     u % ri.tail] = lds_tail[u];
+      return;
+    }
     if (n_tail > 0 && wave_active) {
       constexpr int KW = TG::KW;                                   // keys per sub-tile
       constexpr int NIW = TG::NIW;                                 // 1 KB loads each (K, and V)
@@ -1525,15 +1531,19 @@ hipError_t launch_mixed_step(const PrefixParams& dp, const FusedParams& df, cons
   return hipGetLastError();
 }
 
+bool decode_uses_slot_table(int head_dim, int rows_per_req, int W, int group, int tail_pad) {
+  // beams with a row in one query tile, at most; their tail slots must fit the LDS table
+  const int nbt_max = min(W, (64 * pick_mb(head_dim, rows_per_req) - 1) / group + 2);
+  return (int64_t)nbt_max * tail_pad <= kTailSlots;
+}
+
 hipError_t launch_decode_step(const PrefixParams& p, const FusedParams& f, int dtype,
                               int head_dim, int rows_per_req, int n_items, int tail_pad,
                               hipStream_t s) {
   const unsigned blocks = (unsigned)(n_items * p.hkv * p.n_qtiles);
   if (blocks == 0) return hipSuccess;
   const int mb = pick_mb(head_dim, rows_per_req);
-  // beams with a row in one query tile, at most; their tail slots must fit the LDS table
-  const int nbt_max = min(p.W, (64 * mb - 1) / p.group + 2);
-  if ((int64_t)nbt_max * tail_pad <= kTailSlots) {
+  if (decode_uses_slot_table(head_dim, rows_per_req, p.W, p.group, tail_pad)) {
     if (dtype == BSP_F16) launch_mfma<_Float16, 1>(p, f, head_dim, mb, blocks, s);
     else launch_mfma<__bf16, 1>(p, f, head_dim, mb, blocks, s);
   } else {

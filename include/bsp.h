@@ -432,6 +432,26 @@ bsp_status_t bsp_debug_tail_slots(bsp_plan_t plan, const int32_t* block_tables_d
                                   const int32_t* cache_indirection_d, int32_t* slots_d,
                                   hipStream_t stream);
 
+/* Device: bsp_decode_step's own tail-slot table (TensorRT-LLM PR #21738,
+ * Solution: each beam's tail is gathered through cache_indirection), as the
+ * fused kernel builds it in LDS, written out instead of being used. The launch
+ * runs the step with the same arguments as bsp_decode_step up to the point
+ * where the table is complete (after the prompt, and after the merge of a
+ * split request), writes it and stops: no tails, no output, no token write
+ * (o_out is not written; the pools are only read). Entry (b, g, beam, t), for
+ * KV head g and tail position t < S_b - P_b, is written at int32
+ * slots_out_d[((b * Hkv + g) * W + beam) * max(tail_len, 1) + t] (tail_len =
+ * bsp_plan_tail_len); other entries are left as they were. An entry >= 0 is
+ * the pool row ((page * Hkv + g) * page_size + row); an entry <= -2 is the
+ * current token, read from the new-token row of beam (-entry - 2); -1 an
+ * invalid index (also recorded for bsp_check). BSP_ERR_UNSUPPORTED where the
+ * step gathers the tails key by key (tails too long for the LDS table). */
+bsp_status_t bsp_debug_fused_slots(bsp_plan_t plan, const void* q, const void* k_new,
+                                   const void* v_new, int64_t new_row_stride, void* k_pool,
+                                   void* v_pool, const int32_t* block_tables_d,
+                                   const int32_t* cache_indirection_d, void* o_out,
+                                   int32_t* slots_out_d, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -197,6 +197,106 @@ def test_tail_slots_bit_exact_1200_random_batches():
     assert n_full_last > 100 and n_one_row > 100
 
 
+def _fused_slots_gpu(s, pad):
+    out = torch.full((s.batch, s.num_kv_heads, s.beam, max(pad, 1)), -7, dtype=torch.int32,
+                     device=DEV)
+    B.bsp_debug_fused_slots(s.plan, s.q, s.k_new_beams, s.v_new_beams,
+                            s.num_kv_heads * s.head_dim, s.k_pool, s.v_pool, s.block_tables,
+                            s.cache_indirection, s.out, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _check_fused_slots(inp, got, pad):
+    """The fused kernel's table entry (b, g, beam, t) against oracle.tail_slots:
+    a pool row ((page * Hkv + g) * ps + row) whose page * ps + row is the
+    oracle's slot, and for the current token (t = S - P - 1) the beam whose
+    new-token row it reads, cache_indirection[b, beam, S - 1], the beam the
+    oracle's slot for that position is taken from."""
+    ps, hkv = inp.page_size, inp.num_kv_heads
+    shift = ps.bit_length() - 1
+    ref = oracle.tail_slots(inp.prefix_len, inp.seq_len, inp.block_tables,
+                            inp.cache_indirection, ps, pad)
+    for b in range(inp.batch):
+        P, S_ = int(inp.prefix_len[b]), int(inp.seq_len[b])
+        T = S_ - P
+        assert (got[b, :, :, T:] == -7).all(), b
+        if T == 0:  # no tail (and no current token past the prompt)
+            continue
+        e = got[b, :, :, :T - 1].astype(np.int64)
+        assert (e >= 0).all(), b
+        ph = e >> shift
+        assert (ph % hkv == np.arange(hkv)[:, None, None]).all(), b
+        assert ((ph // hkv) * ps + (e & (ps - 1)) == ref[b][None, :, :T - 1]).all(), b
+        src = -2 - got[b, :, :, T - 1].astype(np.int64)
+        assert (src == inp.cache_indirection[b, :, S_ - 1][None, :]).all(), b
+
+
+def test_fused_slot_table_bit_exact_random_batches(monkeypatch):
+    """bsp_decode_step's LDS tail-slot table, dumped by the kernel itself, bit for
+    bit against the oracle's index function over 600 random batches: page sizes
+    1..1024 at stride 1 or 2, prompts that fill their last page or end one row
+    into it, beams spread over two query tiles, and prompts split into chunks
+    (the table is then built by the last chunk to finish)."""
+    rng = np.random.default_rng(600)
+    n_split = n_tiles = n_full_last = 0
+    for trial in range(600):
+        ps = int(rng.choice([1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024]))
+        kind = trial % 5
+        beam = int(rng.integers(1, 7))
+        if kind == 0:
+            pr = (ps * int(rng.integers(1, 3)),) * 2
+        elif kind == 1:
+            pr = (ps * int(rng.integers(0, 3)) + 1,) * 2
+        elif kind == 2:    # more than 64 query rows: two query tiles
+            pr, beam = (1, 200), int(rng.integers(33, 60))
+        else:
+            pr = (1, int(rng.integers(2, 3 * ps + 3)))
+        split = kind == 4 and trial % 10 == 4
+        if split:
+            pr = (300, 900)
+            monkeypatch.setenv("BSP_SPLIT", "64")
+        else:
+            monkeypatch.delenv("BSP_SPLIT", raising=False)
+        cfg = BeamConfig("fslots", batch=int(rng.integers(1, 5)), beam=beam, num_q_heads=4,
+                         num_kv_heads=2, head_dim=64, dtype="bf16" if trial % 2 else "f16",
+                         page_size=ps, prefix_range=pr, tail_range=(0, int(rng.integers(1, 60))),
+                         shuffle_pages=bool(rng.integers(0, 2)))
+        inp = synth.make_beam_step(cfg, trial, page_stride=int(rng.integers(1, 3)), garbage="unit")
+        s = S.upload_beam_step(inp, DEV)
+        S.plan_beam_step(s)
+        items = B.bsp_debug_plan_items(s.plan)
+        n_split += int(split and (items[:, 3] > 1).any())
+        n_tiles += int(beam * 2 > 64)
+        n_full_last += int(((inp.prefix_len % ps) == 0).sum())
+        pad = s.plan.tail_len
+        got = _fused_slots_gpu(s, pad)
+        B.bsp_check(s.plan)
+        try:
+            _check_fused_slots(inp, got, pad)
+        except AssertionError:
+            say(f"mismatch trial={trial} ps={ps} W={beam} split={split} "
+                f"P={inp.prefix_len.tolist()} S={inp.seq_len.tolist()}")
+            raise
+    say(f"600 batches: {n_split} with split prompts, {n_tiles} with two query tiles, "
+        f"{n_full_last} prompts ending on a page boundary")
+    assert n_split >= 50 and n_tiles >= 100 and n_full_last >= 100
+
+
+def test_fused_slot_table_dump_leaves_outputs_and_pool():
+    """The dump launch writes only the table: the output and the pools are untouched."""
+    inp = synth.make_beam_step("qwen3_0p6b", 3, batch=3)
+    s = S.upload_beam_step(inp, DEV)
+    S.plan_beam_step(s)
+    s.out.fill_(7)
+    k0, v0 = s.k_pool.clone(), s.v_pool.clone()
+    got = _fused_slots_gpu(s, s.plan.tail_len)
+    B.bsp_check(s.plan)
+    _check_fused_slots(inp, got, s.plan.tail_len)
+    assert (s.out == 7).all()
+    assert torch.equal(s.k_pool, k0) and torch.equal(s.v_pool, v0)
+
+
 def test_bad_cache_indirection_is_skipped_and_reported():
     inp = synth.make_beam_step("qwen3_0p6b", 5, batch=2, tail_range=(3, 4))
     s = S.upload_beam_step(inp, DEV)
@@ -849,3 +949,44 @@ def test_decode_step_degenerate_shapes(name, cfg):
     inp = synth.make_beam_step(cfg, 21)
     say(f"fused {name} P={inp.prefix_len.tolist()} T={inp.tail_len.tolist()}")
     _run_fused_and_check(inp, name)
+
+
+def test_plan_returns_without_waiting_for_queued_work():
+    """Re-planning stages its tables in pinned host memory and copies them with
+    an asynchronous copy ordered on the stream: with about a second of work
+    queued ahead on the same stream, two bsp_plan calls (one per staging
+    buffer) return while that work still runs, and the step planned behind it
+    gives the same output as before."""
+    import time
+    beam = S.upload_beam_step(synth.make_beam_step("qwen3_0p6b", 5, batch=8), DEV)
+    S.plan_beam_step(beam)
+    S.run_decode_step(beam)
+    B.bsp_check(beam.plan)
+    torch.cuda.synchronize()
+    ref = beam.out.clone()
+    stream = torch.cuda.current_stream()
+    x = torch.randn(4096, 4096, device=DEV)
+    y = x @ x
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    y = x @ x
+    torch.cuda.synchronize()
+    one = time.perf_counter() - t0
+    n = max(20, min(2000, int(1.0 / max(one, 1e-5))))  # about a second of matrix products
+    for _ in range(n):
+        y = x @ y * 1e-3
+    queued_at = time.perf_counter()
+    plan_s = []
+    for _ in range(2):
+        t0 = time.perf_counter()
+        S.plan_beam_step(beam)
+        plan_s.append(time.perf_counter() - t0)
+    busy = not stream.query()
+    say(f"{n} products of {one * 1e3:.2f} ms queued; plan calls {[round(t * 1e3, 3) for t in plan_s]} ms; "
+        f"stream busy after them: {busy} ({(time.perf_counter() - queued_at) * 1e3:.1f} ms after queueing)")
+    assert busy, "the queued products finished before the plans returned: no evidence either way"
+    assert max(plan_s) < 0.1 * n * one
+    S.run_decode_step(beam)
+    B.bsp_check(beam.plan)
+    torch.cuda.synchronize()
+    assert torch.equal(beam.out, ref)
