@@ -101,6 +101,7 @@ def launch_percentiles(torch, fn, n, stream):
 
 
 KERNEL_SOURCES = ("beam_search_shared_amd/csrc/prefix_attn.hip",
+                  "beam_search_shared_amd/csrc/tile_index.h",
                   "beam_search_shared_amd/csrc/device_common.h",
                   "beam_search_shared_amd/csrc/bsp_internal.h")
 
