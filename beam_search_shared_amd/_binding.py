@@ -94,6 +94,7 @@ _SIGS = {
     "bsp_debug_plan_tables": (_I32, [_P, _P, _P, _P, _P, _P]),
     "bsp_debug_plan_items": (_I32, [_P, _P, _P]),
     "bsp_debug_tail_slots": (_I32, [_P, _P, _P, _P, _P]),
+    "bsp_write_kv_desc": (_I32, [_P, _P, _P, _I64, _P, _I32, _P, _P, _P, _P]),
     "bsp_debug_fused_slots": (_I32, [_P, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P]),
 }
 
@@ -347,6 +348,14 @@ def bsp_debug_plan_items(plan: Plan):
     items = np.zeros((max(int(n[0]), 1), 4), np.int32)
     _check(lib.bsp_debug_plan_items(plan.handle, _ptr(n), _ptr(items)))
     return items[:int(n[0])]
+
+
+def bsp_write_kv_desc(desc: LayerDesc, k_new, v_new, src_row_stride: int, slots, n: int,
+                      k_pool, v_pool, faults=None, stream=None) -> None:
+    _check(load_library().bsp_write_kv_desc(None if desc is None else ctypes.byref(desc),
+                                            _ptr(k_new), _ptr(v_new),
+                                            src_row_stride, _ptr(slots), n, _ptr(k_pool),
+                                            _ptr(v_pool), _ptr(faults), _stream(stream)))
 
 
 def bsp_debug_tail_slots(plan: Plan, block_tables, cache_indirection, slots_out,

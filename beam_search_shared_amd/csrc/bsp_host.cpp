@@ -763,14 +763,13 @@ bsp_status_t bsp_plan_prefill(bsp_plan_t pl, int32_t C, const int32_t* q_len_h,
 }
 
 
-bsp_status_t bsp_write_kv(bsp_plan_t pl, const void* k_new, const void* v_new,
-                          int64_t src_row_stride, const int32_t* slots_d, int32_t n, void* k_pool,
-                          void* v_pool, hipStream_t stream) {
-  bsp_status_t st = check_device_ready(pl);
-  if (st != BSP_OK) return st;
-  if (n < 0) return fail(BSP_ERR_ARG, "n < 0");
-  if (n == 0) return ok();
-  const bsp_layer_desc_t& d = pl->desc;
+namespace {
+
+// Validation and kernel parameters of the current-token write, from the layer
+// geometry alone; faults go to `fault` (int32[3]) or nowhere.
+bsp_status_t write_kv_params(const bsp_layer_desc_t& d, const void* k_new, const void* v_new,
+                             int64_t src_row_stride, const int32_t* slots_d, int32_t n,
+                             void* k_pool, void* v_pool, int32_t* fault, bsp::WriteKvParams& p) {
   if (!k_new || !v_new || !slots_d || !k_pool || !v_pool) return fail(BSP_ERR_ARG, "null pointer");
   const int vec = 16 / elem_bytes(d.dtype);
   if (src_row_stride < (int64_t)d.num_kv_heads * d.head_dim || src_row_stride % vec != 0)
@@ -778,7 +777,6 @@ bsp_status_t bsp_write_kv(bsp_plan_t pl, const void* k_new, const void* v_new,
                 (long long)src_row_stride, d.num_kv_heads * d.head_dim, vec);
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
     return fail(BSP_ERR_ARG, "k_new, v_new and the pools must be 16-byte aligned");
-  bsp::WriteKvParams p;
   p.k_new = k_new;
   p.v_new = v_new;
   p.src_stride = src_row_stride;
@@ -790,8 +788,52 @@ bsp_status_t bsp_write_kv(bsp_plan_t pl, const void* k_new, const void* v_new,
   p.d = d.head_dim;
   p.page_size = d.page_size;
   p.num_slots = (int64_t)d.num_pages * d.page_size;
-  p.hdr = dev_header(pl);
-  return after_launch(pl, bsp::launch_write_kv(p, d.dtype, stream), "write_kv launch", stream);
+  p.fault = fault;
+  return BSP_OK;
+}
+
+}  // namespace
+
+bsp_status_t bsp_write_kv(bsp_plan_t pl, const void* k_new, const void* v_new,
+                          int64_t src_row_stride, const int32_t* slots_d, int32_t n, void* k_pool,
+                          void* v_pool, hipStream_t stream) {
+  bsp_status_t st = check_device_ready(pl);
+  if (st != BSP_OK) return st;
+  if (n < 0) return fail(BSP_ERR_ARG, "n < 0");
+  if (n == 0) return ok();
+  bsp::WriteKvParams p;
+  st = write_kv_params(pl->desc, k_new, v_new, src_row_stride, slots_d, n, k_pool, v_pool,
+                       &dev_header(pl)->error_bits, p);
+  if (st != BSP_OK) return st;
+  return after_launch(pl, bsp::launch_write_kv(p, pl->desc.dtype, stream), "write_kv launch", stream);
+}
+
+bsp_status_t bsp_write_kv_desc(const bsp_layer_desc_t* desc, const void* k_new, const void* v_new,
+                               int64_t src_row_stride, const int32_t* slots_d, int32_t n,
+                               void* k_pool, void* v_pool, int32_t* faults_d, hipStream_t stream) {
+  if (desc == nullptr) return fail(BSP_ERR_ARG, "null descriptor");
+  const bsp_layer_desc_t& d = *desc;
+  if (d.dtype != BSP_F32 && d.dtype != BSP_F16 && d.dtype != BSP_BF16)
+    return fail(BSP_ERR_DTYPE, "dtype %d is not one of f32, f16, bf16", d.dtype);
+  if (d.num_kv_heads <= 0) return fail(BSP_ERR_ARG, "num_kv_heads must be positive");
+  if (d.head_dim != 64 && d.head_dim != 128 && d.head_dim != 256)
+    return fail(BSP_ERR_UNSUPPORTED, "head_dim %d is not 64, 128 or 256", d.head_dim);
+  if (!is_pow2(d.page_size) || d.page_size > 1024)
+    return fail(BSP_ERR_UNSUPPORTED, "page_size %d is not a power of two <= 1024", d.page_size);
+  if (d.num_pages <= 0) return fail(BSP_ERR_ARG, "num_pages must be positive");
+  if ((int64_t)d.num_pages * d.page_size > INT32_MAX)
+    return fail(BSP_ERR_UNSUPPORTED, "num_pages * page_size exceeds the int32 slot range");
+  if (n < 0) return fail(BSP_ERR_ARG, "n < 0");
+  if (n == 0) return ok();
+  if (faults_d != nullptr && (reinterpret_cast<uintptr_t>(faults_d) & 3u) != 0)
+    return fail(BSP_ERR_ARG, "faults_d must be 4-byte aligned");
+  bsp::WriteKvParams p;
+  const bsp_status_t st =
+      write_kv_params(d, k_new, v_new, src_row_stride, slots_d, n, k_pool, v_pool, faults_d, p);
+  if (st != BSP_OK) return st;
+  const hipError_t e = bsp::launch_write_kv(p, d.dtype, stream);
+  if (e != hipSuccess) return hip_fail(e, "write_kv launch");
+  return ok();
 }
 
 // Validation and kernel parameters of bsp_prefix_attn for one plan.

@@ -85,7 +85,7 @@ struct WriteKvParams {
   void* v_pool;
   int32_t hkv, d, page_size;
   int64_t num_slots;
-  DevHeader* hdr;
+  int32_t* fault;       // device int32[3] (error bits, fault count, first value) or null
 };
 
 struct PrefixParams {

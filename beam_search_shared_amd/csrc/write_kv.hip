@@ -25,9 +25,8 @@ __global__ __launch_bounds__(256) void write_kv_kernel(WriteKvParams p) {
 
   const int32_t slot = p.slots[i];
   if (slot < 0 || (int64_t)slot >= p.num_slots) {
-    if (h == 0 && c == 0)
-      record_fault(&p.hdr->error_bits, &p.hdr->fault_count, &p.hdr->first_value,
-                   kErrWriteSlot, slot);
+    if (h == 0 && c == 0 && p.fault != nullptr)
+      record_fault(p.fault, p.fault + 1, p.fault + 2, kErrWriteSlot, slot);
     return;
   }
   const int page = slot / p.page_size;

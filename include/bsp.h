@@ -199,11 +199,28 @@ int32_t bsp_plan_tail_len(bsp_plan_t plan);
  *                  element i * src_row_stride (16-byte aligned)
  *   slots_d        device int32 [n]; a slot outside [0, num_pages*page_size)
  *                  is skipped and recorded in the error word
- * n == 0 succeeds without a launch. Uses the plan's geometry and workspace.
+ * n == 0 succeeds without a launch. Uses the plan's geometry and workspace
+ * (bsp_check reports skipped slots), so the plan must have been planned once.
  */
 bsp_status_t bsp_write_kv(bsp_plan_t plan, const void* k_new, const void* v_new,
                           int64_t src_row_stride, const int32_t* slots_d, int32_t n,
                           void* k_pool, void* v_pool, hipStream_t stream);
+
+/*
+ * bsp_write_kv from the layer descriptor alone, with no plan: the same write
+ * (TensorRT-LLM PR #18614, Description: page and row from the flat slot, K and
+ * V in one launch) for callers that write a token before, or without, a step
+ * plan. The descriptor is checked as bsp_plan_create checks it (dtype,
+ * num_kv_heads, head_dim, page_size, num_pages; the other fields are not
+ * used). Skipped slots are counted in faults_d, device int32[3] or null:
+ * [0] becomes nonzero (an OR of error bits), [1] counts the skipped tokens and
+ * [2] holds one skipped slot value; the caller zeroes it, the call never does.
+ * With faults_d null, skipped slots leave no trace. Asynchronous on `stream`;
+ * n == 0 succeeds without a launch.
+ */
+bsp_status_t bsp_write_kv_desc(const bsp_layer_desc_t* desc, const void* k_new, const void* v_new,
+                               int64_t src_row_stride, const int32_t* slots_d, int32_t n,
+                               void* k_pool, void* v_pool, int32_t* faults_d, hipStream_t stream);
 
 /*
  * Shared-key attention: for each request b and KV head g, all W * q_len * G

@@ -133,6 +133,56 @@ def test_write_kv_skips_and_reports_bad_slots():
     assert not torch.equal(s.k_pool, before_k)
 
 
+@pytest.mark.parametrize("cfg,dtype", [("tiny", None), ("qwen3_4b", None), ("qwen3_0p6b", "f32")])
+def test_write_kv_desc_is_bit_exact_without_a_plan(cfg, dtype):
+    """bsp_write_kv_desc from the layer descriptor alone (no plan object at all):
+    bit-exact against the oracle's write, and skipped slots counted in the
+    caller's fault word."""
+    kw = {"batch": 3} if cfg != "tiny" else {}
+    if dtype:
+        kw["dtype"] = dtype
+    inp = synth.make_beam_step(cfg, 8, **kw)
+    k_pool = S.to_device(inp.k_pool, inp.dtype, DEV)
+    v_pool = S.to_device(inp.v_pool, inp.dtype, DEV)
+    k_new = S.to_device(inp.k_new, inp.dtype, DEV).reshape(len(inp.slots), -1).contiguous()
+    v_new = S.to_device(inp.v_new, inp.dtype, DEV).reshape(len(inp.slots), -1).contiguous()
+    slots = torch.as_tensor(inp.slots, dtype=torch.int32, device=DEV)
+    desc = B.make_desc(inp.num_q_heads, inp.num_kv_heads, inp.head_dim, inp.page_size,
+                       inp.num_pages, inp.dtype)
+    faults = torch.zeros(3, dtype=torch.int32, device=DEV)
+    B.bsp_write_kv_desc(desc, k_new, v_new, inp.num_kv_heads * inp.head_dim, slots, len(slots),
+                        k_pool, v_pool, faults)
+    torch.cuda.synchronize()
+    ref_k, ref_v = oracle.write_kv(inp.k_pool, inp.v_pool, inp.slots, inp.k_new, inp.v_new,
+                                   inp.page_size)
+    assert torch.equal(k_pool.cpu(), S.to_device(ref_k, inp.dtype, "cpu"))
+    assert torch.equal(v_pool.cpu(), S.to_device(ref_v, inp.dtype, "cpu"))
+    assert faults.tolist() == [0, 0, 0]
+    # two bad slots: skipped, counted, the good ones written
+    bad = slots.clone()
+    bad[0] = inp.num_pages * inp.page_size
+    bad[-1] = -3
+    k2 = S.to_device(inp.k_pool, inp.dtype, DEV)
+    v2 = S.to_device(inp.v_pool, inp.dtype, DEV)
+    B.bsp_write_kv_desc(desc, k_new, v_new, inp.num_kv_heads * inp.head_dim, bad, len(bad),
+                        k2, v2, faults)
+    torch.cuda.synchronize()
+    f = faults.tolist()
+    assert f[0] != 0 and f[1] == 2 and f[2] in (inp.num_pages * inp.page_size, -3)
+    good = np.ones(len(inp.slots), dtype=bool)
+    good[[0, -1]] = False
+    ref_k2, _ = oracle.write_kv(inp.k_pool, inp.v_pool, inp.slots[good], inp.k_new[good],
+                                inp.v_new[good], inp.page_size)
+    assert torch.equal(k2.cpu(), S.to_device(ref_k2, inp.dtype, "cpu"))
+    # with no fault word the bad slots are skipped all the same
+    k3 = S.to_device(inp.k_pool, inp.dtype, DEV)
+    v3 = S.to_device(inp.v_pool, inp.dtype, DEV)
+    B.bsp_write_kv_desc(desc, k_new, v_new, inp.num_kv_heads * inp.head_dim, bad, len(bad),
+                        k3, v3, None)
+    torch.cuda.synchronize()
+    assert torch.equal(k3, k2) and torch.equal(v3, v2)
+
+
 # ----------------------------------------------------------- index resolution
 
 def _tail_slots_gpu(s, pad):

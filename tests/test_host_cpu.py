@@ -209,6 +209,30 @@ def test_plan_create_rejects_bad_geometry():
                                   host_only=True))[0] == "BSP_ERR_ARG"
 
 
+def test_write_kv_desc_checks_before_any_launch(lib):
+    """bsp_write_kv_desc validates the descriptor and arguments on the host and
+    returns a status before any launch; n == 0 succeeds without one."""
+    fake = 1 << 20
+    d = B.make_desc(4, 2, 128, 32, 10, "bf16")
+
+    def call(desc, n=4, stride=256, k=fake, faults=None):
+        return B.bsp_write_kv_desc(desc, k, fake, stride, fake, n, fake, fake, faults, stream=0)
+    assert _status(lambda: B.bsp_write_kv_desc(None, fake, fake, 256, fake, 4, fake, fake,
+                                               stream=0))[0] == "BSP_ERR_ARG"
+    bad = B.make_desc(4, 2, 128, 32, 10, "bf16")
+    bad.dtype = 7
+    assert _status(lambda: call(bad))[0] == "BSP_ERR_DTYPE"
+    assert _status(lambda: call(B.make_desc(4, 2, 96, 32, 10, "bf16")))[0] == "BSP_ERR_UNSUPPORTED"
+    assert _status(lambda: call(B.make_desc(4, 2, 128, 24, 10, "bf16")))[0] == "BSP_ERR_UNSUPPORTED"
+    assert _status(lambda: call(B.make_desc(4, 2, 128, 32, 0, "bf16")))[0] == "BSP_ERR_ARG"
+    assert _status(lambda: call(d, n=-1))[0] == "BSP_ERR_ARG"
+    assert _status(lambda: call(d, stride=255))[0] == "BSP_ERR_ARG"   # < Hkv * D
+    assert _status(lambda: call(d, k=fake + 2))[0] == "BSP_ERR_ARG"   # misaligned
+    assert _status(lambda: call(d, k=0))[0] == "BSP_ERR_ARG"          # null
+    assert _status(lambda: call(d, faults=fake + 2))[0] == "BSP_ERR_ARG"
+    call(d, n=0)  # nothing to write: no launch
+
+
 def test_merge_argument_checks(lib):
     fake = 1 << 20
     assert _status(lambda: B.bsp_merge(4, 2, 6, 2, fake, fake, 48, 8, fake, "bf16",
