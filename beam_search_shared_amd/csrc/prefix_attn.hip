@@ -433,20 +433,29 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
   // softmax_tile: masking (`visible(qb, kk)`, consulted only when `full` is
   //   false) and the online softmax; P^T leaves as the B operand of O^T;
   // o_tile: O^T += V^T P^T.
+  // The operands of both products are read from LDS PF ahead of their use,
+  // so a read's latency overlaps the matrix instructions of the operands
+  // before it (reading each operand right before its use waited one LDS round
+  // trip per operand; the compiler keeps what its register budget allows).
+  constexpr int PF = MB == 1 ? 4 : MB == 2 ? 2 : 1;
   auto s_tile = [&](const T* lk, f32x4 (&sacc)[NKB][MB]) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int qb = 0; qb < MB; ++qb) sacc[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr int NOP = NDS * NKB;  // operand i: key block i % NKB, contraction step i / NKB
+    auto ld = [&](int i) -> V8 {
+      return *reinterpret_cast<const V8*>(&lk[TG::k_read((i % NKB) * 16 + l16, (i / NKB) * 4 + l4)]);
+    };
+    V8 a[PF + 1];
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
+    for (int i = 0; i < PF && i < NOP; ++i) a[i] = ld(i);
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const int r = kb * 16 + l16;
-        const V8 a = *reinterpret_cast<const V8*>(&lk[TG::k_read(r, ds * 4 + l4)]);
+    for (int i = 0; i < NOP; ++i) {
+      if (i + PF < NOP) a[(i + PF) % (PF + 1)] = ld(i + PF);
 #pragma unroll
-        for (int qb = 0; qb < MB; ++qb) sacc[kb][qb] = Mfma<T>::mma(a, qv[qb][ds], sacc[kb][qb]);
-      }
+      for (int qb = 0; qb < MB; ++qb)
+        sacc[i % NKB][qb] = Mfma<T>::mma(a[i % (PF + 1)], qv[qb][i / NKB], sacc[i % NKB][qb]);
     }
   };
 
@@ -512,21 +521,25 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
   };
 
   auto o_tile = [&](const T* lv, const V8 (&pb)[NS2][MB]) {
+    constexpr int NOP = NS2 * NDB;  // operand i: key step i / NDB, output block i % NDB
+    auto ld = [&](int i) -> V8 {
+      const int ra = 32 * (i / NDB) + 4 * l4 + (l16 >> 2);  // row read by this lane (+16 for the upper half)
+      // The operand is assembled from whole 32-bit words of the two reads
+      // (rows ra and ra + 16 share the swizzle: it depends on the low 4 bits).
+      const int off = TG::v_read(ra, (i % NDB) * 16 + 4 * (l16 & 3));
+      const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr(&lv[off]));
+      const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr(&lv[off + 16 * D]));
+      return __builtin_bit_cast(V8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+    };
+    V8 a[PF + 1];
 #pragma unroll
-    for (int s2 = 0; s2 < NS2; ++s2) {
-      const int ra = 32 * s2 + 4 * l4 + (l16 >> 2);   // row read by this lane (+16 for the upper half)
+    for (int i = 0; i < PF && i < NOP; ++i) a[i] = ld(i);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int col = db * 16 + 4 * (l16 & 3);
-        // The operand is assembled from whole 32-bit words of the two reads
-        // (rows ra and ra + 16 share the swizzle: it depends on the low 4 bits).
-        const int off = TG::v_read(ra, col);
-        const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr(&lv[off]));
-        const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr(&lv[off + 16 * D]));
-        const V8 a = __builtin_bit_cast(V8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+    for (int i = 0; i < NOP; ++i) {
+      if (i + PF < NOP) a[(i + PF) % (PF + 1)] = ld(i + PF);
 #pragma unroll
-        for (int qb = 0; qb < MB; ++qb) oacc[db][qb] = Mfma<T>::mma(a, pb[s2][qb], oacc[db][qb]);
-      }
+      for (int qb = 0; qb < MB; ++qb)
+        oacc[i % NDB][qb] = Mfma<T>::mma(a[i % (PF + 1)], pb[i / NDB][qb], oacc[i % NDB][qb]);
     }
   };
 
