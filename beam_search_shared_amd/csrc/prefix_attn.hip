@@ -869,12 +869,34 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
           act[qb] = r_lo < row_end && lo < min(u0 + KW, u_hi) && hi > u0;
           sacc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        // With one query block per wave every operand read is issued before
+        // the first is used: the K rows here, the V^T columns right after S^T
+        // so that they land during the softmax (one LDS round trip per
+        // sub-tile instead of one per operand; measured: the n-sample step,
+        // whose tails are long, ~1% faster; at more blocks per wave the
+        // registers cost more than the overlap gains).
+        constexpr bool TPF = MB == 1;
+        auto k_op = [&](int ds) { return *reinterpret_cast<const V8*>(&lk[TG::k_read(l16, ds * 4 + l4)]); };
+        const int ra = 4 * l4 + (l16 >> 2);
+        auto v_op = [&](int db) {
+          return __builtin_bit_cast(u32x2, lds_read_tr(&lv[TG::v_read(ra, db * 16 + 4 * (l16 & 3))]));
+        };
+        V8 ka[TPF ? NDS : 1];
+        if constexpr (TPF) {
+#pragma unroll
+          for (int ds = 0; ds < NDS; ++ds) ka[ds] = k_op(ds);
+        }
 #pragma unroll
         for (int ds = 0; ds < NDS; ++ds) {
-          const V8 a = *reinterpret_cast<const V8*>(&lk[TG::k_read(l16, ds * 4 + l4)]);
+          const V8 a = TPF ? ka[TPF ? ds : 0] : k_op(ds);
 #pragma unroll
           for (int qb = 0; qb < MB; ++qb)
             if (act[qb]) sacc[qb] = Mfma<T>::mma(a, qv[qb][ds], sacc[qb]);
+        }
+        u32x2 va[TPF ? NDB : 1];
+        if constexpr (TPF) {
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) va[db] = v_op(db);
         }
         // ---- mask (own beam, valid slot) and online softmax
         u32x2 pb[MB];
@@ -912,12 +934,10 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
           }
           pb[qb] = __builtin_bit_cast(u32x2, e4);
         }
-        // ---- O^T += V^T P^T over the 16 keys (V^T operand by transpose reads)
-        const int ra = 4 * l4 + (l16 >> 2);
+        // ---- O^T += V^T P^T over the 16 keys (V^T operands by transpose reads)
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const int col = db * 16 + 4 * (l16 & 3);
-          const u32x2 a = __builtin_bit_cast(u32x2, lds_read_tr(&lv[TG::v_read(ra, col)]));
+          const u32x2 a = TPF ? va[TPF ? db : 0] : v_op(db);
 #pragma unroll
           for (int qb = 0; qb < MB; ++qb)
             if (act[qb]) oacc[db][qb] = Mfma<T>::mma16(a, pb[qb], oacc[db][qb]);
