@@ -656,8 +656,16 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
       if (!wave_active) continue;
       const int t0 = seg_lo + t * KT;
       f32x4 sacc[NKB][MB];
+      // Rotated loop: the wave issues its matrix instructions at raised
+      // priority, so that of the two waves sharing a SIMD the one with
+      // matrix work to issue goes first while the other runs its softmax
+      // (measured: wide beam 1.5%, the head_dim 64 4B layer 2-3% and the
+      // cached-prefix prefill's cache segment 4% faster; the unrotated loop,
+      // whose softmax sits between its two products, gains nothing).
+      if (ROT) __builtin_amdgcn_s_setprio(1);
       s_tile(lds_kv[t % NST][0], sacc);
       if (ROT && t > 0) o_tile(lds_kv[(t - 1) % NST][1], pb);
+      if (ROT) __builtin_amdgcn_s_setprio(0);
       softmax_tile(sacc, (t0 + KT <= w.k_hi) && (is_pre || causal1 ? t0 + KT - 1 <= c_first : !p.causal),
                    [&](int qb, int kk) { return (t0 + kk < w.k_hi) & (t0 + kk <= climit[qb]); }, pb);
       if (!ROT) o_tile(lds_kv[t % NST][1], pb);
