@@ -464,6 +464,7 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
   // the tile's probabilities stay below 2^kLazyLog2, far inside the bf16/f16
   // range. The log-sum-exp is taken against the same m, so the result is that
   // of the exact running-max update.
+  const float lazy_keys = kLazyLog2 / c2;  // the lazy threshold in raw score units
   auto softmax_tile = [&](f32x4 (&sacc)[NKB][MB], bool full, auto&& visible, V8 (&pb)[NS2][MB]) {
     if (__builtin_expect(!full, 0)) {  // wave-uniform: only a tile crossing the key bound
       asm volatile("" ::: "memory");     // keep it a branch, not selects on every tile
@@ -482,13 +483,16 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[kb][qb][e]);
-      mx = max4x16(mx);
-      // NaN (both -inf: nothing visible yet) compares false
-      const bool grow = (mx - mrow[qb]) * c2 > kLazyLog2;
-      if (__builtin_expect(__builtin_amdgcn_ballot_w64(grow) != 0, 0)) {
+      // A row's max passes its reference by more than kLazyLog2 exactly when
+      // one of its four lanes' maxima does: each lane tests its own against
+      // the row's threshold and the row max across the lanes is taken only
+      // on the (rare) rescale. -inf + x stays -inf and compares false, as
+      // the difference of two -inf (NaN) did.
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(mx > mrow[qb] + lazy_keys) != 0, 0)) {
         // Keep this a branch: the compiler would otherwise scale O on every
         // tile with alpha = 1.
         asm volatile("" ::: "memory");
+        mx = max4x16(mx);
         const float m_new = fmaxf(mrow[qb], mx);
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
         const float alpha = fast_exp2((mrow[qb] - m_use) * c2);
@@ -920,10 +924,10 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
             sacc[qb][e] = sv;
             mx = fmaxf(mx, sv);
           }
-          mx = max4x16(mx);
-          const bool grow = (mx - mrow[qb]) * c2 > kLazyLog2;
-          if (__builtin_expect(__builtin_amdgcn_ballot_w64(grow) != 0, 0)) {
+          // the same lane-wise test as the prompt loop's
+          if (__builtin_expect(__builtin_amdgcn_ballot_w64(mx > mrow[qb] + lazy_keys) != 0, 0)) {
             asm volatile("" ::: "memory");
+            mx = max4x16(mx);
             const float m_new = fmaxf(mrow[qb], mx);
             const float m_use = m_new == -INFINITY ? 0.f : m_new;
             const float alpha = fast_exp2((mrow[qb] - m_use) * c2);
