@@ -557,6 +557,51 @@ def test_cached_decode_one_launch_many_chunks(L, split):
     assert (c.lse_out - one[1]).abs().max().item() <= 1e-5
 
 
+@pytest.mark.parametrize("hq,hkv,d,dtype,L", [(16, 4, 64, "bf16", 3000), (8, 4, 256, "f16", 2000),
+                                              (32, 4, 128, "bf16", 4100), (16, 4, 256, "bf16", 777),
+                                              (8, 8, 64, "f16", 1)])
+def test_cached_decode_one_launch_other_shapes(hq, hkv, d, dtype, L):
+    """bsp_cached_decode at the other head sizes and group sizes its merge takes
+    (query heads per KV head x head_dim / 4 up to 256), in both 16-bit dtypes:
+    against the oracle, the new row written bit for bit, and equal to the
+    four-launch call within rounding."""
+    R = oracle.bucket_rows(L, 256, 4608)
+    inp = synth.make_cached_prefix(L % 11, valid_rows=L, q_len=1, num_q_heads=hq,
+                                   num_kv_heads=hkv, head_dim=d, dtype=dtype,
+                                   max_cache_rows=4608, nan_from_row=R)
+    c = S.upload_cached_prefix(inp, DEV)
+    S.plan_cached_prefix(c)
+    say(f"one-launch cached decode {hq}/{hkv} heads d={d} {dtype} L={L}: {c.n_split} chunks")
+    o, lse = oracle.cached_prefix_attention(inp, causal=True)
+    S.run_cached_decode(c)
+    B.bsp_check(c.plan_cache)
+    torch.cuda.synchronize()
+    assert_close(c.out.reshape(1, hq, d), c.lse_out.reshape(1, hq), o, lse, dtype,
+                 f"one-launch decode {hq}/{hkv} d={d} {dtype}")
+    one = (c.out.clone(), c.lse_out.clone())
+    page, row = divmod(int(c.slots[0]), c.page_size)
+    assert torch.equal(c.k_pool[page, :, row].cpu(), S.to_device(inp.new_k[0], dtype, "cpu"))
+    assert torch.equal(c.v_pool[page, :, row].cpu(), S.to_device(inp.new_v[0], dtype, "cpu"))
+    S.run_cached_prefix(c)
+    B.bsp_check(c.plan_cache)
+    B.bsp_check(c.plan_new)
+    torch.cuda.synchronize()
+    assert (c.out.float() - one[0].float()).abs().max().item() <= TOL[dtype][0]
+    assert (c.lse_out - one[1]).abs().max().item() <= 1e-5
+
+
+def test_cached_decode_one_launch_rejects_too_wide_groups():
+    """Eight query heads per KV head at head_dim 256 (512 row-chunk pairs) are more
+    than the merge's 256 threads: refused before any launch."""
+    inp = synth.make_cached_prefix(2, valid_rows=500, q_len=1, num_q_heads=16, num_kv_heads=2,
+                                   head_dim=256, dtype="f16", max_cache_rows=1024)
+    c = S.upload_cached_prefix(inp, DEV)
+    S.plan_cached_prefix(c)
+    with pytest.raises(B.BspError) as ei:
+        S.run_cached_decode(c)
+    assert ei.value.name == "BSP_ERR_UNSUPPORTED"
+
+
 def test_cached_decode_one_launch_rejects_other_plans():
     inp = synth.make_cached_prefix(3, valid_rows=300, q_len=4)
     c = S.upload_cached_prefix(inp, DEV)
