@@ -4,6 +4,7 @@ tables bit for bit and returns the documented status for every host-forcible
 error. No kernel is launched here."""
 
 import ctypes
+import re
 import json
 import os
 
@@ -31,6 +32,45 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), name
         assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
     assert lib.bsp_version() >= 100
+
+
+def _c_kind(decl: str) -> str:
+    """The ctypes kind a C parameter or return type maps to."""
+    decl = decl.strip()
+    if "*" in decl or decl.split()[0] in ("bsp_plan_t", "hipStream_t"):
+        return "char*" if decl.replace(" ", "").startswith("constchar*") else "ptr"
+    base = decl.replace("const ", "").split()[0]
+    return {"bsp_status_t": "i32", "int32_t": "i32", "int64_t": "i64", "uint32_t": "u32",
+            "size_t": "size", "void": "void"}[base]
+
+
+def _ctypes_kind(t) -> str:
+    if t is None:
+        return "void"
+    if t is ctypes.c_char_p:
+        return "char*"
+    if t is ctypes.c_void_p or (isinstance(t, type) and issubclass(t, ctypes._Pointer)):
+        return "ptr"
+    return {ctypes.c_int32: "i32", ctypes.c_int64: "i64", ctypes.c_uint32: "u32",
+            ctypes.c_size_t: "size"}[t]
+
+
+def test_binding_signatures_match_the_header():
+    """Every function include/bsp.h declares has a binding entry whose return and
+    argument kinds (pointer, int32, int64, uint32, size_t) match the declaration
+    one for one, so a drifted argument list fails here instead of at a call."""
+    text = open(B.HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    decls = re.findall(r"^[ \t]*([A-Za-z_][\w \t\*]*?)\b(bsp_\w+)\s*\(([^;{]*?)\)\s*;", text,
+                       flags=re.M)
+    assert len(decls) == len(B.declared_symbols())
+    for ret, name, args in decls:
+        assert name in B._SIGS, f"{name} has no binding"
+        res, argtypes = B._SIGS[name]
+        params = [] if args.strip() in ("", "void") else [x for x in args.split(",")]
+        kinds = [_c_kind(x.rsplit(None, 1)[0] if not x.strip().endswith("*") else x) for x in params]
+        assert [_ctypes_kind(t) for t in argtypes] == kinds, name
+        assert _ctypes_kind(res) == _c_kind(ret), name
 
 
 def _host_plan(inp, max_tail=0, key_bucket=0, max_cache_rows=0):
