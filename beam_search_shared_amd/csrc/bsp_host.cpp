@@ -1032,6 +1032,12 @@ bsp_status_t decode_params(bsp_plan_s* pl, const void* q, const void* k_new, con
     f.split_count = reinterpret_cast<int32_t*>(ws + pl->split_count_off);
     f.split_part = reinterpret_cast<float*>(ws + pl->split_part_off);
   }
+  // output rows (and their lse) plus the current tokens' K and V rows
+  const int64_t e = elem_bytes(d.dtype);
+  const int64_t rows = (int64_t)pl->B * pl->W;
+  const int64_t writes = rows * d.num_q_heads * (d.head_dim * e + (lse_out ? 4 : 0)) +
+                         rows * d.num_kv_heads * d.head_dim * e * 2;
+  f.stream_out = writes <= bsp::kStreamOutBytes ? 1 : 0;
   return BSP_OK;
 }
 

@@ -43,6 +43,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uin
 // point, so data written by a workgroup on another XCD is seen).
 constexpr int kCoherentAgent = 16;
 
+// Store with the non-temporal hint. The fused beam step at one query block per
+// wave writes its outputs and the current tokens' pool rows this way when they
+// fit the L2s: a plain store leaves the line dirty in the XCD's L2, and at the
+// end of a kernel every XCD writes its dirty lines back before the next kernel
+// starts, so such a step paid for all of its writes after its last workgroup
+// (0.6B-like step 41.3 -> 38.3 us per launch). The prefill, partial-state,
+// merge and KV-write kernels measured slower with it and keep plain stores.
+template <typename V>
+__device__ __forceinline__ void stream_store(V* p, V v) { __builtin_nontemporal_store(v, p); }
+// A non-temporal or a plain store, by a run-time flag. The two branches carry
+// different (empty) asm markers before and after their store: with identical
+// neighbours the compiler hoists or sinks the two stores into one and keeps
+// it without the hint.
+template <typename V>
+__device__ __forceinline__ void store_maybe_stream(V* p, V v, bool stream) {
+  if (stream) {
+    asm volatile("; streaming store");
+    __builtin_nontemporal_store(v, p);
+    asm volatile("; streaming store done");
+  } else {
+    asm volatile("; store");
+    *p = v;
+    asm volatile("; store done");
+  }
+}
+
 // 2^x on the transcendental unit (v_exp_f32); exp2(-inf) = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

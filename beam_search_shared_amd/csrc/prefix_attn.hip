@@ -804,8 +804,16 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
         continue;
       }
       const int64_t dst = pool_row(page[i], p.hkv, w.g, shift, (ri.seq - 1) & pmask, D) + (task % CPR) * 8;
-      *reinterpret_cast<u32x4*>(static_cast<T*>(f.k_pool_w) + dst) = kd[i];
-      *reinterpret_cast<u32x4*>(static_cast<T*>(f.v_pool_w) + dst) = vd[i];
+      // streaming stores (see kStreamOutBytes) at one query block per wave only:
+      // the step shapes with more blocks gained at most 1% and their tight
+      // register budgets did not take the second store path without spilling
+      if constexpr (MB == 1) {
+        store_maybe_stream(reinterpret_cast<u32x4*>(static_cast<T*>(f.k_pool_w) + dst), kd[i], f.stream_out != 0);
+        store_maybe_stream(reinterpret_cast<u32x4*>(static_cast<T*>(f.v_pool_w) + dst), vd[i], f.stream_out != 0);
+      } else {
+        *reinterpret_cast<u32x4*>(static_cast<T*>(f.k_pool_w) + dst) = kd[i];
+        *reinterpret_cast<u32x4*>(static_cast<T*>(f.v_pool_w) + dst) = vd[i];
+      }
     }
   };
 
@@ -1088,9 +1096,16 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
         T e4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) e4[e] = Traits<T>::from_f(oacc[db][qb][e] * inv);
-        *reinterpret_cast<u32x2*>(op + db * 16) = __builtin_bit_cast(u32x2, e4);
+        if constexpr (MB == 1)
+          store_maybe_stream(reinterpret_cast<u32x2*>(op + db * 16), __builtin_bit_cast(u32x2, e4),
+                             fused && f.stream_out);
+        else
+          *reinterpret_cast<u32x2*>(op + db * 16) = __builtin_bit_cast(u32x2, e4);
       }
-      if (l4 == 0 && f.lse_out != nullptr) f.lse_out[ohead] = lse;
+      if (l4 == 0 && f.lse_out != nullptr) {
+        if constexpr (MB == 1) store_maybe_stream(f.lse_out + ohead, lse, fused && f.stream_out);
+        else f.lse_out[ohead] = lse;
+      }
     } else if constexpr (MODE == 5) {
       // read back by the last chunk to finish, maybe on another XCD: agent-coherent
       // (sc1) stores, 16 bytes each; offsets fit 32 bits (checked by the host)
