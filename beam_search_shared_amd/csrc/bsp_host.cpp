@@ -983,8 +983,8 @@ bsp_status_t decode_params(bsp_plan_s* pl, const void* q, const void* k_new, con
     return fail(BSP_ERR_ARG, "new_row_stride %lld must be >= %d and a multiple of %d",
                 (long long)new_row_stride, d.num_kv_heads * d.head_dim, vec);
   if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) ||
-      !aligned16(v_pool) || (reinterpret_cast<uintptr_t>(o_out) & 7u) != 0)
-    return fail(BSP_ERR_ARG, "q, k_new, v_new and the pools must be 16-byte aligned, o_out 8-byte");
+      !aligned16(v_pool) || !aligned16(o_out))
+    return fail(BSP_ERR_ARG, "q, k_new, v_new, the pools and o_out must be 16-byte aligned");
   p = bsp::PrefixParams{};
   p.q = q;
   p.k_pool = k_pool;

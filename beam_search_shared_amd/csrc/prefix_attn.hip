@@ -1090,17 +1090,42 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
     const float lse = lt > 0.f ? mrow[qb] * p.scale + __logf(lt) : -INFINITY;
     if constexpr (FUSED || PREFILL) {
       const int64_t ohead = grow * p.hq + w.g * p.group + hh;
-      T* op = static_cast<T*>(f.o_out) + ohead * D + l4 * 4;
+      T* orow = static_cast<T*>(f.o_out) + ohead * D;
+      if constexpr (MB == 1) {
+        // Lane row l4 holds columns 4*l4..4*l4+3 of each 16-column block. One
+        // permlane16 swap per dword pairs blocks db and db+1 across neighbouring
+        // lane rows, so even rows hold 8 columns of block db and odd rows 8 of
+        // block db+1: 16 bytes per lane and 64 contiguous bytes per row and
+        // store, whole memory segments for the streaming stores. (At more
+        // blocks per wave the swaps cost registers the loop does not have.)
+        static_assert(NDB % 2 == 0, "output blocks are stored in pairs");
+        T* op = orow + (l4 & 1) * 16 + (l4 >> 1) * 8;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        T e4[4];
+        for (int db = 0; db < NDB; db += 2) {
+          T a4[4], b4[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) e4[e] = Traits<T>::from_f(oacc[db][qb][e] * inv);
-        if constexpr (MB == 1)
-          store_maybe_stream(reinterpret_cast<u32x2*>(op + db * 16), __builtin_bit_cast(u32x2, e4),
-                             fused && f.stream_out);
-        else
+          for (int e = 0; e < 4; ++e) {
+            a4[e] = Traits<T>::from_f(oacc[db][qb][e] * inv);
+            b4[e] = Traits<T>::from_f(oacc[db + 1][qb][e] * inv);
+          }
+          const u32x2 au = __builtin_bit_cast(u32x2, a4);
+          const u32x2 bu = __builtin_bit_cast(u32x2, b4);
+          const unsigned a0 = au[0], a1 = au[1], b0 = bu[0], b1 = bu[1];
+          const auto s0 = __builtin_amdgcn_permlane16_swap(a0, b0, false, false);
+          const auto s1 = __builtin_amdgcn_permlane16_swap(a1, b1, false, false);
+          const unsigned x0 = s0[0], y0 = s0[1], x1 = s1[0], y1 = s1[1];
+          const u32x4 v = {x0, x1, y0, y1};
+          store_maybe_stream(reinterpret_cast<u32x4*>(op + db * 16), v, fused && f.stream_out);
+        }
+      } else {
+        T* op = orow + l4 * 4;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          T e4[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) e4[e] = Traits<T>::from_f(oacc[db][qb][e] * inv);
           *reinterpret_cast<u32x2*>(op + db * 16) = __builtin_bit_cast(u32x2, e4);
+        }
       }
       if (l4 == 0 && f.lse_out != nullptr) {
         if constexpr (MB == 1) store_maybe_stream(f.lse_out + ohead, lse, fused && f.stream_out);

@@ -331,7 +331,9 @@ bsp_status_t bsp_merge(int32_t rows, int32_t heads, int32_t head_dim, int32_t n_
  *                  (b * W + k) * new_row_stride, [Hkv][D] contiguous, 16-byte
  *                  aligned; rows of requests without a tail are not read
  *   k_pool, v_pool written at each beam's slot for position S_b - 1
- *   o_out          dtype [B * W][Hq][D]; lse_out float [B * W][Hq] or null
+ *   o_out          dtype [B * W][Hq][D], 16-byte aligned; lse_out float
+ *                  [B * W][Hq] or null
+ * q and the pools are 16-byte aligned too (BSP_ERR_ARG otherwise).
  * bf16/f16 only (BSP_ERR_UNSUPPORTED for f32: use the separate calls).
  * Work items go longest first. When the plan split a request's prompt into
  * chunks (see bsp_debug_plan_items), each chunk's workgroup leaves its partial
