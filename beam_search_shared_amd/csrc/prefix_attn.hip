@@ -804,10 +804,10 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
         continue;
       }
       const int64_t dst = pool_row(page[i], p.hkv, w.g, shift, (ri.seq - 1) & pmask, D) + (task % CPR) * 8;
-      // streaming stores (see kStreamOutBytes) at one query block per wave only:
-      // the step shapes with more blocks gained at most 1% and their tight
-      // register budgets did not take the second store path without spilling
-      if constexpr (MB == 1) {
+      // streaming stores (see kStreamOutBytes) at up to two query blocks per
+      // wave; at three the register budget does not take the second store path
+      // without spilling
+      if constexpr (MB <= 2) {
         store_maybe_stream(reinterpret_cast<u32x4*>(static_cast<T*>(f.k_pool_w) + dst), kd[i], f.stream_out != 0);
         store_maybe_stream(reinterpret_cast<u32x4*>(static_cast<T*>(f.v_pool_w) + dst), vd[i], f.stream_out != 0);
       } else {
@@ -1091,12 +1091,12 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
     if constexpr (FUSED || PREFILL) {
       const int64_t ohead = grow * p.hq + w.g * p.group + hh;
       T* orow = static_cast<T*>(f.o_out) + ohead * D;
-      if constexpr (MB == 1) {
+      if constexpr (MB <= 2) {
         // Lane row l4 holds columns 4*l4..4*l4+3 of each 16-column block. One
         // permlane16 swap per dword pairs blocks db and db+1 across neighbouring
         // lane rows, so even rows hold 8 columns of block db and odd rows 8 of
         // block db+1: 16 bytes per lane and 64 contiguous bytes per row and
-        // store, whole memory segments for the streaming stores. (At more
+        // store, whole memory segments for the streaming stores. (At three
         // blocks per wave the swaps cost registers the loop does not have.)
         static_assert(NDB % 2 == 0, "output blocks are stored in pairs");
         T* op = orow + (l4 & 1) * 16 + (l4 >> 1) * 8;
@@ -1128,7 +1128,7 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
         }
       }
       if (l4 == 0 && f.lse_out != nullptr) {
-        if constexpr (MB == 1) store_maybe_stream(f.lse_out + ohead, lse, fused && f.stream_out);
+        if constexpr (MB <= 2) store_maybe_stream(f.lse_out + ohead, lse, fused && f.stream_out);
         else f.lse_out[ohead] = lse;
       }
     } else if constexpr (MODE == 5) {
