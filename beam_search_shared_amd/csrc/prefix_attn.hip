@@ -555,6 +555,67 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
   constexpr int AHEAD = ROT ? NST - 2 : NST - 1;  // tiles in flight beyond the one computed
 
   const int n_tail = fused ? ri.tail : 0;
+  // ---- current tokens of this tile's beams: a beam's token is written by the
+  // tile holding its first row, 16 bytes per task. Nothing in this launch
+  // reads it back from the pool (the tails take the current token from the
+  // new-token rows), so the stores go last, where they delay no tile.
+  const int kw_lo = (w.qt * rt + p.group - 1) / p.group;
+  const int kw_hi = min(p.W, ((w.qt + 1) * rt + p.group - 1) / p.group);
+  const int n_tw = fused && n_tail > 0 ? (kw_hi - kw_lo) * CPR : 0;
+  auto tw_load = [&](int base, auto& page, auto& kd, auto& vd) {
+    constexpr int N = (int)(sizeof(page) / sizeof(int32_t));
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int task = base + i * 256 + tid;
+      page[i] = -1;
+      if (task < n_tw) {
+        const int kk = kw_lo + task / CPR;
+        const int64_t src = ((int64_t)w.b * p.W + kk) * f.new_stride + (int64_t)w.g * D + (task % CPR) * 8;
+        page[i] = f.block_tables[((int64_t)w.b * p.W + kk) * f.max_blocks + ((ri.seq - 1) >> shift)];
+        kd[i] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(f.k_new) + src);
+        vd[i] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(f.v_new) + src);
+      }
+    }
+  };
+  auto tw_store = [&](int base, const auto& page, const auto& kd, const auto& vd) {
+    constexpr int N = (int)(sizeof(page) / sizeof(int32_t));
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int task = base + i * 256 + tid;
+      if (task >= n_tw) continue;
+      if (page[i] < 0 || page[i] >= p.num_pages) {
+        if (task % CPR == 0)
+          record_fault(&p.hdr->error_bits, &p.hdr->fault_count, &p.hdr->first_value,
+                       kErrTailPage, page[i]);
+        continue;
+      }
+      const int64_t dst = pool_row(page[i], p.hkv, w.g, shift, (ri.seq - 1) & pmask, D) + (task % CPR) * 8;
+      // streaming stores (see kStreamOutBytes) at up to two query blocks per
+      // wave; at three the register budget does not take the second store path
+      // without spilling
+      if constexpr (MB <= 2) {
+        store_maybe_stream(reinterpret_cast<u32x4*>(static_cast<T*>(f.k_pool_w) + dst), kd[i], f.stream_out != 0);
+        store_maybe_stream(reinterpret_cast<u32x4*>(static_cast<T*>(f.v_pool_w) + dst), vd[i], f.stream_out != 0);
+      } else {
+        *reinterpret_cast<u32x4*>(static_cast<T*>(f.k_pool_w) + dst) = kd[i];
+        *reinterpret_cast<u32x4*>(static_cast<T*>(f.v_pool_w) + dst) = vd[i];
+      }
+    }
+  };
+
+
+  // Where each thread has at most TWE tasks (one or two query blocks per wave,
+  // head_dim <= 128, an unsplit request) the rows are loaded in the prologue,
+  // beside the queries, in the round trip that ends with the wait before the
+  // first tile load (a wait the compiler sees), and held until the end, which
+  // then has only the stores; otherwise both go last. (Storing them right
+  // after the first tile landed measured slower: the stores then count in the
+  // tile waits. So did loading them after the prompt, before the tails.)
+  constexpr int TWE = MB == 1 ? 4 : 2;
+  constexpr bool TW_EARLY = FUSED && MB <= 2 && D <= 128;
+  const bool tw_early = TW_EARLY && !split && n_tw > 0 && n_tw <= 256 * TWE;
+  int32_t e_page[TWE];
+  u32x4 e_kd[TWE], e_vd[TWE];
   // prefill, and causal rows of one sequence: the smallest causal limit among
   // this wave's rows (its first row); a key tile at or below it needs no mask
   const bool causal1 = !FUSED && !is_pre && p.causal && p.W == 1;
@@ -578,6 +639,9 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
       lds_pages[i] = page;
     }
   };
+  if constexpr (TW_EARLY) {
+    if (tw_early) tw_load(0, e_page, e_kd, e_vd);
+  }
   if constexpr (DEFER) {
     if (n_win > 0) fill_pages(0);
     // The queries, the tail parents and the first page ids are complete
@@ -766,56 +830,6 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
       sl_build(256 * TR);
     }
   }
-
-  // ---- current tokens of this tile's beams: a beam's token is written by the
-  // tile holding its first row, 16 bytes per task. Nothing in this launch
-  // reads it back from the pool (the tails take the current token from the
-  // new-token rows), so it is written last, where its loads and stores delay
-  // no tile. (Loading the first tasks before the tails, to overlap the two
-  // round trips, measured slower.)
-  const int kw_lo = (w.qt * rt + p.group - 1) / p.group;
-  const int kw_hi = min(p.W, ((w.qt + 1) * rt + p.group - 1) / p.group);
-  const int n_tw = fused && n_tail > 0 ? (kw_hi - kw_lo) * CPR : 0;
-  auto tw_load = [&](int base, auto& page, auto& kd, auto& vd) {
-    constexpr int N = (int)(sizeof(page) / sizeof(int32_t));
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int task = base + i * 256 + tid;
-      page[i] = -1;
-      if (task < n_tw) {
-        const int kk = kw_lo + task / CPR;
-        const int64_t src = ((int64_t)w.b * p.W + kk) * f.new_stride + (int64_t)w.g * D + (task % CPR) * 8;
-        page[i] = f.block_tables[((int64_t)w.b * p.W + kk) * f.max_blocks + ((ri.seq - 1) >> shift)];
-        kd[i] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(f.k_new) + src);
-        vd[i] = *reinterpret_cast<const u32x4*>(static_cast<const T*>(f.v_new) + src);
-      }
-    }
-  };
-  auto tw_store = [&](int base, const auto& page, const auto& kd, const auto& vd) {
-    constexpr int N = (int)(sizeof(page) / sizeof(int32_t));
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int task = base + i * 256 + tid;
-      if (task >= n_tw) continue;
-      if (page[i] < 0 || page[i] >= p.num_pages) {
-        if (task % CPR == 0)
-          record_fault(&p.hdr->error_bits, &p.hdr->fault_count, &p.hdr->first_value,
-                       kErrTailPage, page[i]);
-        continue;
-      }
-      const int64_t dst = pool_row(page[i], p.hkv, w.g, shift, (ri.seq - 1) & pmask, D) + (task % CPR) * 8;
-      // streaming stores (see kStreamOutBytes) at up to two query blocks per
-      // wave; at three the register budget does not take the second store path
-      // without spilling
-      if constexpr (MB <= 2) {
-        store_maybe_stream(reinterpret_cast<u32x4*>(static_cast<T*>(f.k_pool_w) + dst), kd[i], f.stream_out != 0);
-        store_maybe_stream(reinterpret_cast<u32x4*>(static_cast<T*>(f.v_pool_w) + dst), vd[i], f.stream_out != 0);
-      } else {
-        *reinterpret_cast<u32x4*>(static_cast<T*>(f.k_pool_w) + dst) = kd[i];
-        *reinterpret_cast<u32x4*>(static_cast<T*>(f.v_pool_w) + dst) = vd[i];
-      }
-    }
-  };
 
   // ---- MODE 1: each wave attends its own beams' tails (slot-table rows
   // u = (beam - kb_first) * n_tail + t) in 16-key sub-tiles, double-buffered
@@ -1299,9 +1313,12 @@ __device__ __forceinline__ void prefix_body(PrefixParams p, FusedParams f, int b
     }
   }
 
-  // ---- the current tokens (see above); the unrolled batch holds all of a
-  // wide beam's tasks
-  if (n_tw > 0) {
+  // ---- the current tokens (see above): the stores of the rows loaded in the
+  // prologue, or loads and stores here (the unrolled batch holds all of a wide
+  // beam's tasks)
+  if (TW_EARLY && tw_early) {
+    tw_store(0, e_page, e_kd, e_vd);
+  } else if (n_tw > 0) {
     constexpr int TW = 16;
     for (int base = 0; base < n_tw; base += 256 * TW) {
       int32_t page[TW];
