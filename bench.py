@@ -592,8 +592,9 @@ def main() -> None:
                          "of known size, to scale HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this path runs on a "
-              "single MI355X; see DESIGN.md for how it would shard.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the step runs on a "
+              "single MI355X; across GPUs each would run it on its own share of the requests.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
