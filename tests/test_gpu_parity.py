@@ -786,6 +786,48 @@ def test_decode_step_matches_oracle(case, seed):
     say(f"  max |dO| = {_run_fused_and_check(inp, case, max_tail=mt):.3g}")
 
 
+# Current-token rows at one or two query blocks per wave (head_dim <= 128, no
+# split) are loaded in the prologue when each thread has at most 4 (MB = 1) or
+# 2 (MB = 2) of a tile's 16-byte tasks, else loaded at the end; each case sits
+# on one side of that line (tasks = beams in the tile x head_dim / 8).
+TOKEN_ROW_CASES = {
+    # MB = 1 (64 rows), 64 beams x 16 tasks = 1024 = 256 x 4: prologue
+    "mb1_d128_at_limit": (BeamConfig("tw1", 2, 64, 2, 2, 128, "bf16", 16, (70, 150), (1, 5), True), None),
+    # MB = 2 (100 rows), 100 beams x 16 tasks = 1600 > 512: loaded at the end
+    "mb2_d128_g1_late": (BeamConfig("tw2", 2, 100, 2, 2, 128, "bf16", 16, (70, 150), (1, 5), True), None),
+    # MB = 2 (100 rows), 50 beams x 8 tasks = 400 <= 512: prologue
+    "mb2_d64_g2_early": (BeamConfig("tw3", 2, 50, 4, 2, 64, "f16", 16, (70, 150), (1, 5), True), None),
+    # MB = 2 (128 rows), 64 beams x 8 tasks = 512 = 256 x 2: prologue
+    "mb2_d64_g2_at_limit": (BeamConfig("tw4", 2, 64, 4, 2, 64, "bf16", 16, (70, 150), (1, 5), False), None),
+    # head_dim 256 (MB = 1): loaded at the end
+    "mb1_d256_late": (BeamConfig("tw5", 2, 30, 4, 2, 256, "bf16", 16, (70, 150), (1, 5), True), None),
+    # a split request (chunks of 64 keys): loaded at the end by the finishing chunk
+    "mb1_d128_split": (BeamConfig("tw6", 2, 30, 4, 2, 128, "bf16", 16, (150, 300), (1, 5), True), 64),
+}
+
+
+@pytest.mark.parametrize("case", list(TOKEN_ROW_CASES))
+def test_decode_step_token_rows_early_and_late(case, monkeypatch):
+    cfg, split = TOKEN_ROW_CASES[case]
+    if split is not None:
+        monkeypatch.setenv("BSP_SPLIT", str(split))
+    inp = synth.make_beam_step(cfg, 13)
+    say(f"fused token rows {case} P={inp.prefix_len.tolist()} T={inp.tail_len.tolist()}")
+    assert (inp.tail_len > 0).all()  # every beam writes its current token
+    s = S.upload_beam_step(inp, DEV)
+    S.plan_beam_step(s)
+    items = B.bsp_debug_plan_items(s.plan)
+    assert (items[:, 3] > 1).any() == (split is not None), items
+    S.run_decode_step(s)
+    B.bsp_check(s.plan)
+    torch.cuda.synchronize()
+    ref = _applied(inp)
+    assert torch.equal(s.k_pool.cpu(), S.to_device(ref.k_pool, inp.dtype, "cpu")), case
+    assert torch.equal(s.v_pool.cpu(), S.to_device(ref.v_pool, inp.dtype, "cpu")), case
+    fo, fl = oracle.beam_decode_attention(ref)
+    say(f"  max |dO| = {assert_close(s.out, s.lse_out, fo, fl, inp.dtype, case):.3g}")
+
+
 @pytest.mark.parametrize("case", list(GROUP_CASES))
 def test_decode_step_group_sizes(case):
     g, dt = GROUP_CASES[case]
