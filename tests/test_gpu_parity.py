@@ -1070,6 +1070,37 @@ def test_full_size_fused_sampled(cfg, split_env, monkeypatch):
         assert np.abs(lse[x, k] - fl[0]).max() <= tl, (x, k)
 
 
+@pytest.mark.parametrize("cfg,batch", [("qwen3_4b", 96), ("qwen3_4b_d64", 140), ("qwen3_0p6b", 128)])
+def test_fused_step_above_the_streaming_limit(cfg, batch):
+    """A step whose outputs, LSE and token rows exceed 24 MiB is written with
+    plain stores instead of streaming ones (one and two query blocks per wave):
+    the token rows bit-exact, sampled beams against the oracle."""
+    inp = synth.make_beam_step(cfg, 2, batch=batch, prefix_range=(100, 300), tail_range=(1, 4))
+    W, Hq, Hkv, D = inp.beam, inp.num_q_heads, inp.num_kv_heads, inp.head_dim
+    rows = inp.batch * W
+    writes = rows * Hq * (2 * D + 4) + rows * Hkv * D * 2 * 2
+    assert writes > 24 << 20, writes
+    say(f"large writes {cfg} batch={batch}: {writes / 2**20:.1f} MiB")
+    s = S.upload_beam_step(inp, DEV)
+    S.plan_beam_step(s)
+    S.run_decode_step(s)
+    B.bsp_check(s.plan)
+    torch.cuda.synchronize()
+    ref = _applied(inp)
+    assert torch.equal(s.k_pool.cpu(), S.to_device(ref.k_pool, inp.dtype, "cpu")), cfg
+    assert torch.equal(s.v_pool.cpu(), S.to_device(ref.v_pool, inp.dtype, "cpu")), cfg
+    rng = np.random.default_rng(5)
+    out = s.out.float().cpu().numpy().reshape(inp.batch, W, Hq, D)
+    lse = s.lse_out.cpu().numpy().reshape(inp.batch, W, Hq)
+    to, tl = TOL[inp.dtype]
+    picks = [(0, 0), (inp.batch - 1, W - 1)]
+    picks += [(int(x), int(k)) for x, k in zip(rng.integers(0, inp.batch, 10), rng.integers(0, W, 10))]
+    for x, k in picks:
+        fo, fl = oracle.beam_attention_one(ref, x, k)
+        assert np.abs(out[x, k] - fo[0]).max() <= to, (x, k)
+        assert np.abs(lse[x, k] - fl[0]).max() <= tl, (x, k)
+
+
 # ------------------------------------------------- degenerate shapes, fused
 
 @pytest.mark.parametrize("name,cfg", [
