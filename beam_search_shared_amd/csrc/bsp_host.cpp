@@ -576,9 +576,22 @@ bsp_status_t bsp_plan(bsp_plan_t pl, int32_t B, int32_t W, int32_t q_len,
       }
       if (n > 1) n_slots += n;
     }
+    // Dealt longest first. When the items fill more than one round of
+    // workgroups, a request's tail rows count too (W rows per tail position,
+    // each the bytes of one prompt key, carried by its last chunk), so that
+    // the items a slot runs one after the other even out; within one round
+    // every item starts at once and the order only places them, and the prompt
+    // keys alone decide (measured: the wide-beam step 1-1.5% shorter with the
+    // tails counted, the 0.6B shape's single round 1.7% longer).
+    const bool several_rounds = (int64_t)fitems.size() > slots;
+    auto deal_cost = [&](const bsp::FusedItem& x) {
+      int64_t c = x.k_hi - x.k_lo;
+      if (several_rounds && x.k_hi == x.ri.valid) c += (int64_t)W * x.ri.tail;
+      return c;
+    };
     std::stable_sort(fitems.begin(), fitems.end(),
-                     [](const bsp::FusedItem& x, const bsp::FusedItem& y) {
-                       return x.k_hi - x.k_lo > y.k_hi - y.k_lo;
+                     [&](const bsp::FusedItem& x, const bsp::FusedItem& y) {
+                       return deal_cost(x) > deal_cost(y);
                      });
     std::memcpy(st + pl->fitems_off, fitems.data(), sizeof(bsp::FusedItem) * fitems.size());
     if (n_slots > 0)

@@ -296,7 +296,7 @@ def test_check_mode_requires_shared_prompt_blocks(monkeypatch):
 
 # ------------------------------------- fused-step work items and splits (host plan)
 
-def _item_plan(B_, W, G, D, dtype, prefix, key_bucket=0, hkv=8):
+def _item_plan(B_, W, G, D, dtype, prefix, key_bucket=0, hkv=8, tails=3):
     ps = 32
     nb = -(-(max(prefix) + 8) // ps)
     desc = B.make_desc(hkv * G, hkv, D, ps, 1 << 20, dtype, key_bucket=key_bucket,
@@ -305,16 +305,33 @@ def _item_plan(B_, W, G, D, dtype, prefix, key_bucket=0, hkv=8):
     P = np.asarray(prefix, np.int32)
     bt = np.arange(B_ * W * nb, dtype=np.int32).reshape(B_, W, nb) % (1 << 20)
     bt[:, :, :] = bt[:, :1, :]  # every beam shares its request's blocks
-    S = P if key_bucket else P + 3
+    S = P if key_bucket else P + np.asarray(tails, np.int32)
     B.bsp_plan(plan, B_, W, 1, P, S.astype(np.int32), bt)
     return B.bsp_debug_plan_items(plan)
 
 
-def _check_items(items, P, chunk=None):
+def _deal_cost(items, P, W, G, D, hkv=8, tails=3):
+    """The order items are dealt in: keys, plus W rows per tail position on a
+    request's last chunk when the items fill more than one round of 512
+    workgroups (per KV head and query tile: 64 rows per 16-row block, up to
+    three blocks per wave, one at head_dim 256)."""
+    rows = W * G
+    mb = min(max(-(-rows // 64), 1), 1 if D == 256 else 3)
+    slots = max(1, 512 // (hkv * -(-rows // (64 * mb))))
+    P = np.asarray(P, np.int64)
+    T = np.broadcast_to(np.asarray(tails, np.int64), P.shape)
+    lens = (items[:, 2] - items[:, 1]).astype(np.int64)
+    last = items[:, 2] == P[items[:, 0]]
+    return lens + np.where((len(items) > slots) & last, W * T[items[:, 0]], 0)
+
+
+def _check_items(items, P, chunk=None, deal=None):
     """Each request's items are contiguous, disjoint chunks covering [0, P_b)
-    (one item [0, P_b) when unsplit), listed longest first."""
+    (one item [0, P_b) when unsplit), listed in dealing order: longest first,
+    by `_deal_cost(items, P, *deal)` when given, else by keys."""
     lens = items[:, 2] - items[:, 1]
-    assert np.all(np.diff(lens) <= 0), "items must be listed longest first"
+    cost = lens if deal is None else _deal_cost(items, P, *deal)
+    assert np.all(np.diff(cost) <= 0), "items must be listed in dealing order"
     for b, Pb in enumerate(P):
         mine = items[items[:, 0] == b]
         mine = mine[np.argsort(mine[:, 1])]
@@ -343,11 +360,12 @@ def test_items_cover_every_request_once(monkeypatch):
         else:
             monkeypatch.delenv("BSP_SPLIT", raising=False)
         G = int(rng.choice([1, 2, 4]))
-        items = _item_plan(Bn, int(rng.integers(1, 40)), G, 128, "bf16", P)
+        W = int(rng.integers(1, 40))
+        items = _item_plan(Bn, W, G, 128, "bf16", P)
         chunk = None
         if mode == 1:
             chunk = -(-int(__import__("os").environ["BSP_SPLIT"]) // 64) * 64
-        _check_items(items, P, chunk)
+        _check_items(items, P, chunk, deal=(W, G, 128))
         if mode == 0:
             assert np.all(items[:, 3] == 1) and len(items) == Bn
 
@@ -359,7 +377,7 @@ def test_forced_split_respects_the_partial_state_budget(monkeypatch):
     monkeypatch.setenv("BSP_SPLIT", "64")
     P = np.arange(64, dtype=np.int32) * 40 + 100
     items = _item_plan(64, 96, 2, 128, "bf16", P)  # three 16-row blocks per wave
-    _check_items(items, P, 64)
+    _check_items(items, P, 64, deal=(96, 2, 128))
     split = sorted({int(b) for b, lo, hi, n in items if n > 1})
     assert split and len(split) < 64
     used = sum(-(-int(P[b]) // 64) for b in split)
@@ -408,10 +426,28 @@ def test_split_chosen_only_where_the_model_gains(name, prefix, split, monkeypatc
         P = np.zeros(16, np.int64)
     W, G = (96, 2) if prefix[0] == "u" and prefix[1] == 128 else (30, 2)
     items = _item_plan(len(P), W, G, 128, "bf16", P)
-    _check_items(items, P)
+    _check_items(items, P, deal=(W, G, 128))
     assert bool((items[:, 3] > 1).any()) == split, name
     monkeypatch.setenv("BSP_SPLIT", "0")
     assert not (_item_plan(len(P), W, G, 128, "bf16", P)[:, 3] > 1).any()
+
+
+def test_items_dealt_with_tails_only_over_several_rounds(monkeypatch):
+    """Tail rows count in the dealing order only when the items fill more than
+    one round: 128 requests x beam 96 (two rounds) with tails 0-8 put a short
+    prompt with a long tail ahead of a longer prompt without one; 64 requests
+    (one round) keep the prompt order."""
+    monkeypatch.delenv("BSP_SPLIT", raising=False)
+    rng = np.random.default_rng(11)
+    for Bn in (128, 64):
+        P = rng.integers(2800, 3201, Bn)
+        T = rng.integers(0, 9, Bn)
+        items = _item_plan(Bn, 96, 2, 128, "bf16", P, tails=T)
+        assert np.all(items[:, 3] == 1)
+        _check_items(items, P, deal=(96, 2, 128, 8, T))
+        order = items[:, 0]
+        by_keys = np.all(np.diff(P[order]) <= 0)
+        assert by_keys == (Bn == 64), Bn
 
 
 # ------------------------------------------------ prefill plans (mixed steps)
