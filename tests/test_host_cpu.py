@@ -315,23 +315,31 @@ def _deal_cost(items, P, W, G, D, hkv=8, tails=3):
     request's last chunk when the items fill more than one round of 512
     workgroups (per KV head and query tile: 64 rows per 16-row block, up to
     three blocks per wave, one at head_dim 256)."""
-    rows = W * G
-    mb = min(max(-(-rows // 64), 1), 1 if D == 256 else 3)
-    slots = max(1, 512 // (hkv * -(-rows // (64 * mb))))
     P = np.asarray(P, np.int64)
     T = np.broadcast_to(np.asarray(tails, np.int64), P.shape)
     lens = (items[:, 2] - items[:, 1]).astype(np.int64)
     last = items[:, 2] == P[items[:, 0]]
-    return lens + np.where((len(items) > slots) & last, W * T[items[:, 0]], 0)
+    return lens + np.where(_several_rounds(items, W, G, D, hkv) & last, W * T[items[:, 0]], 0)
 
 
-def _check_items(items, P, chunk=None, deal=None):
+def _several_rounds(items, W, G, D, hkv=8):
+    rows = W * G
+    mb = min(max(-(-rows // 64), 1), 1 if D == 256 else 3)
+    return len(items) > max(1, 512 // (hkv * -(-rows // (64 * mb))))
+
+
+def _check_items(items, P, chunk=None, *, deal):
     """Each request's items are contiguous, disjoint chunks covering [0, P_b)
-    (one item [0, P_b) when unsplit), listed in dealing order: longest first,
-    by `_deal_cost(items, P, *deal)` when given, else by keys."""
-    lens = items[:, 2] - items[:, 1]
-    cost = lens if deal is None else _deal_cost(items, P, *deal)
-    assert np.all(np.diff(cost) <= 0), "items must be listed in dealing order"
+    (one item [0, P_b) when unsplit), listed in dealing order by
+    `_deal_cost(items, P, *deal)`: longest first over several rounds; in one
+    round the longer half longest first, then the shorter half shortest first."""
+    cost = _deal_cost(items, P, *deal)
+    if _several_rounds(items, *deal[:3], *deal[3:4]):
+        assert np.all(np.diff(cost) <= 0), "items must be listed longest first"
+    else:
+        h = len(cost) // 2
+        assert np.all(np.diff(cost[:h]) <= 0) and np.all(np.diff(cost[h:]) >= 0), cost
+        assert h == 0 or cost[:h].min() >= cost[h:].max(), cost
     for b, Pb in enumerate(P):
         mine = items[items[:, 0] == b]
         mine = mine[np.argsort(mine[:, 1])]
@@ -436,7 +444,7 @@ def test_items_dealt_with_tails_only_over_several_rounds(monkeypatch):
     """Tail rows count in the dealing order only when the items fill more than
     one round: 128 requests x beam 96 (two rounds) with tails 0-8 put a short
     prompt with a long tail ahead of a longer prompt without one; 64 requests
-    (one round) keep the prompt order."""
+    (one round) are ordered by their prompts alone (longer half first)."""
     monkeypatch.delenv("BSP_SPLIT", raising=False)
     rng = np.random.default_rng(11)
     for Bn in (128, 64):
@@ -445,8 +453,9 @@ def test_items_dealt_with_tails_only_over_several_rounds(monkeypatch):
         items = _item_plan(Bn, 96, 2, 128, "bf16", P, tails=T)
         assert np.all(items[:, 3] == 1)
         _check_items(items, P, deal=(96, 2, 128, 8, T))
-        order = items[:, 0]
-        by_keys = np.all(np.diff(P[order]) <= 0)
+        keys = P[items[:, 0]]
+        by_keys = np.all(np.diff(keys) <= 0) or (
+            np.all(np.diff(keys[:Bn // 2]) <= 0) and np.all(np.diff(keys[Bn // 2:]) >= 0))
         assert by_keys == (Bn == 64), Bn
 
 
