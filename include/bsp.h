@@ -337,8 +337,8 @@ bsp_status_t bsp_merge(int32_t rows, int32_t heads, int32_t head_dim, int32_t n_
  * bf16/f16 only (BSP_ERR_UNSUPPORTED for f32: use the separate calls).
  * Work items go longest first (when they fill more than one round of
  * workgroups, a request's W x tail rows count as keys; in one round the
- * shorter half is listed shortest first). When the plan split a request's prompt into
- * chunks (see bsp_debug_plan_items), each chunk's workgroup leaves its partial
+ * shorter half is listed shortest first). When the plan split a request's
+ * prompt into chunks (see bsp_debug_plan_items), each chunk's workgroup leaves its partial
  * state in the workspace and counts itself with one atomic add; the last to
  * arrive merges the states exactly through their log-sum-exp (PR #21738,
  * Solution) and finishes the request. No workgroup waits for another. Calls
