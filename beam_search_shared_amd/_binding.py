@@ -82,6 +82,7 @@ _SIGS = {
     "bsp_prefix_attn": (_I32, [_P, _P, _P, _P, _P, _P, _P]),
     "bsp_prefix_attn_two": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "bsp_cached_decode": (_I32, [_P, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "bsp_cached_decode_merge": (_I32, [_P, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P]),
     "bsp_tail_attn": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "bsp_merge": (_I32, [_I32, _I32, _I32, _I32, _P, _P, _I64, _I64, _P, _I32, _P, _P]),
     "bsp_naive_beam_attn": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P]),
@@ -260,6 +261,14 @@ def bsp_cached_decode(plan: Plan, q, k_new, v_new, new_row_stride: int, slots, k
                                             new_row_stride, _ptr(slots), _ptr(k_pool),
                                             _ptr(v_pool), _ptr(o_part), _ptr(lse_part),
                                             _ptr(o_out), _ptr(lse_out), _stream(stream)))
+
+
+def bsp_cached_decode_merge(plan: Plan, q, k_new, v_new, new_row_stride: int, slots, k_pool,
+                            v_pool, o_part, lse_part, o_out, lse_out=None, stream=None) -> None:
+    _check(load_library().bsp_cached_decode_merge(plan.handle, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                                  new_row_stride, _ptr(slots), _ptr(k_pool),
+                                                  _ptr(v_pool), _ptr(o_part), _ptr(lse_part),
+                                                  _ptr(o_out), _ptr(lse_out), _stream(stream)))
 
 
 def bsp_tail_attn(plan: Plan, q, k_pool, v_pool, block_tables, cache_indirection, o_tail,

@@ -18,8 +18,8 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libbsp.so")
 BUILD = os.path.join(HERE, "_build")
 
-SOURCES = ["bsp_host.cpp", "write_kv.hip", "merge.hip", "tail_attn.hip", "prefix_attn.hip",
-           "naive_attn.hip", "static_ws.hip"]
+SOURCES = ["bsp_host.cpp", "write_kv.hip", "merge.hip", "merge_row.hip", "tail_attn.hip",
+           "prefix_attn.hip", "naive_attn.hip", "static_ws.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

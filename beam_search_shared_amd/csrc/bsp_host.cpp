@@ -26,6 +26,7 @@
 #include <vector>
 
 #include "bsp_internal.h"
+#include "merge_row.h"
 
 using bsp::DevHeader;
 using bsp::ReqInfo;
@@ -947,6 +948,55 @@ bsp_status_t bsp_cached_decode(bsp_plan_t pl, const void* q, const void* k_new, 
   f.new_slots = slots_d;
   return after_launch(pl, bsp::launch_cached_decode(p, f, d.dtype, d.head_dim, stream),
                       "cached decode launch", stream);
+}
+
+bsp_status_t bsp_cached_decode_merge(bsp_plan_t pl, const void* q, const void* k_new,
+                                     const void* v_new, int64_t new_row_stride,
+                                     const int32_t* slots_d, void* k_pool, void* v_pool,
+                                     const float* o_part, const float* lse_part, void* o_out,
+                                     float* lse_out, hipStream_t stream) {
+  bsp::PrefixParams p{};
+  bsp_status_t st = prefix_params(pl, q, k_pool, v_pool, const_cast<float*>(o_part),
+                                  const_cast<float*>(lse_part), p);
+  if (st != BSP_OK) return st;
+  const bsp_layer_desc_t& d = pl->desc;
+  if (d.key_bucket <= 0 || pl->q_len != 1 || pl->W != 1)
+    return fail(BSP_ERR_UNSUPPORTED,
+                "bsp_cached_decode_merge needs a cached-prefix plan with q_len 1 and one beam");
+  if (d.dtype == BSP_F32)
+    return fail(BSP_ERR_UNSUPPORTED,
+                "bsp_cached_decode_merge runs bf16/f16; use the separate calls for f32");
+  if (!k_new || !v_new || !slots_d || !o_out) return fail(BSP_ERR_ARG, "null pointer");
+  if (new_row_stride < (int64_t)d.num_kv_heads * d.head_dim || new_row_stride % 8 != 0)
+    return fail(BSP_ERR_ARG, "new_row_stride %lld must be >= %d and a multiple of 8",
+                (long long)new_row_stride, d.num_kv_heads * d.head_dim);
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(BSP_ERR_ARG, "k_new and v_new must be 16-byte aligned");
+  bsp::MergeRowParams m{};
+  m.rows = pl->B;
+  m.hq = d.num_q_heads;
+  m.hkv = d.num_kv_heads;
+  m.d = d.head_dim;
+  m.n_parts = pl->n_split;
+  m.o_parts = o_part;
+  m.lse_parts = lse_part;
+  m.o_stride = (int64_t)pl->B * d.num_q_heads * d.head_dim;
+  m.lse_stride = (int64_t)pl->B * d.num_q_heads;
+  m.q = q;
+  m.k_new = k_new;
+  m.v_new = v_new;
+  m.new_stride = new_row_stride;
+  m.slots = slots_d;
+  m.k_pool = k_pool;
+  m.v_pool = v_pool;
+  m.page_shift = pl->page_shift;
+  m.num_pages = d.num_pages;
+  m.scale = d.sm_scale;
+  m.o_out = o_out;
+  m.lse_out = lse_out;
+  m.hdr = p.hdr;
+  return after_launch(pl, bsp::launch_merge_row(m, d.dtype, stream), "cached decode merge launch",
+                      stream);
 }
 
 bsp_status_t bsp_prefix_attn_two(bsp_plan_t a, bsp_plan_t b, const void* q, const void* k_pool,

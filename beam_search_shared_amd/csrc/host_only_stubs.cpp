@@ -4,6 +4,7 @@
 // launcher here reports that no GPU code is linked, and plans created with
 // BSP_PLAN_HOST_ONLY never reach them.
 #include "bsp_internal.h"
+#include "merge_row.h"
 
 namespace bsp {
 
@@ -37,6 +38,7 @@ hipError_t launch_mixed_step(const PrefixParams&, const FusedParams&, const Pref
 hipError_t launch_tail(const TailParams&, int, int, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_tail_slots(const TailParams&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_merge(const MergeParams&, int, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_merge_row(const MergeRowParams&, int, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_naive(const TailParams&, void*, float*, int, int, hipStream_t) {
   return hipErrorNotSupported;
 }

@@ -285,6 +285,17 @@ def run_cached_decode(c: CachedPrefixDevice, stream=None) -> None:
                         stream)
 
 
+def run_cached_decode_two(c: CachedPrefixDevice, stream=None) -> None:
+    """A one-row cached-prefix decode call in two launches: the cache chunks
+    (bsp_prefix_attn), then their merge with this call's row and the row's write
+    into its page (bsp_cached_decode_merge)."""
+    ns = c.n_split
+    B.bsp_prefix_attn(c.plan_cache, c.q, c.k_pool, c.v_pool, c.o_part[:ns], c.lse_part[:ns], stream)
+    B.bsp_cached_decode_merge(c.plan_cache, c.q, c.new_k, c.new_v, c.num_kv_heads * c.head_dim,
+                              c.slots, c.k_pool, c.v_pool, c.o_part[:ns], c.lse_part[:ns], c.out,
+                              c.lse_out, stream)
+
+
 @dataclass
 class PrefillDevice:
     """The context requests of a mixed step on the device, with their plan."""

@@ -407,9 +407,11 @@ def cached_work(L: int, Sq: int, Hq: int, Hkv: int, D: int, e: int):
 
 
 def bench_cached(args, torch, synth, B, S, prefill: bool) -> dict:
-    """The masked cached-prefix call: bsp_write_kv + bsp_prefix_attn_two (cache chunks
-    and new rows) + bsp_merge, rotating over layer copies; beside it the same call with
-    one bsp_prefix_attn per segment, and the cache chunks alone (the roofline entry)."""
+    """The masked cached-prefix call, rotating over layer copies: bsp_write_kv +
+    bsp_prefix_attn_two (cache chunks and new rows) + bsp_merge; for a one-row decode
+    also bsp_prefix_attn (cache chunks) + bsp_cached_decode_merge (the headline there)
+    and the one-launch bsp_cached_decode; beside them the same call with one
+    bsp_prefix_attn per segment, and the cache chunks alone (the roofline entry)."""
     import oracle
 
     dev = "cuda"
@@ -479,10 +481,17 @@ def bench_cached(args, torch, synth, B, S, prefill: bool) -> dict:
                                            c.k_pool.data_ptr(), c.v_pool.data_ptr(),
                                            c.o_part.data_ptr(), c.lse_part.data_ptr(),
                                            c.out.data_ptr(), c.lse_out.data_ptr(), sh))
+            mrow = (lib.bsp_cached_decode_merge, (c.plan_cache.handle, c.q.data_ptr(),
+                                                  c.new_k.data_ptr(), c.new_v.data_ptr(), hd,
+                                                  c.slots.data_ptr(), c.k_pool.data_ptr(),
+                                                  c.v_pool.data_ptr(), c.o_part.data_ptr(),
+                                                  c.lse_part.data_ptr(), c.out.data_ptr(),
+                                                  c.lse_out.data_ptr(), sh))
             # the call: write, both key segments (one launch when their tiles
             # allow it), merge; the same as one bsp_prefix_attn per segment; and,
-            # for a one-row decode, the whole call in one launch
-            calls.append((write, both, merge, cache, one))
+            # for a one-row decode, the cache chunks then their merge with the
+            # new row (which also writes it), and the whole call in one launch
+            calls.append((write, both, merge, cache, one, mrow))
             calls4.append((write, cache, new, merge))
 
         def runner(table, sel):
@@ -498,13 +507,16 @@ def bench_cached(args, torch, synth, B, S, prefill: bool) -> dict:
                               main_stream, sync)
         _, seg_ms = _timed_loop(torch, runner(calls, (3,)), args.steps, args.warmup, 0.0,
                                 main_stream, sync)
-        one_ms = one_gpu_ms = None
+        one_ms = one_gpu_ms = two_ms = None
         if not prefill:
             sec1, one_gpu_ms = _timed_loop(torch, runner(calls, (4,)), args.steps, args.warmup, 0.0,
                                            main_stream, sync)
             one_ms = sec1 / args.steps * 1e3
+            sec2, _ = _timed_loop(torch, runner(calls, (3, 5)), args.steps, args.warmup, 0.0,
+                                  main_stream, sync)
+            two_ms = sec2 / args.steps * 1e3
         res_t[name] = dict(ms=sec / args.steps * 1e3, ms4=sec4 / args.steps * 1e3, seg_ms=seg_ms,
-                           one_ms=one_ms, one_gpu_ms=one_gpu_ms,
+                           one_ms=one_ms, one_gpu_ms=one_gpu_ms, two_ms=two_ms,
                            n_split=base.n_split, split_keys=base.plan_cache.split_keys,
                            layers=layers)
         del cs, base
@@ -524,9 +536,14 @@ def bench_cached(args, torch, synth, B, S, prefill: bool) -> dict:
                 "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
                 "avg_launch_us": a["seg_ms"] * 1e3, "alg_bytes_per_launch": seg_bytes}
     cfg = "cached_prefill" if prefill else "cached_decode"
-    # the headline is the three-launch call (write, both segments, merge): at this
-    # shape it is faster than the one-launch bsp_cached_decode, reported beside it
-    call_ms = a["ms"]
+    # the headline: for the one-row decode the two-launch call (cache chunks, then
+    # their merge with the new row, which also writes it), with the three-launch
+    # call (write, both segments, merge) and the one-launch bsp_cached_decode
+    # beside it; for the prefill the three-launch call
+    call_ms = a["ms"] if prefill else a["two_ms"]
+    step = ("bsp_write_kv + bsp_prefix_attn_two (cache chunks and new rows) + bsp_merge" if prefill
+            else "bsp_prefix_attn (cache chunks) + bsp_cached_decode_merge (merge with the new "
+                 "row, which it writes into its page)")
     res = {
         "metric": "masked cached-prefix calls/s per layer (write + cache chunks and new rows + merge)",
         "value": 1e3 / call_ms, "unit": "calls/s", "n_gpus": 1, "steps": args.steps,
@@ -535,7 +552,7 @@ def bench_cached(args, torch, synth, B, S, prefill: bool) -> dict:
         "config": {"workload": WORKLOADS[cfg], "name": cfg, "valid_rows": L, "new_rows": Sq,
                    "layers_rotated": a["layers"], "chunks": a["n_split"],
                    "chunk_keys": a["split_keys"], "flops": flops, "alg_bytes": nbytes,
-                   "step": "bsp_write_kv + bsp_prefix_attn_two (cache chunks and new rows) + bsp_merge",
+                   "step": step,
                    "segments_one_launch_each_ms_per_step": a["ms4"],
                    "fixed_256_chunks": res_t["fixed_256"]["n_split"],
                    "fixed_256_ms_per_step": res_t["fixed_256"]["ms"],
@@ -545,6 +562,7 @@ def bench_cached(args, torch, synth, B, S, prefill: bool) -> dict:
     if not prefill:
         # bsp_cached_decode: the same one-row call as one launch (write, cache
         # chunks, new row and merge), host-timed per call and event-timed per launch
+        res["config"]["three_launch_ms_per_step"] = a["ms"]
         res["config"]["one_launch_ms_per_step"] = a["one_ms"]
         res["config"]["one_launch_kernel_us"] = a["one_gpu_ms"] * 1e3
     if not args.no_cpu_baseline:

@@ -286,6 +286,33 @@ bsp_status_t bsp_cached_decode(bsp_plan_t plan, const void* q, const void* k_new
                                float* lse_out, hipStream_t stream);
 
 /*
+ * The one-row cached-prefix decode in two launches: bsp_prefix_attn on the
+ * plan (the cache chunks' partial states into o_part/lse_part), then this
+ * call, which merges them exactly with the call's own row (PR #2202,
+ * Background: a decode step attends the valid cached rows plus its own row;
+ * TensorRT-LLM PR #21738, Description: Solution, merged with the log-sum-exp)
+ * -- the row is one more part, its score scale * q . k_new and its value
+ * v_new -- into o_out (dtype [B][Hq][D]) and lse_out (float [B][Hq], may be
+ * null), and writes the row into the pools at slots_d[b] (device int32 [B],
+ * page * page_size + row; a slot outside the pool is skipped and recorded for
+ * bsp_check). No separate KV write is needed, and the new row is never read
+ * from the pool.
+ *   q             [B, 1, 1, Hq, D]
+ *   k_new, v_new  request b's new row at element b * new_row_stride, [Hkv][D],
+ *                 16-byte aligned; new_row_stride a multiple of 8
+ *   o_part        float [n_split][B][Hq][D], 16-byte aligned; lse_part float
+ *                 [n_split][B][Hq], as bsp_prefix_attn wrote them for this plan
+ * The same result as bsp_cached_decode, up to fp32 summation order. The plan
+ * as for bsp_cached_decode (key_bucket > 0, W = 1, q_len = 1, bf16/f16):
+ * BSP_ERR_UNSUPPORTED otherwise; BSP_ERR_ARG for null or misaligned pointers.
+ */
+bsp_status_t bsp_cached_decode_merge(bsp_plan_t plan, const void* q, const void* k_new,
+                                     const void* v_new, int64_t new_row_stride,
+                                     const int32_t* slots_d, void* k_pool, void* v_pool,
+                                     const float* o_part, const float* lse_part, void* o_out,
+                                     float* lse_out, hipStream_t stream);
+
+/*
  * Tail attention: each beam's G query rows against its own tail positions
  * P_b <= j < S_b, gathered through cache_indirection: position j of beam k is
  * read from beam src = cache_indirection[b][k][j], page

@@ -590,6 +590,98 @@ def test_cached_decode_one_launch_other_shapes(hq, hkv, d, dtype, L):
     assert (c.lse_out - one[1]).abs().max().item() <= 1e-5
 
 
+@pytest.mark.parametrize("L", CACHED_L + RANDOM_L[8:])
+def test_cached_decode_two_launches(L):
+    """The one-row decode as the cache chunks plus bsp_cached_decode_merge (the
+    merge folded with the call's row, which it also writes into its page), at
+    the edge and random valid lengths of the 10368-row allocation, twice in a
+    row: against the oracle, the new row bit for bit, and equal to the
+    four-launch call within rounding."""
+    R = oracle.bucket_rows(L, 256, 10368)
+    inp = synth.make_cached_prefix(L % 7, valid_rows=L, q_len=1, nan_from_row=R)
+    c = S.upload_cached_prefix(inp, DEV)
+    S.plan_cached_prefix(c)
+    say(f"two-launch cached decode L={L}: {c.n_split} chunks of {c.plan_cache.split_keys} keys")
+    o, lse = oracle.cached_prefix_attention(inp, causal=True)
+    outs = []
+    for rep in range(2):
+        S.run_cached_decode_two(c)
+        B.bsp_check(c.plan_cache)
+        torch.cuda.synchronize()
+        assert_close(c.out.reshape(1, 24, 128), c.lse_out.reshape(1, 24), o, lse, "f16",
+                     f"two-launch decode L={L} launch {rep}")
+        outs.append((c.out.clone(), c.lse_out.clone()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    page, row = divmod(int(c.slots[0]), c.page_size)
+    assert torch.equal(c.k_pool[page, :, row].cpu(), S.to_device(inp.new_k[0], "f16", "cpu"))
+    assert torch.equal(c.v_pool[page, :, row].cpu(), S.to_device(inp.new_v[0], "f16", "cpu"))
+    S.run_cached_prefix(c)  # the four-launch call
+    B.bsp_check(c.plan_cache)
+    B.bsp_check(c.plan_new)
+    torch.cuda.synchronize()
+    assert (c.out.float() - outs[0][0].float()).abs().max().item() <= 2e-3
+    assert (c.lse_out - outs[0][1]).abs().max().item() <= 1e-5
+
+
+@pytest.mark.parametrize("hq,hkv,d,dtype,L,split", [
+    (16, 4, 64, "bf16", 3000, 0), (8, 4, 256, "f16", 2000, 0), (32, 4, 128, "bf16", 4100, 0),
+    (16, 2, 256, "bf16", 777, 0), (8, 8, 64, "f16", 1, 0),
+    (24, 8, 128, "f16", 4608, 64),   # 72 chunks: more than the 64 held in registers
+    (24, 8, 128, "bf16", 4500, 64)])  # 71 chunks
+def test_cached_decode_two_launches_other_shapes(hq, hkv, d, dtype, L, split):
+    """bsp_cached_decode_merge at other head and group sizes (groups of eight at
+    head_dim 256 too), both 16-bit dtypes, and with more chunks than its merge
+    holds in registers: against the oracle, the row written bit for bit."""
+    R = oracle.bucket_rows(L, 256, 4608)
+    inp = synth.make_cached_prefix(L % 11, valid_rows=L, q_len=1, num_q_heads=hq,
+                                   num_kv_heads=hkv, head_dim=d, dtype=dtype,
+                                   max_cache_rows=4608, nan_from_row=R)
+    c = S.upload_cached_prefix(inp, DEV, kv_split=split if split else -1)
+    S.plan_cached_prefix(c)
+    say(f"two-launch cached decode {hq}/{hkv} heads d={d} {dtype} L={L}: {c.n_split} chunks")
+    if split:
+        assert c.n_split > 64
+    o, lse = oracle.cached_prefix_attention(inp, causal=True)
+    S.run_cached_decode_two(c)
+    B.bsp_check(c.plan_cache)
+    torch.cuda.synchronize()
+    assert_close(c.out.reshape(1, hq, d), c.lse_out.reshape(1, hq), o, lse, dtype,
+                 f"two-launch decode {hq}/{hkv} d={d} {dtype}")
+    page, row = divmod(int(c.slots[0]), c.page_size)
+    assert torch.equal(c.k_pool[page, :, row].cpu(), S.to_device(inp.new_k[0], dtype, "cpu"))
+    assert torch.equal(c.v_pool[page, :, row].cpu(), S.to_device(inp.new_v[0], dtype, "cpu"))
+
+
+def test_cached_decode_two_launches_bad_slot_is_skipped_and_reported():
+    """A slot outside the pool: the row is not written, bsp_check reports the
+    fault, and the output (which never reads the row from the pool) is right."""
+    inp = synth.make_cached_prefix(4, valid_rows=900, q_len=1)
+    c = S.upload_cached_prefix(inp, DEV)
+    S.plan_cached_prefix(c)
+    before_k, before_v = c.k_pool.clone(), c.v_pool.clone()
+    c.slots.fill_(int(c.k_pool.shape[0]) * c.page_size)  # one past the pool
+    S.run_cached_decode_two(c)
+    with pytest.raises(B.BspError):
+        B.bsp_check(c.plan_cache)
+    torch.cuda.synchronize()
+    # bit patterns: the pools hold NaN past the valid rows
+    assert torch.equal(c.k_pool.view(torch.int16), before_k.view(torch.int16))
+    assert torch.equal(c.v_pool.view(torch.int16), before_v.view(torch.int16))
+    o, lse = oracle.cached_prefix_attention(inp, causal=True)
+    assert_close(c.out.reshape(1, 24, 128), c.lse_out.reshape(1, 24), o, lse, "f16", "bad slot")
+
+
+def test_cached_decode_two_launches_rejects_other_plans():
+    inp = synth.make_cached_prefix(3, valid_rows=300, q_len=4)
+    c = S.upload_cached_prefix(inp, DEV)
+    S.plan_cached_prefix(c)
+    with pytest.raises(B.BspError) as ei:
+        B.bsp_cached_decode_merge(c.plan_cache, c.q, c.new_k, c.new_v, c.num_kv_heads * c.head_dim,
+                                  c.slots, c.k_pool, c.v_pool, c.o_part, c.lse_part, c.out,
+                                  c.lse_out)
+    assert ei.value.name == "BSP_ERR_UNSUPPORTED"
+
+
 def test_cached_decode_one_launch_rejects_too_wide_groups():
     """Eight query heads per KV head at head_dim 256 (512 row-chunk pairs) are more
     than the merge's 256 threads: refused before any launch."""
