@@ -24,7 +24,7 @@ constexpr int kRowRegParts = 8;  // parts per slice held in registers (64 in all
 
 template <typename T>
 __global__ __launch_bounds__(256) void merge_row_kernel(MergeRowParams p) {
-  __shared__ float red[4];
+  __shared__ float red_m[4], red_d[4];
   __shared__ float s_new_sh;
   __shared__ float w_s[kRowSlices * kRowRegParts];
   __shared__ float acc_s[kRowSlices][256];  // head_dim <= 256
@@ -64,13 +64,21 @@ __global__ __launch_bounds__(256) void merge_row_kernel(MergeRowParams p) {
   if (wave == 0)
     for (int i = lane; i < p.d; i += 64)
       dot = fmaf(Traits<T>::to_f(qrow[i]), Traits<T>::to_f(krow[i]), dot);
-  float vv[2][4];
+  // the row's write into its page, once per (request, KV head) by the group's
+  // first head: its slot and 16-byte chunks are loaded with everything else
+  const bool writer = h % group == 0 && tid < p.d / 8;
+  int32_t slot = -1;
+  u32x4 kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
+  if (writer) {
+    slot = p.slots[b];
+    kw = *reinterpret_cast<const u32x4*>(krow + tid * 8);
+    vw = *reinterpret_cast<const u32x4*>(vrow + tid * 8);
+  }
+  u32x2 vv[2] = {u32x2{0u, 0u}, u32x2{0u, 0u}};  // slice 0: the row's value, 4 columns a chunk
 #pragma unroll
   for (int cc = 0; cc < 2; ++cc) {
     const int c = cl + 32 * cc;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      vv[cc][e] = slice == 0 && c < chunks ? Traits<T>::to_f(vrow[c * 4 + e]) : 0.f;
+    if (slice == 0 && c < chunks) vv[cc] = *reinterpret_cast<const u32x2*>(vrow + c * 4);
   }
 
   // ---- the maximum over the parts and the row's score
@@ -79,12 +87,11 @@ __global__ __launch_bounds__(256) void merge_row_kernel(MergeRowParams p) {
     for (int part = tid; part < p.n_parts; part += 256) m = fmaxf(m, lse_p[part * p.lse_stride]);
   m = wave_max(m);
   if (wave == 0) dot = wave_sum(dot);
-  if (lane == 0) red[wave] = m;
+  if (lane == 0) red_m[wave] = m;
   if (tid == 0) s_new_sh = dot * p.scale;
   __syncthreads();
   const float s_new = s_new_sh;
-  const float M = fmaxf(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])), s_new);
-  __syncthreads();
+  const float M = fmaxf(fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3])), s_new);
 
   // ---- weights and the denominator (an empty part, lse -inf, weighs 0)
   float dl = 0.f;
@@ -97,10 +104,10 @@ __global__ __launch_bounds__(256) void merge_row_kernel(MergeRowParams p) {
       dl += fast_exp2((lse_p[part * p.lse_stride] - M) * kLog2e);
   }
   dl = wave_sum(dl);
-  if (lane == 0) red[wave] = dl;
+  if (lane == 0) red_d[wave] = dl;
   __syncthreads();
   const float w_new = fast_exp2((s_new - M) * kLog2e);
-  const float den = ((red[0] + red[1]) + (red[2] + red[3])) + w_new;
+  const float den = ((red_d[0] + red_d[1]) + (red_d[2] + red_d[3])) + w_new;
 
   // ---- weighted sums per slice; slice 0 adds the row's value
 #pragma unroll
@@ -127,8 +134,9 @@ __global__ __launch_bounds__(256) void merge_row_kernel(MergeRowParams p) {
       }
     }
     if (slice == 0) {
+      const T* ve = reinterpret_cast<const T*>(&vv[cc]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = fmaf(w_new, vv[cc][e], acc[e]);
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(w_new, Traits<T>::to_f(ve[e]), acc[e]);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc_s[slice][c * 4 + e] = acc[e];
@@ -144,19 +152,16 @@ __global__ __launch_bounds__(256) void merge_row_kernel(MergeRowParams p) {
   }
   if (p.lse_out != nullptr && tid == 0) p.lse_out[rh] = M + __logf(den);
 
-  // ---- the row into its page, once per (request, KV head): by the group's first head
-  if (h % group == 0 && tid < p.d / 8) {
-    const int32_t slot = p.slots[b];
+  // ---- the row into its page (a slot outside the pool is skipped and recorded)
+  if (writer) {
     if (slot < 0 || (int64_t)slot >= ((int64_t)p.num_pages << p.page_shift)) {
       if (tid == 0)
         record_fault(&p.hdr->error_bits, &p.hdr->fault_count, &p.hdr->first_value, kErrWriteSlot, slot);
     } else {
       const int64_t dst = pool_row(slot >> p.page_shift, p.hkv, g, p.page_shift,
                                    slot & ((1 << p.page_shift) - 1), p.d) + tid * 8;
-      *reinterpret_cast<u32x4*>(static_cast<T*>(p.k_pool) + dst) =
-          *reinterpret_cast<const u32x4*>(krow + tid * 8);
-      *reinterpret_cast<u32x4*>(static_cast<T*>(p.v_pool) + dst) =
-          *reinterpret_cast<const u32x4*>(vrow + tid * 8);
+      *reinterpret_cast<u32x4*>(static_cast<T*>(p.k_pool) + dst) = kw;
+      *reinterpret_cast<u32x4*>(static_cast<T*>(p.v_pool) + dst) = vw;
     }
   }
 }
