@@ -173,14 +173,14 @@ struct MergeParams {
   float* lse_out;
 };
 
-// Bytes of the library's static device scratch (bsp_plan_static).
-// A beam step (one query block per wave) whose output and current-token
-// writes total at most this many bytes writes them with non-temporal stores:
-// written normally they would all still be dirty in the eight XCDs' L2s (4 MB
-// each) when the kernel ends, and the write-back there runs after the last
-// workgroup. Larger writes drain during the kernel anyway, and the hint
-// measured slightly slower there.
+// A beam step with one or two query blocks per wave whose output, LSE and
+// current-token writes total at most this many bytes writes them with
+// non-temporal stores: written normally they would all still be dirty in the
+// eight XCDs' L2s (4 MB each) when the kernel ends, and the write-back there
+// runs after the last workgroup. Larger writes drain during the kernel anyway,
+// and the hint measured slightly slower there.
 constexpr int64_t kStreamOutBytes = int64_t(24) << 20;
+// Bytes of the library's static device scratch (bsp_plan_static).
 constexpr size_t kStaticWorkspaceBytes = size_t(32) << 20;
 // The calling thread's error message (bsp_last_error) and status.
 bsp_status_t set_error(bsp_status_t st, const char* fmt, ...);
